@@ -1,0 +1,175 @@
+/*
+ * bigemm.h -- C ABI of libbigemm, batch-invariant GEMMs for AMD MI355X (gfx950).
+ *
+ * Every entry point computes C[M,N] = A[M,K] . B[K,N] with alpha = 1 and
+ * beta = 0: C[i][j] = sum over k of A[i][k] * B[k][j], the definition given
+ * in section 2.1 of "DeepSeek V4的batch invariance：大模型确定性推理的工程基石";
+ * the fixed alpha = 1 / beta = 0 form is the one section 3.1 of the wmrh.cn
+ * V4 engineering blog describes.  Output is bf16, rounded to nearest even
+ * from an fp32 accumulator, with subnormals kept.
+ *
+ * Batch invariance (article "DeepSeek不惜代价保住它！V4关键特性被挖出来了",
+ * section "什么是batch invariance"): for the same operands B (and scales) and
+ * the same K, N, every output row C[i,:] is bit-identical whatever M is, where
+ * row i sits in the batch and which other rows share the batch.  The library
+ * guarantees this because, for the three invariant entry points:
+ *   - the kernel schedule (MFMA instruction, tile sizes, K step and K order)
+ *     is a function of (dtype, N, K) only -- M is not an input to it;
+ *   - one workgroup owns the whole K loop of each output element, with the
+ *     fp32 accumulator in registers: no split-K, no stream-K, no atomics
+ *     (the split-K conflict is the one the same article's section
+ *     "牺牲了什么" describes);
+ *   - the M tail is handled only by zero-filling rows >= M and masking stores.
+ *
+ * Conventions common to all entry points
+ *   - All matrix pointers are DEVICE pointers (hipMalloc'd or torch tensors).
+ *     The caller owns every buffer; the library never allocates, frees or
+ *     synchronises, and keeps no mutable global state, so calls are
+ *     thread-safe and reentrant.
+ *   - Matrices are row-major with an explicit leading dimension (elements
+ *     for bf16/fp32, bytes for 8-bit and packed 4-bit data).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Each invariant
+ *     call enqueues exactly one kernel on it and returns; device-side faults
+ *     surface at the caller's next synchronisation.
+ *   - Arguments are validated synchronously, before any HIP call; on any
+ *     error a non-zero bi_status is returned and nothing is launched.
+ *   - M == 0 or N == 0 is a valid no-op (pointers may then be NULL).
+ *     K == 0 writes C = +0 (the empty sum); A and B may then be NULL.
+ *   - Rows are read as whole 16-byte chunks: the library may read up to the
+ *     next 16-byte boundary past the end of each row (never past the row
+ *     pitch, which must be a multiple of 16 bytes).  Elements read that way
+ *     beyond K are zeroed before use.
+ *   - Base pointers of A, B, C (and of the fp4 scales) must be 16-byte
+ *     aligned.
+ *   - C must not alias A, B or the scales (not checked).
+ */
+#ifndef BIGEMM_H
+#define BIGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bi_status {
+    BI_OK = 0,
+    BI_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    BI_ERR_SHAPE = 2,       /* negative dimension, or K / N not a multiple of the
+                               format's block (fp8: K % 128, fp4: K % 32, N even) */
+    BI_ERR_STRIDE = 3,      /* a leading dimension is smaller than its row        */
+    BI_ERR_ALIGN = 4,       /* base pointer or row pitch not a multiple of 16 B   */
+    BI_ERR_UNSUPPORTED = 5, /* size beyond the library's limits, unknown dtype    */
+    BI_ERR_LAUNCH = 6,      /* the HIP launch itself failed                       */
+    BI_ERR_WORKSPACE = 7    /* split-K comparator: workspace missing or too small */
+} bi_status;
+
+typedef enum bi_dtype {
+    BI_BF16 = 0,            /* bf16 A x bf16 B                                    */
+    BI_FP8_BS = 1,          /* e4m3fn A (1x128 fp32 scales) x e4m3fn B (128x128)  */
+    BI_FP4_W = 2            /* bf16 A x e2m1 B with e4m3fn scales per 32 along K  */
+} bi_dtype;
+
+/* Introspection only: the schedule a (dtype, N, K) triple runs with. */
+typedef struct bi_schedule {
+    int32_t mfma_m, mfma_n, mfma_k; /* shape of the one MFMA instruction used      */
+    int32_t bm, bn;                 /* output tile of one workgroup                 */
+    int32_t bk;                     /* K consumed per pipeline stage                */
+    int32_t k_block;                /* K per accumulation block (scale granularity) */
+    int32_t waves;                  /* wavefronts per workgroup                     */
+    int32_t stages;                 /* global->LDS pipeline depth (stages)          */
+    int32_t id;                     /* schedule identifier                          */
+} bi_schedule;
+
+/* Largest supported extent of any single dimension (M, N or K). */
+#define BI_MAX_DIM ((int64_t)1 << 24)
+
+/*
+ * bf16 x bf16 -> bf16.
+ *   A : bf16 [M,K], row pitch lda >= K   (elements; lda % 8 == 0)
+ *   B : bf16 [K,N], row pitch ldb >= N   (elements; ldb % 8 == 0)
+ *   C : bf16 [M,N], row pitch ldc >= N   (elements; ldc % 8 == 0)
+ * Any K >= 0 is accepted; the K tail is zero-filled.
+ */
+bi_status bi_gemm_bf16(int64_t M, int64_t N, int64_t K,
+                       const uint16_t* A, int64_t lda,
+                       const uint16_t* B, int64_t ldb,
+                       uint16_t* C, int64_t ldc, void* stream);
+
+/*
+ * fp8 e4m3fn (OCP, "fn": no infinities) with fp32 block scales -> bf16.
+ * The fused dequantisation of section 3.2 of the lshu.cn article: the scales
+ * are applied inside the K loop, never in a separate pass.
+ *   A  : e4m3fn [M,K], row pitch lda >= K bytes (lda % 16 == 0)
+ *   sA : fp32 [M, K/128], row pitch ldsa >= K/128; scale of A[m, 128j .. 128j+127]
+ *   B  : e4m3fn [K,N], row pitch ldb >= N bytes (ldb % 16 == 0)
+ *   sB : fp32 [K/128, ceil(N/128)], row pitch ldsb >= ceil(N/128);
+ *        scale of the 128x128 block B[128i.., 128j..]
+ *   C  : bf16 [M,N], ldc >= N, ldc % 8 == 0
+ * Requires K % 128 == 0.  Value: C[m,n] = sum_kb sA[m,kb] sB[kb,n/128] *
+ * sum_{k in kb} dec(A[m,k]) dec(B[k,n]); each 128-long block sum is formed by
+ * the MFMA unit, then added as acc = fma(P_kb, sA*sB, acc) with kb ascending.
+ */
+bi_status bi_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
+                                  const uint8_t* A, int64_t lda,
+                                  const float* sA, int64_t ldsa,
+                                  const uint8_t* B, int64_t ldb,
+                                  const float* sB, int64_t ldsb,
+                                  uint16_t* C, int64_t ldc, void* stream);
+
+/*
+ * bf16 activations x fp4 e2m1 weights (weight-only quantisation) -> bf16.
+ *   A  : bf16 [M,K], lda >= K, lda % 8 == 0
+ *   Bq : packed e2m1 [K, N/2] bytes, row pitch ldbq >= N/2 (ldbq % 16 == 0);
+ *        byte j of row k = code(k, 2j) | code(k, 2j+1) << 4
+ *   sB : e4m3fn [K/32, N] bytes, row pitch ldsb >= N (ldsb % 16 == 0);
+ *        scale of B[32i .. 32i+31, n]
+ *   C  : bf16 [M,N], ldc >= N, ldc % 8 == 0
+ * Requires K % 32 == 0 and N even.  Each weight is dequantised to
+ * w = e2m1(code) * e4m3fn(scale) inside the K loop; the product has at most
+ * six significant bits, so it is exact in bf16, and then enters a bf16 MFMA.
+ */
+bi_status bi_gemm_fp4_w(int64_t M, int64_t N, int64_t K,
+                        const uint16_t* A, int64_t lda,
+                        const uint8_t* Bq, int64_t ldbq,
+                        const uint8_t* sB, int64_t ldsb,
+                        uint16_t* C, int64_t ldc, void* stream);
+
+/* The schedule (dtype, N, K) selects.  There is no M argument by design.
+ * Returns BI_ERR_NULL for out == NULL, BI_ERR_UNSUPPORTED for an unknown
+ * dtype, BI_ERR_SHAPE for invalid N or K. */
+bi_status bi_schedule_query(bi_dtype dtype, int64_t N, int64_t K, bi_schedule* out);
+
+/* Static string naming a status code ("BI_OK", ...); never NULL. */
+const char* bi_status_str(bi_status s);
+
+/* Library version, e.g. "libbigemm 0.1.0 gfx950". */
+const char* bi_version(void);
+
+/*
+ * NOT batch-invariant.  Comparator for measurement and for the negative
+ * control of the invariance checker only: the split-K GEMM that section
+ * "牺牲了什么" of the QbitAI article says batch invariance rules out, with the
+ * split count taken from M as the lshu.cn article's section 2.1 describes
+ * for library heuristics.  Same operands as bi_gemm_bf16.
+ *   workspace : device fp32 buffer of at least M*N*4 bytes (ws_bytes)
+ *   splits    : number of K pieces; 0 = choose from M (more pieces at small M)
+ * Enqueues a zero-fill kernel, the split kernel (fp32 atomics into the
+ * workspace) and a rounding kernel on `stream`.
+ */
+bi_status bi_gemm_bf16_splitk(int64_t M, int64_t N, int64_t K,
+                              const uint16_t* A, int64_t lda,
+                              const uint16_t* B, int64_t ldb,
+                              uint16_t* C, int64_t ldc,
+                              float* workspace, size_t ws_bytes,
+                              int splits, void* stream);
+
+/* Split count bi_gemm_bf16_splitk uses for splits == 0. */
+int bi_splitk_choose(int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BIGEMM_H */

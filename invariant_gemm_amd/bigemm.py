@@ -1,0 +1,175 @@
+"""Python binding of libbigemm (ctypes): argument marshalling only.
+
+Every function here forwards device pointers, sizes, row pitches and the
+current HIP stream of torch to the C ABI declared in ``include/bigemm.h``;
+all arithmetic runs in the library's HIP kernels.  Importing this module
+raises if ``libbigemm.so`` is missing -- there is no fallback path.
+
+torch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbigemm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libbigemm.so not found at {LIB_PATH}; build it first with "
+        "`python -m invariant_gemm_amd.build` (hipcc, gfx950)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_i64, _vp, _i32, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+
+STATUS = {0: "BI_OK", 1: "BI_ERR_NULL", 2: "BI_ERR_SHAPE", 3: "BI_ERR_STRIDE",
+          4: "BI_ERR_ALIGN", 5: "BI_ERR_UNSUPPORTED", 6: "BI_ERR_LAUNCH", 7: "BI_ERR_WORKSPACE"}
+BI_BF16, BI_FP8_BS, BI_FP4_W = 0, 1, 2
+
+
+class BiSchedule(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("mfma_m", "mfma_n", "mfma_k", "bm", "bn", "bk", "k_block", "waves", "stages", "id")]
+
+
+lib.bi_gemm_bf16.restype = _i32
+lib.bi_gemm_bf16.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+lib.bi_gemm_fp8_blockscaled.restype = _i32
+lib.bi_gemm_fp8_blockscaled.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                        _vp, _i64, _vp]
+lib.bi_gemm_fp4_w.restype = _i32
+lib.bi_gemm_fp4_w.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+lib.bi_gemm_bf16_splitk.restype = _i32
+lib.bi_gemm_bf16_splitk.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz,
+                                    _i32, _vp]
+lib.bi_splitk_choose.restype = _i32
+lib.bi_splitk_choose.argtypes = [_i64, _i64, _i64]
+lib.bi_schedule_query.restype = _i32
+lib.bi_schedule_query.argtypes = [_i32, _i64, _i64, ctypes.POINTER(BiSchedule)]
+lib.bi_status_str.restype = ctypes.c_char_p
+lib.bi_status_str.argtypes = [_i32]
+lib.bi_version.restype = ctypes.c_char_p
+lib.bi_version.argtypes = []
+
+
+class BigemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib.bi_status_str(status).decode()}")
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise BigemmError(status, what)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _mat(t: torch.Tensor, dtypes, name: str) -> torch.Tensor:
+    if t.dim() != 2:
+        raise ValueError(f"{name}: expected a 2-D tensor, got shape {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if t.numel() and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: rows must be contiguous (stride(1) == 1)")
+    return t
+
+
+def _ld(t: torch.Tensor) -> int:
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8, torch.float8_e4m3fn, torch.int8)
+
+
+def version() -> str:
+    return lib.bi_version().decode()
+
+
+def schedule(dtype: int, N: int, K: int) -> dict:
+    s = BiSchedule()
+    _check(lib.bi_schedule_query(dtype, N, K, ctypes.byref(s)), "bi_schedule_query")
+    return {n: getattr(s, n) for n, _ in BiSchedule._fields_}
+
+
+def _out(M, N, device, out):
+    if out is None:
+        return torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    return _mat(out, _BF16, "out")
+
+
+def gemm_bf16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = A . B (bf16 in/out) via bi_gemm_bf16 on torch's current stream."""
+    A = _mat(A, _BF16, "A")
+    B = _mat(B, _BF16, "B")
+    M, K = A.shape
+    if B.shape[0] != K:
+        raise ValueError("A and B inner dimensions differ")
+    N = B.shape[1]
+    C = _out(M, N, A.device, out)
+    _check(lib.bi_gemm_bf16(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
+                            C.data_ptr(), _ld(C), _stream()), "bi_gemm_bf16")
+    return C
+
+
+def gemm_fp8_blockscaled(A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB: torch.Tensor,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = (A * sA) . (B * sB) with e4m3fn codes and fp32 1x128 / 128x128 scales."""
+    A = _mat(A, _U8, "A")
+    B = _mat(B, _U8, "B")
+    sA = _mat(sA, (torch.float32,), "sA")
+    sB = _mat(sB, (torch.float32,), "sB")
+    M, K = A.shape
+    if B.shape[0] != K:
+        raise ValueError("A and B inner dimensions differ")
+    N = B.shape[1]
+    C = _out(M, N, A.device, out)
+    _check(lib.bi_gemm_fp8_blockscaled(M, N, K, A.data_ptr(), _ld(A), sA.data_ptr(), _ld(sA),
+                                       B.data_ptr(), _ld(B), sB.data_ptr(), _ld(sB),
+                                       C.data_ptr(), _ld(C), _stream()), "bi_gemm_fp8_blockscaled")
+    return C
+
+
+def gemm_fp4_w(A: torch.Tensor, Bq: torch.Tensor, sB: torch.Tensor, N: int,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = A . dequant(Bq, sB): bf16 activations, packed e2m1 weights, e4m3fn scales per 32 K."""
+    A = _mat(A, _BF16, "A")
+    Bq = _mat(Bq, _U8, "Bq")
+    sB = _mat(sB, _U8, "sB")
+    M, K = A.shape
+    if Bq.shape[0] != K:
+        raise ValueError("A and Bq inner dimensions differ")
+    C = _out(M, N, A.device, out)
+    _check(lib.bi_gemm_fp4_w(M, N, K, A.data_ptr(), _ld(A), Bq.data_ptr(), _ld(Bq),
+                             sB.data_ptr(), _ld(sB), C.data_ptr(), _ld(C), _stream()),
+           "bi_gemm_fp4_w")
+    return C
+
+
+def splitk_choose(M: int, N: int, K: int) -> int:
+    return int(lib.bi_splitk_choose(M, N, K))
+
+
+def gemm_bf16_splitk(A: torch.Tensor, B: torch.Tensor, workspace: torch.Tensor, splits: int = 0,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """NOT batch-invariant: the split-K comparator (fp32 atomics into `workspace`)."""
+    A = _mat(A, _BF16, "A")
+    B = _mat(B, _BF16, "B")
+    M, K = A.shape
+    N = B.shape[1]
+    C = _out(M, N, A.device, out)
+    if workspace.dtype != torch.float32 or not workspace.is_cuda:
+        raise TypeError("workspace must be a float32 device tensor")
+    _check(lib.bi_gemm_bf16_splitk(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
+                                   C.data_ptr(), _ld(C), workspace.data_ptr(),
+                                   workspace.numel() * 4, splits, _stream()), "bi_gemm_bf16_splitk")
+    return C

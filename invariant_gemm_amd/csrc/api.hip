@@ -1,0 +1,282 @@
+// api.hip -- the C ABI of libbigemm: argument validation, schedule table,
+// kernel dispatch.  Validation runs before any HIP call; an invalid call
+// returns a status and launches nothing.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/bigemm.h"
+#include "launch.h"
+
+namespace bigemm {
+namespace {
+
+// ------------------------------------------------------------------ schedules
+//
+// The schedule of a call is a function of (dtype, N, K) only.  M never
+// reaches this table, so the MFMA instruction, the K step and the order in
+// which an output element's K blocks are accumulated cannot depend on the
+// batch: the "all paths fixed at compile time, no runtime heuristic" rule of
+// section 3.1 of the lshu.cn article, applied per shape class.
+Schedule schedule_for(bi_dtype dt, int64_t N, int64_t K)
+{
+    (void)N;
+    (void)K;
+    Schedule s{};
+    switch (dt) {
+    case BI_BF16:
+        s = Schedule{/*id*/ 1, /*rb*/ 2, /*pf*/ 8, /*bm*/ 64, /*bn*/ 32, /*bk*/ 128, /*kblock*/ 32};
+        break;
+    case BI_FP8_BS:
+        s = Schedule{/*id*/ 2, /*rb*/ 2, /*pf*/ 8, /*bm*/ 64, /*bn*/ 16, /*bk*/ 128, /*kblock*/ 128};
+        break;
+    case BI_FP4_W:
+        s = Schedule{/*id*/ 3, /*rb*/ 2, /*pf*/ 8, /*bm*/ 64, /*bn*/ 32, /*bk*/ 128, /*kblock*/ 32};
+        break;
+    }
+    return s;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bi_status check_dims(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return BI_ERR_SHAPE;
+    if (M > BI_MAX_DIM || N > BI_MAX_DIM || K > BI_MAX_DIM)
+        return BI_ERR_UNSUPPORTED;
+    return BI_OK;
+}
+
+bi_status check_grid(int64_t M, int64_t N, const Schedule& s)
+{
+    const int64_t tiles = ((N + s.bn - 1) / s.bn) * ((M + s.bm - 1) / s.bm);
+    return tiles <= 0x7FFFFFFF ? BI_OK : BI_ERR_UNSUPPORTED;
+}
+
+bi_status launched(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_LAUNCH; }
+
+bi_status validate_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                        const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, bool* noop)
+{
+    *noop = false;
+    bi_status st = check_dims(M, N, K);
+    if (st != BI_OK)
+        return st;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return BI_OK;
+    }
+    if (!C || (K > 0 && (!A || !B)))
+        return BI_ERR_NULL;
+    if ((K > 0 && (lda < K || ldb < N)) || ldc < N)
+        return BI_ERR_STRIDE;
+    if (!aligned16(C) || ldc % 8)
+        return BI_ERR_ALIGN;
+    if (K > 0 && (!aligned16(A) || !aligned16(B) || lda % 8 || ldb % 8))
+        return BI_ERR_ALIGN;
+    return BI_OK;
+}
+
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+bi_status validate_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                       const float* sA, int64_t ldsa, const uint8_t* B, int64_t ldb,
+                       const float* sB, int64_t ldsb, uint16_t* C, int64_t ldc, bool* noop)
+{
+    *noop = false;
+    bi_status st = check_dims(M, N, K);
+    if (st != BI_OK)
+        return st;
+    if (K % 128)
+        return BI_ERR_SHAPE;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return BI_OK;
+    }
+    const int64_t kb = K / 128, nb = (N + 127) / 128;
+    if (!C || (K > 0 && (!A || !B || !sA || !sB)))
+        return BI_ERR_NULL;
+    if ((K > 0 && (lda < K || ldb < N || ldsa < kb || ldsb < nb)) || ldc < N)
+        return BI_ERR_STRIDE;
+    if (!aligned16(C) || ldc % 8)
+        return BI_ERR_ALIGN;
+    if (K > 0 && (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16 || !aligned4(sA) ||
+                  !aligned4(sB)))
+        return BI_ERR_ALIGN;
+    return BI_OK;
+}
+
+bi_status validate_fp4(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                       const uint8_t* Bq, int64_t ldbq, const uint8_t* sB, int64_t ldsb,
+                       uint16_t* C, int64_t ldc, bool* noop)
+{
+    *noop = false;
+    bi_status st = check_dims(M, N, K);
+    if (st != BI_OK)
+        return st;
+    if (K % 32 || N % 2)
+        return BI_ERR_SHAPE;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return BI_OK;
+    }
+    if (!C || (K > 0 && (!A || !Bq || !sB)))
+        return BI_ERR_NULL;
+    if ((K > 0 && (lda < K || ldbq < N / 2 || ldsb < N)) || ldc < N)
+        return BI_ERR_STRIDE;
+    if (!aligned16(C) || ldc % 8)
+        return BI_ERR_ALIGN;
+    if (K > 0 && (!aligned16(A) || !aligned16(Bq) || !aligned16(sB) || lda % 8 || ldbq % 16 ||
+                  ldsb % 16))
+        return BI_ERR_ALIGN;
+    return BI_OK;
+}
+
+}  // namespace
+}  // namespace bigemm
+
+using namespace bigemm;
+
+extern "C" {
+
+const char* bi_status_str(bi_status s)
+{
+    switch (s) {
+    case BI_OK: return "BI_OK";
+    case BI_ERR_NULL: return "BI_ERR_NULL";
+    case BI_ERR_SHAPE: return "BI_ERR_SHAPE";
+    case BI_ERR_STRIDE: return "BI_ERR_STRIDE";
+    case BI_ERR_ALIGN: return "BI_ERR_ALIGN";
+    case BI_ERR_UNSUPPORTED: return "BI_ERR_UNSUPPORTED";
+    case BI_ERR_LAUNCH: return "BI_ERR_LAUNCH";
+    case BI_ERR_WORKSPACE: return "BI_ERR_WORKSPACE";
+    }
+    return "BI_ERR_UNKNOWN";
+}
+
+const char* bi_version(void) { return "libbigemm 0.1.0 gfx950"; }
+
+bi_status bi_schedule_query(bi_dtype dtype, int64_t N, int64_t K, bi_schedule* out)
+{
+    if (!out)
+        return BI_ERR_NULL;
+    if (dtype != BI_BF16 && dtype != BI_FP8_BS && dtype != BI_FP4_W)
+        return BI_ERR_UNSUPPORTED;
+    if (N < 0 || K < 0)
+        return BI_ERR_SHAPE;
+    if (N > BI_MAX_DIM || K > BI_MAX_DIM)
+        return BI_ERR_UNSUPPORTED;
+    if ((dtype == BI_FP8_BS && K % 128) || (dtype == BI_FP4_W && (K % 32 || N % 2)))
+        return BI_ERR_SHAPE;
+    const Schedule s = schedule_for(dtype, N, K);
+    memset(out, 0, sizeof *out);
+    out->mfma_m = 16;
+    out->mfma_n = 16;
+    out->mfma_k = dtype == BI_FP8_BS ? 128 : 32;
+    out->bm = s.bm;
+    out->bn = s.bn;
+    out->bk = s.bk;
+    out->k_block = s.kblock;
+    out->waves = 4;
+    out->stages = s.pf;
+    out->id = s.id;
+    return BI_OK;
+}
+
+bi_status bi_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                       const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, void* stream)
+{
+    bool noop;
+    bi_status st = validate_bf16(M, N, K, A, lda, B, ldb, C, ldc, &noop);
+    if (st != BI_OK || noop)
+        return st;
+    const Schedule s = schedule_for(BI_BF16, N, K);
+    if ((st = check_grid(M, N, s)) != BI_OK)
+        return st;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, B, ldb, nullptr, 0, C, ldc};
+    return launched(launch_bf16(a, s, (hipStream_t)stream));
+}
+
+bi_status bi_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                  const float* sA, int64_t ldsa, const uint8_t* B, int64_t ldb,
+                                  const float* sB, int64_t ldsb, uint16_t* C, int64_t ldc,
+                                  void* stream)
+{
+    bool noop;
+    bi_status st = validate_fp8(M, N, K, A, lda, sA, ldsa, B, ldb, sB, ldsb, C, ldc, &noop);
+    if (st != BI_OK || noop)
+        return st;
+    const Schedule s = schedule_for(BI_FP8_BS, N, K);
+    if ((st = check_grid(M, N, s)) != BI_OK)
+        return st;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, sA, ldsa, B, ldb, sB, ldsb, C, ldc};
+    return launched(launch_fp8bs(a, s, (hipStream_t)stream));
+}
+
+bi_status bi_gemm_fp4_w(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                        const uint8_t* Bq, int64_t ldbq, const uint8_t* sB, int64_t ldsb,
+                        uint16_t* C, int64_t ldc, void* stream)
+{
+    bool noop;
+    bi_status st = validate_fp4(M, N, K, A, lda, Bq, ldbq, sB, ldsb, C, ldc, &noop);
+    if (st != BI_OK || noop)
+        return st;
+    const Schedule s = schedule_for(BI_FP4_W, N, K);
+    if ((st = check_grid(M, N, s)) != BI_OK)
+        return st;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, Bq, ldbq, sB, ldsb, C, ldc};
+    return launched(launch_fp4w(a, s, (hipStream_t)stream));
+}
+
+int bi_splitk_choose(int64_t M, int64_t N, int64_t K)
+{
+    (void)N;
+    // More K pieces for larger batches, two at least: the batch-dependent
+    // choice the invariant path forbids.  Capped by the number of 128-row
+    // K stages.
+    int64_t lg = 0;
+    while (((int64_t)1 << lg) < M + 1)
+        ++lg;
+    int64_t s = 2 * lg;
+    if (s < 2)
+        s = 2;
+    const int64_t nst = (K + 127) / 128;
+    if (s > nst)
+        s = nst;
+    if (s < 1)
+        s = 1;
+    return (int)s;
+}
+
+bi_status bi_gemm_bf16_splitk(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                              const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc,
+                              float* workspace, size_t ws_bytes, int splits, void* stream)
+{
+    bool noop;
+    bi_status st = validate_bf16(M, N, K, A, lda, B, ldb, C, ldc, &noop);
+    if (st != BI_OK || noop)
+        return st;
+    if (splits < 0)
+        return BI_ERR_SHAPE;
+    if (!workspace)
+        return BI_ERR_WORKSPACE;
+    if (ws_bytes < (size_t)M * (size_t)N * sizeof(float))
+        return BI_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 3u) != 0)
+        return BI_ERR_ALIGN;
+    const int64_t nst = (K + 127) / 128;
+    int S = splits == 0 ? bi_splitk_choose(M, N, K) : splits;
+    if (nst == 0)
+        S = 1;
+    else if (S > nst)
+        S = (int)nst;
+    if (S > 65535 || M * N > ((int64_t)1 << 31))
+        return BI_ERR_UNSUPPORTED;
+    const Schedule s = schedule_for(BI_BF16, N, K);
+    if ((st = check_grid(M, N, s)) != BI_OK)
+        return st;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, B, ldb, nullptr, 0, C, ldc};
+    return launched(launch_bf16_splitk(a, s, workspace, S, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// common.h -- device helpers shared by the libbigemm kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bigemm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;   // CDNA wavefront width
+constexpr int kXcds = 8;    // MI355X: 8 accelerator dies, each with its own L2
+
+// One MFMA shape for all bf16 products: 16x16 output block, K = 32 per
+// instruction, fp32 accumulate.  Operand lane layout (64 lanes):
+//   A: lane (i = l % 16, g = l / 16) holds A[i][8g .. 8g+7]
+//   B: lane (n = l % 16, g = l / 16) holds B[8g .. 8g+7][n]
+//   D: lane (n = l % 16, g = l / 16), register j holds D[4g + j][n]
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// fp32 -> bf16, round to nearest even, subnormals kept, NaN -> quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return ((u >> 16) & 0x8000u) | 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Workgroups are dispatched round-robin over the XCDs (id % 8).  Remap the
+// dispatch id so that each XCD receives a contiguous range of tile ids: the
+// tiles sharing B columns (and the M tiles of one N strip) then meet in the
+// same L2.  Only which workgroup computes which tile changes, never the
+// arithmetic of any output element.
+__device__ __forceinline__ int xcd_remap(int b, int G)
+{
+    const int G8 = G - G % kXcds;
+    if (b >= G8)
+        return b;
+    return (b % kXcds) * (G8 / kXcds) + b / kXcds;
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p)
+{
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+}  // namespace bigemm

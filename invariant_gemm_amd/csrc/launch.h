@@ -1,0 +1,34 @@
+// launch.h -- internal interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bigemm {
+
+// A kernel schedule.  Chosen from (dtype, N, K) only; see schedule_for().
+struct Schedule {
+    int id;       // table entry
+    int rb;       // 16-row MFMA blocks per wave along M
+    int pf;       // B stages kept in flight (register prefetch depth)
+    int bm, bn;   // workgroup output tile
+    int bk;       // K rows per pipeline stage
+    int kblock;   // K per accumulation / scale block
+};
+
+struct GemmArgs {
+    int M, N, K;
+    const void* A;  int64_t lda;
+    const void* sA; int64_t ldsa;
+    const void* B;  int64_t ldb;
+    const void* sB; int64_t ldsb;
+    uint16_t* C;    int64_t ldc;
+};
+
+hipError_t launch_bf16(const GemmArgs& a, const Schedule& s, hipStream_t stream);
+hipError_t launch_fp8bs(const GemmArgs& a, const Schedule& s, hipStream_t stream);
+hipError_t launch_fp4w(const GemmArgs& a, const Schedule& s, hipStream_t stream);
+hipError_t launch_bf16_splitk(const GemmArgs& a, const Schedule& s, float* ws, int splits,
+                              hipStream_t stream);
+
+}  // namespace bigemm

@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects every invalid argument with the documented
+status before any HIP call (the pointers below are never dereferenced)."""
+import ctypes
+import inspect
+import os
+import re
+
+import pytest
+
+from invariant_gemm_amd import bigemm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "bigemm.h")
+
+OK, NULL, SHAPE, STRIDE, ALIGN, UNSUP, LAUNCH, WS = range(8)
+P = 0x10000          # fake, 16-byte aligned "device" address; never dereferenced
+lib = bigemm.lib
+
+
+def _declared():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bi_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {"bi_gemm_bf16", "bi_gemm_fp8_blockscaled", "bi_gemm_fp4_w", "bi_schedule_query",
+            "bi_status_str", "bi_gemm_bf16_splitk"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code, name in bigemm.STATUS.items():
+        assert lib.bi_status_str(code).decode() == name
+    assert lib.bi_status_str(99).decode() == "BI_ERR_UNKNOWN"
+    assert bigemm.version().startswith("libbigemm")
+
+
+def bf16(M, N, K, A=P, lda=None, B=P, ldb=None, C=P, ldc=None):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return lib.bi_gemm_bf16(M, N, K, A, lda, B, ldb, C, ldc, None)
+
+
+def test_bf16_validation():
+    assert bf16(-1, 8, 8) == SHAPE
+    assert bf16(8, -1, 8) == SHAPE
+    assert bf16(8, 8, -1) == SHAPE
+    assert bf16(8, (1 << 24) + 1, 8) == UNSUP
+    assert bf16(0, 8, 8, A=None, B=None, C=None) == OK        # empty: no-op
+    assert bf16(8, 0, 8, A=None, B=None, C=None) == OK
+    assert bf16(8, 8, 8, A=None) == NULL
+    assert bf16(8, 8, 8, B=None) == NULL
+    assert bf16(8, 8, 8, C=None) == NULL
+    assert bf16(8, 8, 16, lda=8) == STRIDE
+    assert bf16(8, 16, 8, ldb=8) == STRIDE
+    assert bf16(8, 16, 8, ldc=8) == STRIDE
+    assert bf16(8, 8, 8, A=P + 2) == ALIGN
+    assert bf16(8, 8, 8, B=P + 8) == ALIGN
+    assert bf16(8, 8, 8, C=P + 4) == ALIGN
+    assert bf16(8, 8, 12) == ALIGN            # lda = 12: row pitch 24 B
+
+
+def test_bf16_k0_needs_no_operands():
+    # K == 0 with NULL A/B passes validation; it would launch (C = 0), so
+    # only the validation order is checked here: a NULL C is still rejected.
+    assert bf16(4, 8, 0, A=None, B=None, C=None) == NULL
+
+
+def fp8(M, N, K, A=P, lda=None, sA=P, ldsa=None, B=P, ldb=None, sB=P, ldsb=None, C=P, ldc=None):
+    lda = K if lda is None else lda
+    ldsa = K // 128 if ldsa is None else ldsa
+    ldb = N if ldb is None else ldb
+    ldsb = (N + 127) // 128 if ldsb is None else ldsb
+    ldc = N if ldc is None else ldc
+    return lib.bi_gemm_fp8_blockscaled(M, N, K, A, lda, sA, ldsa, B, ldb, sB, ldsb, C, ldc, None)
+
+
+def test_fp8_validation():
+    assert fp8(-1, 16, 128) == SHAPE
+    assert fp8(4, 16, 100) == SHAPE          # K % 128
+    assert fp8(0, 16, 128, A=None) == OK
+    assert fp8(4, 16, 128, sA=None) == NULL
+    assert fp8(4, 16, 128, sB=None) == NULL
+    assert fp8(4, 16, 256, ldsa=1) == STRIDE
+    assert fp8(4, 300, 128, ldsb=2) == STRIDE
+    assert fp8(4, 16, 128, lda=120) == STRIDE
+    assert fp8(4, 16, 128, lda=136) == ALIGN   # 136 B pitch
+    assert fp8(4, 24, 128) == ALIGN            # ldb = 24 B pitch
+    assert fp8(4, 16, 128, sA=P + 2) == ALIGN  # fp32 scales need 4-byte alignment
+
+
+def fp4(M, N, K, A=P, lda=None, Bq=P, ldbq=None, sB=P, ldsb=None, C=P, ldc=None):
+    lda = K if lda is None else lda
+    ldbq = N // 2 if ldbq is None else ldbq
+    ldsb = N if ldsb is None else ldsb
+    ldc = N if ldc is None else ldc
+    return lib.bi_gemm_fp4_w(M, N, K, A, lda, Bq, ldbq, sB, ldsb, C, ldc, None)
+
+
+def test_fp4_validation():
+    assert fp4(4, 64, 48) == SHAPE             # K % 32
+    assert fp4(4, 63, 64) == SHAPE             # odd N
+    assert fp4(4, 64, 64, Bq=None) == NULL
+    assert fp4(4, 64, 64, sB=None) == NULL
+    assert fp4(4, 64, 64, ldbq=16) == STRIDE
+    assert fp4(4, 64, 64, ldsb=32) == STRIDE
+    assert fp4(4, 48, 64) == ALIGN             # ldbq = 24 B
+    assert fp4(4, 64, 64, sB=P + 1) == ALIGN
+    assert fp4(0, 64, 64, A=None, Bq=None, sB=None, C=None) == OK
+
+
+def test_splitk_validation():
+    f = lib.bi_gemm_bf16_splitk
+    assert f(4, 8, 128, P, 128, P, 8, P, 8, None, 1 << 20, 0, None) == WS
+    assert f(4, 8, 128, P, 128, P, 8, P, 8, P, 4 * 8 * 4 - 1, 0, None) == WS
+    assert f(4, 8, 128, P, 128, P, 8, P, 8, P, 1 << 20, -1, None) == SHAPE
+    assert f(4, 8, 128, P + 2, 128, P, 8, P, 8, P, 1 << 20, 0, None) == ALIGN
+    # the comparator's split count follows M -- by design, unlike the invariant path
+    ks = [bigemm.splitk_choose(m, 8192, 8192) for m in (1, 2, 4, 8, 16, 256)]
+    assert len(set(ks)) > 1 and all(1 <= s <= 64 for s in ks)
+
+
+def test_schedule_has_no_m_argument():
+    # the schedule is a function of (dtype, N, K) by construction: the C
+    # signature has exactly four parameters and none of them is M
+    assert len(lib.bi_schedule_query.argtypes) == 4
+    hdr = open(HDR).read()
+    decl = re.search(r"bi_status bi_schedule_query\(([^)]*)\)", hdr).group(1)
+    params = [p.strip().split()[-1].lstrip("*") for p in decl.split(",")]
+    assert params == ["dtype", "N", "K", "out"]
+    for dt in (bigemm.BI_BF16, bigemm.BI_FP8_BS, bigemm.BI_FP4_W):
+        s = bigemm.schedule(dt, 8192, 8192)
+        assert s["mfma_m"] == 16 and s["waves"] == 4
+    assert lib.bi_schedule_query(7, 8192, 8192, ctypes.byref(bigemm.BiSchedule())) == UNSUP
+    assert lib.bi_schedule_query(0, 8192, 8192, None) == NULL
+    assert lib.bi_schedule_query(1, 8192, 100, ctypes.byref(bigemm.BiSchedule())) == SHAPE
