@@ -130,6 +130,29 @@ def traffic_from_profiles(kernel_src: str, algorithmic_bytes: float):
     return d.get("hbm_bytes_per_launch")
 
 
+# ------------------------------------------------------------------ counters
+
+COPY_BYTES = 256 << 20
+
+
+def pmc_probe(torch, wl):
+    """Launch sequence for the HBM-traffic counters: a plain device copy of
+    COPY_BYTES (the calibration reference: it must fetch and write exactly
+    that many bytes), then three launches per M of the swept GEMM, each on a
+    different rotated copy of B."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for M in SWEEP_C2:
+        for _ in range(3):
+            wl.launch(M)
+    torch.cuda.synchronize()
+    log("pmc probe done: copy", COPY_BYTES, "bytes x3, then 3 launches per M", SWEEP_C2)
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -140,6 +163,8 @@ def main():
     ap.add_argument("--rounds", type=int, default=20, help="rounds per-M timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-M and comparator legs")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="only run a known-size copy plus 3 launches per M (for rocprofv3 --pmc)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -155,6 +180,9 @@ def main():
     log(f"device: {dev.name}, CUs {dev.multi_processor_count}")
 
     wl = C2Workload(torch, bigemm, inputs)
+    if args.pmc_probe:
+        pmc_probe(torch, wl)
+        return
     step_flops = sum(flops(M, N2, K2) for M in SWEEP_C2)
     step_bytes = sum(bytes_bf16(M, N2, K2) for M in SWEEP_C2)
 

@@ -55,3 +55,27 @@ __device__ __forceinline__ u32x4 ldg16(const void* p)
 }
 
 }  // namespace bigemm
+
+namespace bigemm {
+
+// Raw buffer resource (gfx9 layout): 48-bit base, stride 0, byte extent,
+// dword3 = 0x00020000.  A load whose offset is at or beyond `bytes` returns
+// zero and touches no memory -- the M / K tails are handled this way.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+// Byte extent clamp for a buffer resource.
+__device__ __forceinline__ uint32_t clamp_bytes(int64_t b)
+{
+    return b <= 0 ? 0u : (b >= 0x7FFFFFFF ? 0x7FFFFFFFu : (uint32_t)b);
+}
+
+}  // namespace bigemm

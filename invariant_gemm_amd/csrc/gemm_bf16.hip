@@ -12,21 +12,22 @@
 //     the MFMA results of K-steps 0, 1, 2, ... in that order -- no split-K,
 //     no stream-K, no atomics (the split-K conflict described in section
 //     "牺牲了什么" of the QbitAI article);
-//   * rows >= M are zero-filled or skipped as whole 16-row MFMA blocks, which
-//     cannot change another row's result: an MFMA output row depends only on
-//     its own A row.
+//   * rows >= M are zero-filled (buffer loads past the operand's extent
+//     return zero) or skipped as whole 16-row MFMA blocks, which cannot change
+//     another row's result: an MFMA output row depends only on its own A row.
 //
 // Workgroup: 256 threads = 4 waves, output tile BM x 32 (BM = 32 * RB).
 //   wave w: 16-column block cb = w & 1, row group rg = w >> 1 with RB
 //   16-row blocks each.  Small M is served by N-tiling alone: N/32 workgroups
 //   stream disjoint column strips of B.
 //
-// Data path per pipeline stage of 128 K rows:
-//   B [K,N] row-major (N contiguous) --global_load_dwordx4--> registers
-//   (PF stages in flight) --k-pair pack--> LDS as [k/8][n][8] (k contiguous,
-//   XOR-swizzled 16-byte slots) --ds_read_b128--> MFMA B operand.
-//   A [M,K] row-major (K contiguous) --global_load_dwordx4--> MFMA A operand,
-//   one stage ahead.
+// Data path per pipeline stage of 128 K rows (PF stages in flight):
+//   A [M,K] --buffer_load_dwordx4--> VGPR --ds_write_b128--> LDS [m][k]
+//     (16-byte chunks XOR-swizzled by row) --ds_read_b128--> MFMA A operand
+//   B [K,N] --buffer_load_dwordx4--> VGPR --ds_write_b128--> LDS [k][n]
+//     (rows as in memory) --ds_read_b64_tr_b16 x2--> MFMA B operand
+// All global loads are issued unconditionally and consumed in issue order,
+// so the wait counters stay exact and PF stages remain in flight.
 #include "common.h"
 #include "launch.h"
 
@@ -37,25 +38,27 @@ constexpr int BN = 32;                   // columns per workgroup
 constexpr int BKS = 128;                 // K rows per stage
 constexpr int KSTEP = 32;                // K per MFMA
 constexpr int KS_PER_ST = BKS / KSTEP;   // 4
-constexpr int STAGE_DW = (BKS / 8) * BN * 4;   // 16 octets x 32 cols x 4 dwords = 8 KiB
+constexpr int B_PITCH = BN * 2 + 16;     // LDS bytes per B row (padded against bank conflicts)
+constexpr int B_STAGE = BKS * B_PITCH;
 
-// Physical 16-byte slot of column c in k-octet o.  The XOR keeps each aligned
-// group of 8 columns inside its group (so the 8-lane phases of ds_read_b128
-// stay conflict-free) and spreads the k-pair writes over all banks.
-__device__ __forceinline__ int swz_col(int o, int c)
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint8_t* lds_byte_ptr)
 {
-    return (c & ~7) | (((c & 7) ^ (4 * o + (c >> 3))) & 7);
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(__attribute__((address_space(3))) uint8_t*)lds_byte_ptr);
+    return __builtin_bit_cast(u32x2, v);
 }
 
-// Zero the bf16 elements [valid, 8) of a 16-byte chunk (K tail).
+// Zero the bf16 elements [valid, 8) of an 8-element fragment (K tail).
 __device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
 {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        if (2 * d >= valid)
-            v[d] = 0;
-        else if (2 * d + 1 >= valid)
-            v[d] &= 0xFFFFu;
+        const uint32_t lo = (2 * d < valid) ? 0xFFFFu : 0u;
+        const uint32_t hi = (2 * d + 1 < valid) ? 0xFFFF0000u : 0u;
+        v[d] &= (lo | hi);
     }
     return v;
 }
@@ -71,9 +74,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     uint16_t* __restrict__ C, int64_t ldc,
     float* __restrict__ ws, int m_tiles, int splits)
 {
-    static_assert(PF % 2 == 0, "prefetch depth must be even (LDS double buffer parity)");
+    static_assert(PF % 2 == 0, "the LDS double buffer is indexed by stage parity");
     constexpr int BM = 32 * RB;
-    __shared__ __attribute__((aligned(16))) uint32_t lds[2 * STAGE_DW];
+    constexpr int A_STAGE = BM * BKS * 2;        // bytes
+    constexpr int A_LD = BM / 16;                // 16-byte A chunks per lane per stage
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (A_STAGE + B_STAGE)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -85,7 +90,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     const int m0 = mt * BM;
 
     const int nst_all = (K + BKS - 1) / BKS;
-    const int nks = (K + KSTEP - 1) / KSTEP;
     int st_lo = 0, st_hi = nst_all;
     if constexpr (SPLIT) {
         st_lo = (int)((int64_t)nst_all * blockIdx.y / splits);
@@ -93,123 +97,131 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     }
     const int nst = st_hi - st_lo;
 
-    // ---- B staging: this lane moves rows 2q, 2q+1 of each stage, 8 columns.
-    const int lq = (lane >> 2) + 16 * wave;   // k-pair within the stage, 0..63
-    const int lc = lane & 3;                   // 8-column group, 0..3
-    const int bcol = n0 + 8 * lc;
-    const bool bcol_ok = bcol < N;
-    const uint16_t* bsrc = B + (int64_t)(st_lo * BKS + 2 * lq) * ldb + (bcol_ok ? bcol : 0);
-    const int kpair0 = st_lo * BKS + 2 * lq;   // K row of this lane's first row
-    const int wo = lq >> 2;
-    const int wp = lq & 3;
-    const int wbase = wo * BN * 4 + wp;
+    const int kpad = (K + 7) & ~7;
+    const int npad = (N + 7) & ~7;
+    const int rows_valid = M - m0 < BM ? M - m0 : BM;
+
+    // ---- A staging map: chunk c = j*256 + tid -> row c/16, 16-byte k-chunk
+    //      (c % 16) ^ (row % 8) of the stage; LDS slot c.
+    uint32_t a_voff[A_LD];
+#pragma unroll
+    for (int j = 0; j < A_LD; ++j) {
+        const int c = j * 256 + tid;
+        const int row = c >> 4;
+        const int kc = (c & 15) ^ (row & 7);
+        a_voff[j] = (uint32_t)(row * lda + kc * 8) * 2u;
+    }
+    // ---- B staging map: rows 2q, 2q+1 of the stage, 16-byte column chunk lc.
+    const int q = tid >> 2;
+    const int lc = tid & 3;
+    const uint32_t b_voff = (uint32_t)(2 * q * ldb + 8 * lc) * 2u;
+    const uint32_t b_ldb2 = (uint32_t)ldb * 2u;
+    const int b_lds = 2 * q * B_PITCH + lc * 16;
 
     // ---- MFMA role.
     const int cb = wave & 1;
     const int rg = wave >> 1;
     const int li = lane & 15;
     const int lg = lane >> 4;
-    const int rbase = m0 + rg * 16 * RB;
-    int nrb = (M - rbase + 15) >> 4;
+    const int rbase = rg * 16 * RB;          // first tile row of this wave
+    int nrb = (rows_valid - rbase + 15) >> 4;
     nrb = nrb < 0 ? 0 : (nrb > RB ? RB : nrb);
 
-    int rofs[KS_PER_ST];
-#pragma unroll
-    for (int ks = 0; ks < KS_PER_ST; ++ks) {
-        const int o = ks * 4 + lg;
-        rofs[ks] = (o * BN + swz_col(o, cb * 16 + li)) * 4;
-    }
-
-    const uint16_t* arow[RB];
-    bool arow_ok[RB];
+    int a_rd[RB][KS_PER_ST];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
         const int row = rbase + 16 * r + li;
-        arow_ok[r] = row < M;
-        arow[r] = A + (int64_t)(arow_ok[r] ? row : 0) * lda + 8 * lg;
+#pragma unroll
+        for (int ks = 0; ks < KS_PER_ST; ++ks)
+            a_rd[r][ks] = (row * 16 + ((ks * 4 + lg) ^ (row & 7))) * 16;
     }
+    // transposed B reads: within 16-lane group lg, lane li points at row
+    // 8*lg + 4*half + li/4 of the k-step, columns cb*16 + 4*(li%4) .. +3
+    const int b_rd = (8 * lg + (li >> 2)) * B_PITCH + cb * 32 + (li & 3) * 8;
 
+    u32x4 areg[PF][A_LD];
     u32x4 breg[PF][2];
-    u32x4 areg[2][KS_PER_ST][RB];
     f32x4 acc[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r)
         acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto load_b = [&](int s, u32x4 (&dst)[2]) {   // s: stage index relative to st_lo
-        const int k = kpair0 + s * BKS;
-        const uint16_t* p = bsrc + (int64_t)s * BKS * ldb;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        dst[0] = (bcol_ok && k < K) ? ldg16(p) : z;
-        dst[1] = (bcol_ok && k + 1 < K) ? ldg16(p + ldb) : z;
-    };
-    auto load_a = [&](int s, u32x4 (&dst)[KS_PER_ST][RB]) {
+    auto issue = [&](int s, u32x4 (&ar)[A_LD], u32x4 (&br)[2]) {
+        // stages past this workgroup's range get an empty extent: no traffic
+        const bool live = s < nst;
+        const int kst = (st_lo + s) * BKS;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+            A + (int64_t)m0 * lda + kst,
+            live ? clamp_bytes(((int64_t)(rows_valid - 1) * lda + kpad - kst) * 2) : 0u);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+            B + (int64_t)kst * ldb + n0,
+            live ? clamp_bytes(((int64_t)(K - 1 - kst) * ldb + npad - n0) * 2) : 0u);
 #pragma unroll
-        for (int ks = 0; ks < KS_PER_ST; ++ks) {
-            const int k = (st_lo + s) * BKS + ks * KSTEP + 8 * lg;
-#pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (r < nrb && arow_ok[r] && k < K) {
-                    v = ldg16(arow[r] + (k - 8 * lg));
-                    if (k + 8 > K)
-                        v = keep_first(v, K - k);
-                }
-                dst[ks][r] = v;
-            }
-        }
+        for (int j = 0; j < A_LD; ++j)
+            ar[j] = buf_load16(ra, a_voff[j]);
+        br[0] = buf_load16(rb, b_voff);
+        br[1] = buf_load16(rb, b_voff + b_ldb2);
     };
 
-    // prologue
+    // prologue: PF stages in flight
 #pragma unroll
     for (int p = 0; p < PF; ++p)
-        if (p < nst)
-            load_b(p, breg[p]);
-    if (nst > 0)
-        load_a(0, areg[0]);
+        issue(p, areg[p], breg[p]);
 
-    for (int s0 = 0; s0 < nst; s0 += PF) {
+    // The stage count is padded to a multiple of PF so that every pass of the
+    // unrolled body issues and consumes the same loads; padding stages have an
+    // empty extent, so their LDS tiles are zero.  The MFMA chain is
+    // branch-free: every wave runs every K step of every stage.  A step whose
+    // operands are zero (padding stage, K tail, rows past M) adds an exact
+    // zero, and the sequence of steps depends on K only.
+    const int nst_pad = (nst + PF - 1) / PF * PF;
+    for (int s0 = 0; s0 < nst_pad; s0 += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
             const int s = s0 + p;
-            if (s >= nst)
-                break;
-            uint32_t* buf = lds + (p & 1) * STAGE_DW;
-            // k-pair pack: dword = (B[k][n], B[k+1][n]) for the lane's 8 columns
+            uint8_t* abuf = smem + (p & 1) * (A_STAGE + B_STAGE);
+            uint8_t* bbuf = abuf + A_STAGE;
+            const int kst = (st_lo + s) * BKS;
+            if (kst + BKS > K) {
+                // K tail: zero the A elements at k >= K (the row pitch past K
+                // may hold anything; B rows past K already load as zero)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t r0 = breg[p][0][j >> 1];
-                const uint32_t r1 = breg[p][1][j >> 1];
-                const uint32_t v = (j & 1) ? ((r0 >> 16) | (r1 & 0xFFFF0000u))
-                                           : ((r0 & 0xFFFFu) | (r1 << 16));
-                buf[wbase + swz_col(wo, 8 * lc + j) * 4] = v;
+                for (int j = 0; j < A_LD; ++j) {
+                    const int c = j * 256 + tid;
+                    const int kc = (c & 15) ^ ((c >> 4) & 7);
+                    areg[p][j] = keep_first(areg[p][j], K - (kst + 8 * kc));
+                }
             }
-            if (s + PF < nst)
-                load_b(s + PF, breg[p]);
-            if (s + 1 < nst)
-                load_a(s + 1, areg[(p + 1) & 1]);
+#pragma unroll
+            for (int j = 0; j < A_LD; ++j)
+                *reinterpret_cast<u32x4*>(abuf + (j * 256 + tid) * 16) = areg[p][j];
+            *reinterpret_cast<u32x4*>(bbuf + b_lds) = breg[p][0];
+            *reinterpret_cast<u32x4*>(bbuf + b_lds + B_PITCH) = breg[p][1];
+            issue(s + PF, areg[p], breg[p]);
             __syncthreads();
 #pragma unroll
             for (int ks = 0; ks < KS_PER_ST; ++ks) {
-                if ((st_lo + s) * KS_PER_ST + ks < nks) {
-                    const u32x4 bfrag = *reinterpret_cast<const u32x4*>(buf + rofs[ks]);
+                const uint8_t* bp = bbuf + b_rd + ks * KSTEP * B_PITCH;
+                const u32x2 b0 = ds_read_tr16(bp);
+                const u32x2 b1 = ds_read_tr16(bp + 4 * B_PITCH);
+                const u32x4 bfrag = {b0[0], b0[1], b1[0], b1[1]};
 #pragma unroll
-                    for (int r = 0; r < RB; ++r)
-                        if (r < nrb)
-                            acc[r] = mfma_bf16(areg[p & 1][ks][r], bfrag, acc[r]);
+                for (int r = 0; r < RB; ++r) {
+                    const u32x4 afrag = *reinterpret_cast<const u32x4*>(abuf + a_rd[r][ks]);
+                    acc[r] = mfma_bf16(afrag, bfrag, acc[r]);
                 }
             }
         }
     }
 
-    // epilogue
+    // epilogue: lane (li, lg) holds rows 4*lg + j of each row block, column li
     const int col = n0 + cb * 16 + li;
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
         if (r < nrb) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = rbase + 16 * r + 4 * lg + j;
+                const int row = m0 + rbase + 16 * r + 4 * lg + j;
                 if (row < M && col < N) {
                     if constexpr (SPLIT)
                         atomicAdd(ws + (int64_t)row * N + col, acc[r][j]);
@@ -270,8 +282,7 @@ hipError_t launch_bf16(const GemmArgs& a, const Schedule& s, hipStream_t stream)
 {
     switch (s.rb) {
     case 1: return launch_rb<1, 8>(a, stream);
-    case 2: return launch_rb<2, 8>(a, stream);
-    case 4: return launch_rb<4, 4>(a, stream);
+    case 2: return launch_rb<2, 6>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -281,8 +292,7 @@ hipError_t launch_bf16_splitk(const GemmArgs& a, const Schedule& s, float* ws, i
 {
     switch (s.rb) {
     case 1: return launch_rb_split<1, 8>(a, ws, splits, stream);
-    case 2: return launch_rb_split<2, 8>(a, ws, splits, stream);
-    case 4: return launch_rb_split<4, 4>(a, ws, splits, stream);
+    case 2: return launch_rb_split<2, 6>(a, ws, splits, stream);
     default: return hipErrorInvalidValue;
     }
 }
