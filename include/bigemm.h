@@ -39,8 +39,9 @@
  *     next 16-byte boundary past the end of each row (never past the row
  *     pitch, which must be a multiple of 16 bytes).  Elements read that way
  *     beyond K are zeroed before use.
- *   - Base pointers of A, B, C (and of the fp4 scales) must be 16-byte
- *     aligned.
+ *   - Base pointers of A and B (and of the fp4 scales) must be 16-byte
+ *     aligned; C is written element by element and needs only its natural
+ *     2-byte alignment, with any ldc >= N.
  *   - C must not alias A, B or the scales (not checked).
  */
 #ifndef BIGEMM_H
@@ -89,7 +90,7 @@ typedef struct bi_schedule {
  * bf16 x bf16 -> bf16.
  *   A : bf16 [M,K], row pitch lda >= K   (elements; lda % 8 == 0)
  *   B : bf16 [K,N], row pitch ldb >= N   (elements; ldb % 8 == 0)
- *   C : bf16 [M,N], row pitch ldc >= N   (elements; ldc % 8 == 0)
+ *   C : bf16 [M,N], row pitch ldc >= N   (elements)
  * Any K >= 0 is accepted; the K tail is zero-filled.
  */
 bi_status bi_gemm_bf16(int64_t M, int64_t N, int64_t K,
@@ -106,7 +107,7 @@ bi_status bi_gemm_bf16(int64_t M, int64_t N, int64_t K,
  *   B  : e4m3fn [K,N], row pitch ldb >= N bytes (ldb % 16 == 0)
  *   sB : fp32 [K/128, ceil(N/128)], row pitch ldsb >= ceil(N/128);
  *        scale of the 128x128 block B[128i.., 128j..]
- *   C  : bf16 [M,N], ldc >= N, ldc % 8 == 0
+ *   C  : bf16 [M,N], ldc >= N
  * Requires K % 128 == 0.  Value: C[m,n] = sum_kb sA[m,kb] sB[kb,n/128] *
  * sum_{k in kb} dec(A[m,k]) dec(B[k,n]); each 128-long block sum is formed by
  * the MFMA unit, then added as acc = fma(P_kb, sA*sB, acc) with kb ascending.
@@ -125,10 +126,13 @@ bi_status bi_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K,
  *        byte j of row k = code(k, 2j) | code(k, 2j+1) << 4
  *   sB : e4m3fn [K/32, N] bytes, row pitch ldsb >= N (ldsb % 16 == 0);
  *        scale of B[32i .. 32i+31, n]
- *   C  : bf16 [M,N], ldc >= N, ldc % 8 == 0
- * Requires K % 32 == 0 and N even.  Each weight is dequantised to
- * w = e2m1(code) * e4m3fn(scale) inside the K loop; the product has at most
- * six significant bits, so it is exact in bf16, and then enters a bf16 MFMA.
+ *   C  : bf16 [M,N], ldc >= N
+ * Requires K % 32 == 0 and N even.  Dequantisation is fused into the K
+ * loop: each e2m1 code is converted exactly to bf16, one bf16 MFMA per
+ * 32-long K block forms P_kb[m,n] = sum_{k in kb} A[m,k] * e2m1(code(k,n)),
+ * and the block's scale (shared by those 32 weights of column n) is applied
+ * as acc = fma(P_kb, e4m3fn(sB[kb,n]), acc) in fp32, kb ascending -- the
+ * value sum_k A[m,k] * (e2m1 * e4m3fn) with one rounding per block.
  */
 bi_status bi_gemm_fp4_w(int64_t M, int64_t N, int64_t K,
                         const uint16_t* A, int64_t lda,

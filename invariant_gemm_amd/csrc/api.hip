@@ -70,7 +70,7 @@ bi_status validate_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int6
         return BI_ERR_NULL;
     if ((K > 0 && (lda < K || ldb < N)) || ldc < N)
         return BI_ERR_STRIDE;
-    if (!aligned16(C) || ldc % 8)
+    if (((uintptr_t)C & 1u) != 0)
         return BI_ERR_ALIGN;
     if (K > 0 && (!aligned16(A) || !aligned16(B) || lda % 8 || ldb % 8))
         return BI_ERR_ALIGN;
@@ -98,7 +98,7 @@ bi_status validate_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_
         return BI_ERR_NULL;
     if ((K > 0 && (lda < K || ldb < N || ldsa < kb || ldsb < nb)) || ldc < N)
         return BI_ERR_STRIDE;
-    if (!aligned16(C) || ldc % 8)
+    if (((uintptr_t)C & 1u) != 0)
         return BI_ERR_ALIGN;
     if (K > 0 && (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16 || !aligned4(sA) ||
                   !aligned4(sB)))
@@ -124,7 +124,7 @@ bi_status validate_fp4(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64
         return BI_ERR_NULL;
     if ((K > 0 && (lda < K || ldbq < N / 2 || ldsb < N)) || ldc < N)
         return BI_ERR_STRIDE;
-    if (!aligned16(C) || ldc % 8)
+    if (((uintptr_t)C & 1u) != 0)
         return BI_ERR_ALIGN;
     if (K > 0 && (!aligned16(A) || !aligned16(Bq) || !aligned16(sB) || lda % 8 || ldbq % 16 ||
                   ldsb % 16))

@@ -61,7 +61,7 @@ def test_bf16_validation():
     assert bf16(8, 16, 8, ldc=8) == STRIDE
     assert bf16(8, 8, 8, A=P + 2) == ALIGN
     assert bf16(8, 8, 8, B=P + 8) == ALIGN
-    assert bf16(8, 8, 8, C=P + 4) == ALIGN
+    assert bf16(8, 8, 8, C=P + 1) == ALIGN
     assert bf16(8, 8, 12) == ALIGN            # lda = 12: row pitch 24 B
 
 
