@@ -1,20 +1,21 @@
 #!/usr/bin/env python3
 """Throughput of the batch-invariant GEMMs on one MI355X against its roofline.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--quick]
 
-Workload (one "step"): the bf16 projection GEMM, K = N = 8192, weights
-B ~ N(0, 0.02), activations A ~ N(0, 1), swept over M = 1, 2, 4, ..., 256 --
-nine launches of bi_gemm_bf16, one per M.  Every launch reads a different
-copy of (A, B) out of a rotation that totals more than 1 GiB, so B is read
-from HBM and not from the 256 MB Infinity Cache.  Inputs are resident in HBM
-before the timed region starts.
+Headline workload (one "step"): the bf16 projection GEMM, K = N = 8192,
+weights B ~ N(0, 0.02), activations A ~ N(0, 1), swept over
+M = 1, 2, 4, ..., 256 -- nine launches of bi_gemm_bf16, one per M.  Every
+launch reads a different copy of (A, B) from a rotation of more than 1 GiB,
+so B comes from HBM and not from the 256 MB Infinity Cache.  Inputs are
+resident in HBM before the timed region starts.  `value` is whole-job TFLOP/s
+over the timed steps (2MNK per launch).
 
-`value` is whole-job TFLOP/s over the timed steps (2MNK per launch).  The
-JSON line also carries, per M, the launch time, TFLOP/s, algorithmic GB/s and
-roofline fractions; the fp8 block-scaled and fp4 weight-only sweeps; the gap
-against the non-invariant split-K comparator; and the fp64 oracle timed on
-the host (a bounded sample of the same workload).
+The same JSON line carries, per M: launch time, TFLOP/s, algorithmic GB/s and
+the fractions of the HBM and MFMA roofs and of the attainable roof
+(min over both); the fp8 block-scaled (K=7168, N=2048) and fp4 weight-only
+(K=4096, N=14336) sweeps; the dynamic-batching replay; the gap against the
+non-invariant split-K comparator; and the fp64 oracle timed on the host.
 """
 from __future__ import annotations
 
@@ -27,50 +28,47 @@ import time
 
 import numpy as np
 
-HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+HBM_PEAK_GBS = 8000.0                      # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense, published
-SWEEP_C2 = [1, 2, 4, 8, 16, 32, 64, 128, 256]
-K2 = N2 = 8192
-ROT_BYTES = 1 << 30             # rotation footprint per operand set (> 2 x (MALL + L2))
-
+ROT_BYTES = 1 << 30                        # rotation footprint (> 2 x (MALL + L2))
 ROOT = os.path.dirname(os.path.abspath(__file__))
+
+SWEEP_C2 = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+SWEEP_C3 = [1, 2, 4, 8, 16, 32, 37, 64, 128, 129, 256, 512]
+SWEEP_C4 = [1, 8, 64, 512]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def bytes_bf16(M, N, K):
-    return 2 * M * K + 2 * K * N + 2 * M * N
-
-
 def flops(M, N, K):
     return 2.0 * M * N * K
 
 
-# ------------------------------------------------------------------ workload
+# algorithmic bytes: each operand once, plus the output
+def bytes_bf16(M, N, K):
+    return 2 * M * K + 2 * K * N + 2 * M * N
 
-class C2Workload:
-    def __init__(self, torch, bigemm, inputs):
-        self.torch, self.bg = torch, bigemm
-        pool = inputs.normal_bf16((256, K2), 1.0, 201)
-        Bc = inputs.normal_bf16((K2, N2), 0.02, 202)
-        A0 = torch.from_numpy(pool.view(np.int16)).view(torch.bfloat16).cuda()
-        B0 = torch.from_numpy(Bc.view(np.int16)).view(torch.bfloat16).cuda()
-        self.nbuf = max(2, -(-ROT_BYTES // (K2 * N2 * 2)))
-        self.A = [A0.clone() for _ in range(self.nbuf)]
-        self.B = [B0.clone() for _ in range(self.nbuf)]
-        self.C = torch.empty((256, N2), dtype=torch.bfloat16, device="cuda")
-        self.i = 0
 
-    def launch(self, M):
-        j = self.i % self.nbuf
-        self.i += 1
-        self.bg.gemm_bf16(self.A[j][:M], self.B[j], out=self.C[:M])
+def bytes_fp8(M, N, K):
+    kb, nb = K // 128, (N + 127) // 128
+    return M * K + 4 * M * kb + K * N + 4 * kb * nb + 2 * M * N
 
-    def step(self):
-        for M in SWEEP_C2:
-            self.launch(M)
+
+def bytes_fp4(M, N, K):
+    return 2 * M * K + K * N // 2 + (K // 32) * N + 2 * M * N
+
+
+def roof(M, N, K, nbytes, t_us, mfma_peak):
+    f = flops(M, N, K)
+    t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), f / (mfma_peak * 1e12)) * 1e6
+    return {"us": round(t_us, 2), "tflops": round(f / t_us / 1e6, 2),
+            "gbs": round(nbytes / t_us / 1e3, 1),
+            "frac_hbm": round(nbytes / t_us / 1e3 / HBM_PEAK_GBS, 4),
+            "frac_mfma": round(f / t_us / 1e6 / mfma_peak, 4),
+            "frac_attainable": round(t_roof / t_us, 4),
+            "bound": "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= f / (mfma_peak * 1e12) else "mfma"}
 
 
 def time_launches(torch, fn, reps, rounds):
@@ -90,37 +88,121 @@ def time_launches(torch, fn, reps, rounds):
     return per[len(per) // 2], per[0]
 
 
+def rotation(one_copy_bytes):
+    return max(2, -(-ROT_BYTES // one_copy_bytes))
+
+
+# ------------------------------------------------------------------ workloads
+
+class C2:
+    """bf16 projection GEMM K=N=8192, A ~ N(0,1) [256 rows], B ~ N(0,0.02)."""
+    K = N = 8192
+
+    def __init__(self, torch, bg, inputs):
+        self.torch, self.bg = torch, bg
+        pool = inputs.normal_bf16((256, self.K), 1.0, 201)
+        Bc = inputs.normal_bf16((self.K, self.N), 0.02, 202)
+        A0 = torch.from_numpy(pool.view(np.int16)).view(torch.bfloat16).cuda()
+        B0 = torch.from_numpy(Bc.view(np.int16)).view(torch.bfloat16).cuda()
+        self.nbuf = rotation(self.K * self.N * 2)
+        self.A = [A0.clone() for _ in range(self.nbuf)]
+        self.B = [B0.clone() for _ in range(self.nbuf)]
+        self.C = torch.empty((256, self.N), dtype=torch.bfloat16, device="cuda")
+        self.i = 0
+
+    def launch(self, M):
+        j = self.i % self.nbuf
+        self.i += 1
+        self.bg.gemm_bf16(self.A[j][:M], self.B[j], out=self.C[:M])
+
+    def launch_splitk(self, M, ws):
+        j = self.i % self.nbuf
+        self.i += 1
+        self.bg.gemm_bf16_splitk(self.A[j][:M], self.B[j], ws, 0, out=self.C[:M])
+
+    def step(self):
+        for M in SWEEP_C2:
+            self.launch(M)
+
+
+class C3:
+    """fp8 e4m3 K=7168, N=2048, 1x128 / 128x128 fp32 scales, values N(0,1)."""
+    K, N = 7168, 2048
+
+    def __init__(self, torch, bg, inputs):
+        self.bg = bg
+        qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((512, self.K), 1.0, 301))
+        qB, sB = inputs.quant_fp8_tiles(inputs.normal_f32((self.K, self.N), 1.0, 302))
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        self.nbuf = rotation(qB.nbytes)
+        self.A = [t(qA) for _ in range(self.nbuf)]
+        self.sA = [t(sA) for _ in range(self.nbuf)]
+        self.B = [t(qB) for _ in range(self.nbuf)]
+        self.sB = [t(sB) for _ in range(self.nbuf)]
+        self.C = torch.empty((512, self.N), dtype=torch.bfloat16, device="cuda")
+        self.i = 0
+
+    def launch(self, M):
+        j = self.i % self.nbuf
+        self.i += 1
+        self.bg.gemm_fp8_blockscaled(self.A[j][:M], self.sA[j][:M], self.B[j], self.sB[j],
+                                     out=self.C[:M])
+
+
+class C4:
+    """fp4 e2m1 weight-only K=4096, N=14336, e4m3 scales per 32 K, W ~ N(0,0.02)."""
+    K, N = 4096, 14336
+
+    def __init__(self, torch, bg, inputs):
+        self.bg = bg
+        A = inputs.normal_bf16((512, self.K), 1.0, 401)
+        Bq, sB = inputs.quant_fp4_weights(inputs.normal_f32((self.K, self.N), 0.02, 402))
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        self.nbuf = rotation(Bq.nbytes + sB.nbytes)
+        self.A = [t(A.view(np.int16)).view(torch.bfloat16) for _ in range(self.nbuf)]
+        self.B = [t(Bq) for _ in range(self.nbuf)]
+        self.sB = [t(sB) for _ in range(self.nbuf)]
+        self.C = torch.empty((512, self.N), dtype=torch.bfloat16, device="cuda")
+        self.i = 0
+
+    def launch(self, M):
+        j = self.i % self.nbuf
+        self.i += 1
+        self.bg.gemm_fp4_w(self.A[j][:M], self.B[j], self.sB[j], self.N, out=self.C[:M])
+
+
 # ------------------------------------------------------------------ cpu baseline
 
 def cpu_baseline(budget_s=12.0):
     """The fp64 oracle as it stands, on the host cores, on a bounded sample of
-    the same workload (rows of the M = 256 batch, full N and K)."""
+    the headline workload (rows of the M = 256 batch, full N and K)."""
     import oracle
     from invariant_gemm_amd import inputs
-    pool = inputs.normal_bf16((256, K2), 1.0, 201)
-    Bc = inputs.normal_bf16((K2, N2), 0.02, 202)
+    K, N = C2.K, C2.N
+    pool = inputs.normal_bf16((256, K), 1.0, 201)
+    Bc = inputs.normal_bf16((K, N), 0.02, 202)
     rows, t_tot, r = 0, 0.0, 0
-    chunk = 8
     while t_tot < budget_s and rows < 256:
-        A = np.ascontiguousarray(pool[r:r + chunk])
+        A = np.ascontiguousarray(pool[r:r + 8])
         t0 = time.perf_counter()
         oracle.gemm_bf16(A, Bc)
         t_tot += time.perf_counter() - t0
         rows += A.shape[0]
-        r += chunk
-    fl = flops(rows, N2, K2)
-    return {"value": fl / t_tot / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+        r += 8
+    fl = flops(rows, N, K)
+    return {"value": round(fl / t_tot / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"fp64 oracle on {rows} rows of the M=256 batch (K=N=8192): "
+            "sample": f"fp64 oracle on {rows} rows of the M=256 bf16 batch (K=N=8192): "
                       f"{fl / 1e9:.1f} GFLOP in {t_tot:.2f} s"}
 
 
 # ------------------------------------------------------------------ traffic evidence
 
-def traffic_from_profiles(kernel_src: str, algorithmic_bytes: float):
-    """HBM traffic per launch from the committed rocprofv3 --pmc summary, if it
-    was taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "gemm_bf16_c2_pmc.json")
+def traffic_from_profiles(kernel_src: str):
+    """Measured HBM bytes per launch of the headline sweep, from the committed
+    rocprofv3 --pmc summary, if that summary was taken on the current kernel
+    source; else None."""
+    p = os.path.join(ROOT, "profiles", "gemm_bf16_c2_traffic.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
@@ -130,16 +212,14 @@ def traffic_from_profiles(kernel_src: str, algorithmic_bytes: float):
     return d.get("hbm_bytes_per_launch")
 
 
-# ------------------------------------------------------------------ counters
-
 COPY_BYTES = 256 << 20
 
 
 def pmc_probe(torch, wl):
     """Launch sequence for the HBM-traffic counters: a plain device copy of
     COPY_BYTES (the calibration reference: it must fetch and write exactly
-    that many bytes), then three launches per M of the swept GEMM, each on a
-    different rotated copy of B."""
+    that many bytes), then three launches per M of the headline sweep, each on
+    a different rotated copy of B."""
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -153,6 +233,42 @@ def pmc_probe(torch, wl):
     log("pmc probe done: copy", COPY_BYTES, "bytes x3, then 3 launches per M", SWEEP_C2)
 
 
+# ------------------------------------------------------------------ legs
+
+def sweep(torch, wl, Ms, nbytes_fn, peak, rounds):
+    out = {}
+    for M in Ms:
+        med, mn = time_launches(torch, lambda: wl.launch(M), reps=wl.nbuf, rounds=rounds)
+        r = roof(M, wl.N, wl.K, nbytes_fn(M, wl.N, wl.K), med, peak)
+        r["us_min"] = round(mn, 2)
+        out[str(M)] = r
+    return out
+
+
+def replay(torch, bg, inputs, steps=1000):
+    """Dynamic-batching replay on the bf16 projection shape: pool of 4096 rows,
+    `steps` batches of 1..256 distinct rows; GPU time of the GEMM launches."""
+    K = N = 8192
+    P = torch.from_numpy(inputs.normal_bf16((4096, K), 1.0, 501).view(np.int16)).view(torch.bfloat16).cuda()
+    B = torch.from_numpy(inputs.normal_bf16((K, N), 0.02, 502).view(np.int16)).view(torch.bfloat16).cuda()
+    batches = [torch.as_tensor(b, device="cuda") for b in inputs.replay_batches(4096, steps, 256, 503)]
+    As = [P.index_select(0, b) for b in batches]
+    C = torch.empty((256, N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for A in As:
+        bg.gemm_bf16(A, B, out=C[:A.shape[0]])
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1)
+    rows = sum(a.shape[0] for a in As)
+    return {"steps": steps, "rows": rows, "ms": round(ms, 3),
+            "tflops": round(flops(rows, N, K) / (ms * 1e-3) / 1e12, 2),
+            "note": "B stays in the Infinity Cache across steps (one weight matrix, as in serving)"}
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -160,16 +276,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rounds", type=int, default=20, help="rounds per-M timing")
+    ap.add_argument("--rounds", type=int, default=10, help="rounds per timed M point")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the per-M and comparator legs")
+    ap.add_argument("--quick", action="store_true", help="headline only, no extra legs")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only run a known-size copy plus 3 launches per M (for rocprofv3 --pmc)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the batch-invariant GEMM is timed on a single "
-              "MI355X; multi-GPU sharding is described in DESIGN.md and not run here.",
+              "MI355X; how the path would shard over GPUs is described in DESIGN.md.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -179,12 +295,13 @@ def main():
     dev = torch.cuda.get_device_properties(0)
     log(f"device: {dev.name}, CUs {dev.multi_processor_count}")
 
-    wl = C2Workload(torch, bigemm, inputs)
+    wl = C2(torch, bigemm, inputs)
     if args.pmc_probe:
         pmc_probe(torch, wl)
         return
-    step_flops = sum(flops(M, N2, K2) for M in SWEEP_C2)
-    step_bytes = sum(bytes_bf16(M, N2, K2) for M in SWEEP_C2)
+    K, N = C2.K, C2.N
+    step_flops = sum(flops(M, N, K) for M in SWEEP_C2)
+    step_bytes = sum(bytes_bf16(M, N, K) for M in SWEEP_C2)
 
     for _ in range(args.warmup):
         wl.step()
@@ -204,8 +321,6 @@ def main():
     tflops = step_flops / (ms * 1e-3) / 1e12
     gbs = step_bytes / (ms * 1e-3) / 1e9
     kernel_src = os.path.join(ROOT, "invariant_gemm_amd", "csrc", "gemm_bf16.hip")
-    traffic = traffic_from_profiles(kernel_src, step_bytes / len(SWEEP_C2))
-
     out = {
         "metric": "TFLOP/s and HBM GB/s vs roofline per M (1..512), bitwise-invariant rows",
         "value": round(tflops, 3),
@@ -219,40 +334,36 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
-        "config": {"workload": "bf16 projection GEMM C=A.B, K=N=8192, M sweep "
-                               "1,2,4,...,256 (one launch per M); B rotated over "
-                               f"{wl.nbuf} HBM copies",
-                   "launches_per_step": len(SWEEP_C2), "K": K2, "N": N2, "M": SWEEP_C2},
+        "config": {"workload": "bf16 projection GEMM C=A.B, K=N=8192, M sweep 1,2,4,...,256 "
+                               f"(one launch per M); B row-major, rotated over {wl.nbuf} HBM copies",
+                   "launches_per_step": len(SWEEP_C2), "K": K, "N": N, "M": SWEEP_C2},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
+                     "traffic": traffic_from_profiles(kernel_src),
                      "kernel": "gemm_bf16_kernel (bi_gemm_bf16)",
                      "algorithmic_bytes_per_launch": step_bytes / len(SWEEP_C2)},
     }
 
-    if not args.no_extra:
-        per_m = {}
-        for M in SWEEP_C2:
-            med, mn = time_launches(torch, lambda: wl.launch(M), reps=8 * wl.nbuf // 8 or 8,
-                                    rounds=args.rounds)
-            f, b = flops(M, N2, K2), bytes_bf16(M, N2, K2)
-            per_m[str(M)] = {"us": round(med, 2), "us_min": round(mn, 2),
-                             "tflops": round(f / med / 1e6, 2), "gbs": round(b / med / 1e3, 1),
-                             "frac_hbm": round(b / med / 1e3 / HBM_PEAK_GBS, 4),
-                             "frac_mfma": round(f / med / 1e6 / MFMA_PEAK_TFLOPS["bf16"], 4)}
-        out["per_m"] = per_m
-        # split-K comparator (not invariant): split count chosen from M
-        ws = torch.empty(256 * N2, dtype=torch.float32, device="cuda")
+    if not args.quick:
+        out["per_m"] = sweep(torch, wl, SWEEP_C2, bytes_bf16, MFMA_PEAK_TFLOPS["bf16"], args.rounds)
+        ws = torch.empty(256 * N, dtype=torch.float32, device="cuda")
         gap = {}
         for M in SWEEP_C2:
-            def sk(M=M):
-                j = wl.i % wl.nbuf
-                wl.i += 1
-                bigemm.gemm_bf16_splitk(wl.A[j][:M], wl.B[j], ws, 0, out=wl.C[:M])
-            med, _ = time_launches(torch, sk, reps=8, rounds=max(5, args.rounds // 2))
-            gap[str(M)] = {"splits": bigemm.splitk_choose(M, N2, K2), "us": round(med, 2),
-                           "invariant_over_splitk_time": round(per_m[str(M)]["us"] / med, 3)}
+            med, _ = time_launches(torch, lambda: wl.launch_splitk(M, ws), reps=wl.nbuf,
+                                   rounds=max(3, args.rounds // 2))
+            gap[str(M)] = {"splits": bigemm.splitk_choose(M, N, K), "us": round(med, 2),
+                           "invariant_over_splitk_time": round(out["per_m"][str(M)]["us"] / med, 3)}
         out["splitk_gap"] = gap
+        del ws
+        c3 = C3(torch, bigemm, inputs)
+        out["fp8_blockscaled_K7168_N2048"] = sweep(torch, c3, SWEEP_C3, bytes_fp8,
+                                                   MFMA_PEAK_TFLOPS["fp8"], args.rounds)
+        del c3
+        c4 = C4(torch, bigemm, inputs)
+        out["fp4_weight_only_K4096_N14336"] = sweep(torch, c4, SWEEP_C4, bytes_fp4,
+                                                    MFMA_PEAK_TFLOPS["bf16"], args.rounds)
+        del c4
+        out["replay_bf16_K8192_N8192"] = replay(torch, bigemm, inputs)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
