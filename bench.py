@@ -125,6 +125,37 @@ class C2:
             self.launch(M)
 
 
+class C2T(C2):
+    """The same projection GEMM with the weights stored transposed (Bt [N,K])."""
+
+    def __init__(self, torch, bg, inputs):
+        super().__init__(torch, bg, inputs)
+        self.B = [b.t().contiguous() for b in self.B]
+        torch.cuda.synchronize()
+
+    def launch(self, M):
+        j = self.i % self.nbuf
+        self.i += 1
+        self.bg.gemm_bf16_bt(self.A[j][:M], self.B[j], out=self.C[:M])
+
+
+class C2P(C2):
+    """The same projection GEMM on weights packed once into the MFMA order."""
+
+    def __init__(self, torch, bg, inputs):
+        super().__init__(torch, bg, inputs)
+        t0 = time.perf_counter()
+        self.Bp = [bg.pack_b_bf16(b) for b in self.B]
+        torch.cuda.synchronize()
+        self.pack_ms = (time.perf_counter() - t0) * 1e3 / len(self.B)
+        self.B = None
+
+    def launch(self, M):
+        j = self.i % self.nbuf
+        self.i += 1
+        self.bg.gemm_bf16_packed(self.A[j][:M], self.Bp[j], out=self.C[:M])
+
+
 class C3:
     """fp8 e4m3 K=7168, N=2048, 1x128 / 128x128 fp32 scales, values N(0,1)."""
     K, N = 7168, 2048
@@ -355,6 +386,16 @@ def main():
                            "invariant_over_splitk_time": round(out["per_m"][str(M)]["us"] / med, 3)}
         out["splitk_gap"] = gap
         del ws
+        del wl
+        c2t = C2T(torch, bigemm, inputs)
+        out["bf16_bt_K8192_N8192"] = sweep(torch, c2t, SWEEP_C2, bytes_bf16,
+                                           MFMA_PEAK_TFLOPS["bf16"], args.rounds)
+        del c2t
+        c2p = C2P(torch, bigemm, inputs)
+        out["bf16_packed_K8192_N8192"] = sweep(torch, c2p, SWEEP_C2, bytes_bf16,
+                                               MFMA_PEAK_TFLOPS["bf16"], args.rounds)
+        out["bf16_packed_K8192_N8192"]["pack_ms_once"] = round(c2p.pack_ms, 3)
+        del c2p
         c3 = C3(torch, bigemm, inputs)
         out["fp8_blockscaled_K7168_N2048"] = sweep(torch, c3, SWEEP_C3, bytes_fp8,
                                                    MFMA_PEAK_TFLOPS["fp8"], args.rounds)

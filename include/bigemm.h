@@ -99,6 +99,56 @@ bi_status bi_gemm_bf16(int64_t M, int64_t N, int64_t K,
                        uint16_t* C, int64_t ldc, void* stream);
 
 /*
+ * bf16 with the weight matrix stored transposed: C = A . Bt^T, the A.B^T form
+ * of section 3.1 of the wmrh.cn V4 engineering blog (and the usual storage of
+ * projection weights, output-major).
+ *   A  : bf16 [M,K], lda >= K, lda % 8 == 0
+ *   Bt : bf16 [N,K], row pitch ldbt >= K (elements; ldbt % 8 == 0);
+ *        Bt[n][k] = B[k][n]
+ *   C  : bf16 [M,N], ldc >= N
+ * Same K order, MFMA and rounding as bi_gemm_bf16: for the same values both
+ * entry points return identical bits.  Each weight row is streamed as one
+ * contiguous run, which is what lets the small-M regime approach the HBM
+ * roof.
+ */
+bi_status bi_gemm_bf16_bt(int64_t M, int64_t N, int64_t K,
+                          const uint16_t* A, int64_t lda,
+                          const uint16_t* Bt, int64_t ldbt,
+                          uint16_t* C, int64_t ldc, void* stream);
+
+/*
+ * Packed weights.  A weight matrix that is applied to many batches can be
+ * rearranged once into the order in which the MFMA unit consumes it, so that
+ * every wave streams its weights as one contiguous run of HBM (see the packed
+ * layouts below).  The arithmetic of each output element is exactly that of
+ * the unpacked entry point -- the same MFMA sequence in the same K order --
+ * so packed and unpacked calls return identical bits.
+ *
+ * bf16 packed layout: NB = ceil(N/16), KS = ceil(K/32); 1 KiB tile (nb, ks)
+ * at byte (nb*KS + ks)*1024; within it lane l = 16g + i holds the 8 bf16
+ * B[32ks + 8g + j][16nb + i], j = 0..7, zero past K or N.
+ */
+
+/* Bytes of the packed form of a K x N weight matrix of `dtype`
+ * (0 for invalid sizes or formats without a packed form). */
+size_t bi_packed_b_bytes(bi_dtype dtype, int64_t N, int64_t K);
+
+/* Pack row-major bf16 B[K,N] (pitch ldb >= N, 2-byte aligned) into Bp
+ * (16-byte aligned, bp_bytes >= bi_packed_b_bytes(BI_BF16, N, K)).
+ * Enqueues one kernel on `stream`.  BI_ERR_WORKSPACE if Bp is too small. */
+bi_status bi_pack_b_bf16(int64_t N, int64_t K, const uint16_t* B, int64_t ldb,
+                         void* Bp, size_t bp_bytes, void* stream);
+
+/* C = A . B with B given in the packed bf16 layout.  Same rules for A and C
+ * as bi_gemm_bf16; identical bits to bi_gemm_bf16 on the unpacked B.  The
+ * launch geometry (how output tiles are shared among workgroups) adapts to
+ * M; the per-element arithmetic does not. */
+bi_status bi_gemm_bf16_packed(int64_t M, int64_t N, int64_t K,
+                              const uint16_t* A, int64_t lda,
+                              const void* Bp, size_t bp_bytes,
+                              uint16_t* C, int64_t ldc, void* stream);
+
+/*
  * fp8 e4m3fn (OCP, "fn": no infinities) with fp32 block scales -> bf16.
  * The fused dequantisation of section 3.2 of the lshu.cn article: the scales
  * are applied inside the K loop, never in a separate pass.

@@ -38,6 +38,14 @@ class BiSchedule(ctypes.Structure):
 
 lib.bi_gemm_bf16.restype = _i32
 lib.bi_gemm_bf16.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+lib.bi_gemm_bf16_bt.restype = _i32
+lib.bi_gemm_bf16_bt.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+lib.bi_packed_b_bytes.restype = _sz
+lib.bi_packed_b_bytes.argtypes = [_i32, _i64, _i64]
+lib.bi_pack_b_bf16.restype = _i32
+lib.bi_pack_b_bf16.argtypes = [_i64, _i64, _vp, _i64, _vp, _sz, _vp]
+lib.bi_gemm_bf16_packed.restype = _i32
+lib.bi_gemm_bf16_packed.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _sz, _vp, _i64, _vp]
 lib.bi_gemm_fp8_blockscaled.restype = _i32
 lib.bi_gemm_fp8_blockscaled.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                         _vp, _i64, _vp]
@@ -118,6 +126,55 @@ def gemm_bf16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None)
     C = _out(M, N, A.device, out)
     _check(lib.bi_gemm_bf16(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
                             C.data_ptr(), _ld(C), _stream()), "bi_gemm_bf16")
+    return C
+
+
+def gemm_bf16_bt(A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = A . Bt^T with the weights stored transposed (Bt [N,K]) via bi_gemm_bf16_bt."""
+    A = _mat(A, _BF16, "A")
+    Bt = _mat(Bt, _BF16, "Bt")
+    M, K = A.shape
+    if Bt.shape[1] != K:
+        raise ValueError("A and Bt inner dimensions differ")
+    N = Bt.shape[0]
+    C = _out(M, N, A.device, out)
+    _check(lib.bi_gemm_bf16_bt(M, N, K, A.data_ptr(), _ld(A), Bt.data_ptr(), _ld(Bt),
+                               C.data_ptr(), _ld(C), _stream()), "bi_gemm_bf16_bt")
+    return C
+
+
+class PackedWeights:
+    """A weight matrix in the library's MFMA-ordered packed layout (device bytes)."""
+
+    def __init__(self, dtype: int, K: int, N: int, data: torch.Tensor, extra=None):
+        self.dtype, self.K, self.N, self.data, self.extra = dtype, K, N, data, extra
+
+
+def packed_b_bytes(dtype: int, N: int, K: int) -> int:
+    return int(lib.bi_packed_b_bytes(dtype, N, K))
+
+
+def pack_b_bf16(B: torch.Tensor) -> PackedWeights:
+    """Pack row-major bf16 B [K,N] once (one kernel on the current stream)."""
+    B = _mat(B, _BF16, "B")
+    K, N = B.shape
+    nbytes = packed_b_bytes(BI_BF16, N, K)
+    buf = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=B.device)
+    _check(lib.bi_pack_b_bf16(N, K, B.data_ptr(), _ld(B), buf.data_ptr(), buf.numel(), _stream()),
+           "bi_pack_b_bf16")
+    return PackedWeights(BI_BF16, K, N, buf)
+
+
+def gemm_bf16_packed(A: torch.Tensor, Bp: PackedWeights, out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = A . B with B packed by pack_b_bf16 (identical bits to gemm_bf16)."""
+    A = _mat(A, _BF16, "A")
+    M, K = A.shape
+    if Bp.dtype != BI_BF16 or Bp.K != K:
+        raise ValueError("packed weights do not match A")
+    C = _out(M, Bp.N, A.device, out)
+    _check(lib.bi_gemm_bf16_packed(M, Bp.N, K, A.data_ptr(), _ld(A), Bp.data.data_ptr(),
+                                   Bp.data.numel(), C.data_ptr(), _ld(C), _stream()),
+           "bi_gemm_bf16_packed")
     return C
 
 

@@ -55,8 +55,10 @@ bi_status check_grid(int64_t M, int64_t N, const Schedule& s)
 
 bi_status launched(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_LAUNCH; }
 
+// b_row: the length of one stored row of B -- N for B[K,N], K for Bt[N,K]
 bi_status validate_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
-                        const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, bool* noop)
+                        const uint16_t* B, int64_t ldb, int64_t b_row, uint16_t* C, int64_t ldc,
+                        bool* noop)
 {
     *noop = false;
     bi_status st = check_dims(M, N, K);
@@ -68,7 +70,7 @@ bi_status validate_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int6
     }
     if (!C || (K > 0 && (!A || !B)))
         return BI_ERR_NULL;
-    if ((K > 0 && (lda < K || ldb < N)) || ldc < N)
+    if ((K > 0 && (lda < K || ldb < b_row)) || ldc < N)
         return BI_ERR_STRIDE;
     if (((uintptr_t)C & 1u) != 0)
         return BI_ERR_ALIGN;
@@ -187,7 +189,7 @@ bi_status bi_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64
                        const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, void* stream)
 {
     bool noop;
-    bi_status st = validate_bf16(M, N, K, A, lda, B, ldb, C, ldc, &noop);
+    bi_status st = validate_bf16(M, N, K, A, lda, B, ldb, N, C, ldc, &noop);
     if (st != BI_OK || noop)
         return st;
     const Schedule s = schedule_for(BI_BF16, N, K);
@@ -195,6 +197,74 @@ bi_status bi_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64
         return st;
     GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, B, ldb, nullptr, 0, C, ldc};
     return launched(launch_bf16(a, s, (hipStream_t)stream));
+}
+
+bi_status bi_gemm_bf16_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                          const uint16_t* Bt, int64_t ldbt, uint16_t* C, int64_t ldc, void* stream)
+{
+    bool noop;
+    bi_status st = validate_bf16(M, N, K, A, lda, Bt, ldbt, K, C, ldc, &noop);
+    if (st != BI_OK || noop)
+        return st;
+    const Schedule s = schedule_for(BI_BF16, N, K);
+    if ((st = check_grid(M, N, s)) != BI_OK)
+        return st;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, Bt, ldbt, nullptr, 0, C, ldc};
+    return launched(launch_bf16_bt(a, s, (hipStream_t)stream));
+}
+
+size_t bi_packed_b_bytes(bi_dtype dtype, int64_t N, int64_t K)
+{
+    if (N < 0 || K < 0 || N > BI_MAX_DIM || K > BI_MAX_DIM)
+        return 0;
+    const int64_t nb = (N + 15) / 16;
+    switch (dtype) {
+    case BI_BF16: return (size_t)(nb * ((K + 31) / 32) * 1024);
+    default: return 0;
+    }
+}
+
+bi_status bi_pack_b_bf16(int64_t N, int64_t K, const uint16_t* B, int64_t ldb, void* Bp,
+                         size_t bp_bytes, void* stream)
+{
+    bi_status st = check_dims(1, N, K);
+    if (st != BI_OK)
+        return st;
+    const size_t need = bi_packed_b_bytes(BI_BF16, N, K);
+    if (need == 0)
+        return BI_OK;
+    if (!B || !Bp)
+        return BI_ERR_NULL;
+    if (ldb < N)
+        return BI_ERR_STRIDE;
+    if (((uintptr_t)B & 1u) || ((uintptr_t)Bp & 15u))
+        return BI_ERR_ALIGN;
+    if (bp_bytes < need)
+        return BI_ERR_WORKSPACE;
+    return launched(launch_pack_b_bf16((int)N, (int)K, B, ldb, (uint8_t*)Bp, (hipStream_t)stream));
+}
+
+bi_status bi_gemm_bf16_packed(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                              const void* Bp, size_t bp_bytes, uint16_t* C, int64_t ldc,
+                              void* stream)
+{
+    bi_status st = check_dims(M, N, K);
+    if (st != BI_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return BI_OK;
+    if (!C || (K > 0 && (!A || !Bp)))
+        return BI_ERR_NULL;
+    if ((K > 0 && lda < K) || ldc < N)
+        return BI_ERR_STRIDE;
+    if (((uintptr_t)C & 1u) || (K > 0 && (!aligned16(A) || lda % 8 || !aligned16(Bp))))
+        return BI_ERR_ALIGN;
+    if (bp_bytes < bi_packed_b_bytes(BI_BF16, N, K))
+        return BI_ERR_WORKSPACE;
+    if ((M + 15) / 16 * ((N + 31) / 32) > 0x7FFFFFFF)
+        return BI_ERR_UNSUPPORTED;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, Bp, 0, nullptr, 0, C, ldc};
+    return launched(launch_bf16_packed(a, (hipStream_t)stream));
 }
 
 bi_status bi_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
@@ -253,7 +323,7 @@ bi_status bi_gemm_bf16_splitk(int64_t M, int64_t N, int64_t K, const uint16_t* A
                               float* workspace, size_t ws_bytes, int splits, void* stream)
 {
     bool noop;
-    bi_status st = validate_bf16(M, N, K, A, lda, B, ldb, C, ldc, &noop);
+    bi_status st = validate_bf16(M, N, K, A, lda, B, ldb, N, C, ldc, &noop);
     if (st != BI_OK || noop)
         return st;
     if (splits < 0)

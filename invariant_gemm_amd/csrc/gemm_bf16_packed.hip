@@ -1,0 +1,261 @@
+// gemm_bf16_packed.hip -- batch-invariant bf16 GEMM on MFMA-ordered packed
+// weights, plus the packing kernel.
+//
+// Packed layout (one-time transform of the weight matrix, see bigemm.h):
+//   NB = ceil(N/16) column blocks, KS = ceil(K/32) K steps; tile (nb, ks) is
+//   1 KiB at byte offset (nb*KS + ks)*1024; inside it lane l = 16g + i holds
+//   the 16 bytes B[32ks + 8g + j][16nb + i], j = 0..7 (zero past K or N) --
+//   exactly the B operand of one v_mfma_f32_16x16x32_bf16 for that lane.
+// A wave therefore streams its weights as one contiguous run of KS KiB.
+//
+// Arithmetic per output element: the same as bi_gemm_bf16 and bi_gemm_bf16_bt
+// -- one v_mfma_f32_16x16x32_bf16 per 32-long K step, K steps ascending into
+// one fp32 accumulator from zero, RNE to bf16 -- so all three entry points
+// return identical bits, and each row is independent of M, its position and
+// its batch companions (the invariance definition in section
+// "什么是batch invariance" of the QbitAI article).
+//
+// Three launch geometries share that arithmetic (the dual-program idea of
+// section 4.1 of the lshu.cn article and section 3.3 of the wmrh.cn blog,
+// applied to the GEMM: programs for "GPU not saturated" / "saturated" whose
+// results are bit-identical):
+//   streaming : 2 waves x 1 column block, BM = 16, 32 or 64 -- N/32
+//               workgroups stream B;
+//   medium    : 4 waves x 1 column block, BM = 64;
+//   large     : 4 waves x 2 column blocks, BM = 64 -- B fragments reused over
+//               four row blocks, A fragments over two column blocks.
+// None changes the K order, the MFMA or the epilogue of any element.
+#include "common.h"
+#include "launch.h"
+
+namespace bigemm {
+namespace {
+
+constexpr int KSTEP = 32;
+
+__device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
+{
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = (2 * d < valid) ? 0xFFFFu : 0u;
+        const uint32_t hi = (2 * d + 1 < valid) ? 0xFFFF0000u : 0u;
+        v[d] &= (lo | hi);
+    }
+    return v;
+}
+
+// WAVES waves; wave w owns column blocks nb0 + w*CB .. +CB-1; the workgroup
+// owns RB row blocks (BM = 16*RB rows).  Stage = KS_ST K steps.
+template <int WAVES, int CB, int RB, int KS_ST, int PF>
+__global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
+    int M, int N, int K,
+    const uint16_t* __restrict__ A, int64_t lda,
+    const uint8_t* __restrict__ Bp,
+    uint16_t* __restrict__ C, int64_t ldc, int m_tiles)
+{
+    constexpr int NTHR = 64 * WAVES;
+    constexpr int BM = 16 * RB;
+    constexpr int BKS = KS_ST * KSTEP;
+    constexpr int CPR = BKS * 2 / 16;                 // 16-byte A chunks per row per stage
+    constexpr int A_STAGE = BM * BKS * 2;
+    constexpr int A_LD = A_STAGE / (NTHR * 16);
+    static_assert(A_LD * NTHR * 16 == A_STAGE, "A stage must split evenly over the threads");
+    static_assert(PF % 2 == 0, "the LDS double buffer is indexed by stage parity");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * A_STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    const int nt = tile / m_tiles;
+    const int mt = tile - nt * m_tiles;
+    const int m0 = mt * BM;
+    const int NB = (N + 15) >> 4;
+    const int KS = (K + KSTEP - 1) / KSTEP;
+    const int nb0 = nt * (WAVES * CB) + wave * CB;    // first column block of this wave
+
+    const int nst = (K + BKS - 1) / BKS;
+    const int kpad = (K + 7) & ~7;
+    const int rows_valid = M - m0 < BM ? M - m0 : BM;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+
+    uint32_t a_voff[A_LD];
+#pragma unroll
+    for (int j = 0; j < A_LD; ++j) {
+        const int c = j * NTHR + tid;
+        const int row = c / CPR;
+        a_voff[j] = (uint32_t)(row * lda + (((c % CPR) ^ (row & 7)) * 8)) * 2u;
+    }
+
+    u32x4 areg[PF][A_LD];
+    u32x4 breg[PF][KS_ST][CB];
+    f32x4 acc[RB][CB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+            acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int s, u32x4 (&ar)[A_LD], u32x4 (&br)[KS_ST][CB]) {
+        const bool live = s < nst;
+        const int kst = s * BKS;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+            A + (int64_t)m0 * lda + kst,
+            live ? clamp_bytes(((int64_t)(rows_valid - 1) * lda + kpad - kst) * 2) : 0u);
+#pragma unroll
+        for (int j = 0; j < A_LD; ++j)
+            ar[j] = buf_load16(ra, a_voff[j]);
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            const int nb = nb0 + c;
+            const int ks0 = s * KS_ST;
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+                Bp + ((int64_t)nb * KS + ks0) * 1024,
+                live && nb < NB ? clamp_bytes((int64_t)(KS - ks0) * 1024) : 0u);
+#pragma unroll
+            for (int ks = 0; ks < KS_ST; ++ks)
+                br[ks][c] = buf_load16(rb, (uint32_t)(ks * 1024 + lane * 16));
+        }
+    };
+
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        issue(p, areg[p], breg[p]);
+
+    const int nst_pad = (nst + PF - 1) / PF * PF;
+    for (int s0 = 0; s0 < nst_pad; s0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int s = s0 + p;
+            const int kst = s * BKS;
+            uint8_t* abuf = smem + (p & 1) * A_STAGE;
+            if (kst + BKS > K) {
+                // K tail: A's row pitch past K may hold anything (packed B is
+                // already zero past K)
+#pragma unroll
+                for (int j = 0; j < A_LD; ++j) {
+                    const int c = j * NTHR + tid;
+                    const int kc = (c % CPR) ^ ((c / CPR) & 7);
+                    areg[p][j] = keep_first(areg[p][j], K - (kst + 8 * kc));
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < A_LD; ++j)
+                *reinterpret_cast<u32x4*>(abuf + (j * NTHR + tid) * 16) = areg[p][j];
+            __syncthreads();
+#pragma unroll
+            for (int ks = 0; ks < KS_ST; ++ks) {
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    const int row = 16 * r + li;
+                    const u32x4 afrag = *reinterpret_cast<const u32x4*>(
+                        abuf + (row * CPR + ((ks * 4 + lg) ^ (row & 7))) * 16);
+#pragma unroll
+                    for (int c = 0; c < CB; ++c)
+                        acc[r][c] = mfma_bf16(afrag, breg[p][ks][c], acc[r][c]);
+                }
+            }
+            issue(s + PF, areg[p], breg[p]);
+        }
+    }
+
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+        const int col = 16 * (nb0 + c) + li;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = m0 + 16 * r + 4 * lg + j;
+                if (row < M && col < N)
+                    C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[r][c][j]);
+            }
+        }
+    }
+}
+
+// One thread per 16-byte packed chunk: chunk q = (nb*KS + ks)*64 + l.
+__global__ void pack_b_bf16_kernel(int N, int K, const uint16_t* __restrict__ B, int64_t ldb,
+                                   uint8_t* __restrict__ Bp, int64_t nchunks)
+{
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= nchunks)
+        return;
+    const int KS = (K + KSTEP - 1) / KSTEP;
+    const int l = (int)(q & 63);
+    const int64_t t = q >> 6;
+    const int ks = (int)(t % KS);
+    const int nb = (int)(t / KS);
+    const int n = 16 * nb + (l & 15);
+    const int k0 = 32 * ks + 8 * (l >> 4);
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int ka = k0 + 2 * d, kb = ka + 1;
+        const uint32_t lo = (n < N && ka < K) ? B[(int64_t)ka * ldb + n] : 0u;
+        const uint32_t hi = (n < N && kb < K) ? B[(int64_t)kb * ldb + n] : 0u;
+        w[d] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(Bp + q * 16) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+template <int WAVES, int CB, int RB, int KS_ST, int PF>
+hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
+{
+    const int n_tiles = ((a.N + 15) / 16 + WAVES * CB - 1) / (WAVES * CB);
+    const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
+    gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF><<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0,
+                                                       stream>>>(
+        a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Launch geometry for a call.  Every geometry runs the same per-element
+// arithmetic (same MFMA, same K steps in the same order, same epilogue), so
+// this choice -- unlike the arithmetic -- may follow M: it only decides how
+// the output tiles are shared among workgroups.  The largest tile that still
+// yields a workgroup per compute unit wins; below that, the streaming
+// geometry (one 16-row block, two 16-column waves) covers N with N/32
+// workgroups.
+int packed_geometry(int M, int N)
+{
+    const int nb = (N + 15) / 16;
+    const int large = ((M + 63) / 64) * ((nb + 7) / 8);     // 4 waves x 2 blocks, BM 64
+    const int medium = ((M + 63) / 64) * ((nb + 3) / 4);    // 4 waves x 1 block,  BM 64
+    if (M >= 64 && large >= 256)
+        return 4;
+    if (M >= 64 && medium >= 256)
+        return 3;
+    if (M > 32)
+        return 2;                                           // streaming, BM 64
+    if (M > 16)
+        return 1;                                           // streaming, BM 32
+    return 0;                                               // streaming, BM 16
+}
+
+hipError_t launch_bf16_packed(const GemmArgs& a, hipStream_t stream)
+{
+    switch (packed_geometry(a.M, a.N)) {
+    case 4: return launch_geometry<4, 2, 4, 4, 4>(a, stream);
+    case 3: return launch_geometry<4, 1, 4, 4, 4>(a, stream);
+    case 2: return launch_geometry<2, 1, 4, 2, 8>(a, stream);
+    case 1: return launch_geometry<2, 1, 2, 4, 6>(a, stream);
+    default: return launch_geometry<2, 1, 1, 8, 4>(a, stream);
+    }
+}
+
+hipError_t launch_pack_b_bf16(int N, int K, const uint16_t* B, int64_t ldb, uint8_t* Bp,
+                              hipStream_t stream)
+{
+    const int64_t nchunks = (int64_t)((N + 15) / 16) * ((K + KSTEP - 1) / KSTEP) * 64;
+    if (nchunks == 0)
+        return hipSuccess;
+    pack_b_bf16_kernel<<<dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, stream>>>(
+        N, K, B, ldb, Bp, nchunks);
+    return hipGetLastError();
+}
+
+}  // namespace bigemm

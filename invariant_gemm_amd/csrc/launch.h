@@ -26,6 +26,11 @@ struct GemmArgs {
 };
 
 hipError_t launch_bf16(const GemmArgs& a, const Schedule& s, hipStream_t stream);
+hipError_t launch_bf16_bt(const GemmArgs& a, const Schedule& s, hipStream_t stream);
+hipError_t launch_bf16_packed(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_pack_b_bf16(int N, int K, const uint16_t* B, int64_t ldb, uint8_t* Bp,
+                              hipStream_t stream);
+int packed_geometry(int M, int N);
 hipError_t launch_fp8bs(const GemmArgs& a, const Schedule& s, hipStream_t stream);
 hipError_t launch_fp4w(const GemmArgs& a, const Schedule& s, hipStream_t stream);
 hipError_t launch_bf16_splitk(const GemmArgs& a, const Schedule& s, float* ws, int splits,

@@ -65,6 +65,17 @@ def test_bf16_validation():
     assert bf16(8, 8, 12) == ALIGN            # lda = 12: row pitch 24 B
 
 
+def test_bf16_bt_validation():
+    f = lambda M, N, K, A=P, lda=None, Bt=P, ldbt=None, C=P, ldc=None: lib.bi_gemm_bf16_bt(
+        M, N, K, A, K if lda is None else lda, Bt, K if ldbt is None else ldbt, C,
+        N if ldc is None else ldc, None)
+    assert f(-1, 8, 8) == SHAPE
+    assert f(8, 8, 8, Bt=None) == NULL
+    assert f(8, 64, 16, ldbt=8) == STRIDE       # Bt rows hold K elements
+    assert f(8, 64, 16, ldbt=20) == ALIGN
+    assert f(0, 8, 8, A=None, Bt=None, C=None) == OK
+
+
 def test_bf16_k0_needs_no_operands():
     # K == 0 with NULL A/B passes validation; it would launch (C = 0), so
     # only the validation order is checked here: a NULL C is still rejected.

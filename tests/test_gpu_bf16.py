@@ -237,3 +237,70 @@ def test_splitk_comparator_is_flagged(bg, c2):
     # and the invariant kernel on the same rows is clean
     inv_alone = _alone(bg, A[:M], B)
     assert bool(rows_equal(inv_alone, bg.gemm_bf16(A[:M], B)).all())
+
+
+# ------------------------------------------------------------------ transposed weight storage
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 256, 512), (37, 100, 203), (1, 8, 1), (65, 40, 129),
+                                   (130, 264, 1000), (1, 8192, 8192), (200, 96, 4096)])
+def test_bt_bitwise_equal_to_rowmajor(bg, M, N, K):
+    """Storing the weights transposed changes only the data movement: the same
+    MFMA sequence per element must give identical bits."""
+    A = inputs.normal_bf16((M, K), 1.0, 500 + M)
+    B = inputs.normal_bf16((K, N), 1.0, 600 + N)
+    lda = (K + 7) // 8 * 8
+    ldb = (N + 7) // 8 * 8
+    rm = run(bg, A, B, lda=lda, ldb=ldb, ldc=ldb)
+    Ad = dev_bf16(A, lda)
+    Bt = dev_bf16(np.ascontiguousarray(B.T), lda)
+    bt = host_codes(bg.gemm_bf16_bt(Ad, Bt))
+    assert np.array_equal(bt, rm)
+    C64, S = oracle.gemm_bf16(A, B)
+    check_parity(bt, C64, S, K, f"bt M{M} N{N} K{K}")
+
+
+def test_bt_c2_invariance_all_m(bg, c2):
+    pool, Bc, A, B = c2
+    Bt = dev_bf16(np.ascontiguousarray(Bc.T))
+    ref = torch.cat([bg.gemm_bf16_bt(A[i:i + 1], Bt) for i in range(256)])
+    assert bool(rows_equal(ref, bg.gemm_bf16(A, B)).all()), "bt rows differ from row-major rows"
+    for m in [2**i for i in range(9)] + [3, 17, 100, 255]:
+        assert bool(rows_equal(bg.gemm_bf16_bt(A[:m], Bt), ref[:m]).all()), f"M={m}"
+    p = torch.as_tensor(inputs.permutation(256, 207), device="cuda")
+    assert bool(rows_equal(bg.gemm_bf16_bt(A.index_select(0, p), Bt), ref.index_select(0, p)).all())
+
+
+# ------------------------------------------------------------------ packed weights
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 256, 512), (37, 100, 203), (1, 8, 1), (65, 40, 129),
+                                   (130, 264, 1000), (200, 96, 4096), (256, 2048, 512),
+                                   (300, 4096, 256)])
+def test_packed_bitwise_equal_to_rowmajor(bg, M, N, K):
+    A = inputs.normal_bf16((M, K), 1.0, 700 + M)
+    B = inputs.normal_bf16((K, N), 1.0, 800 + N)
+    lda = (K + 7) // 8 * 8
+    ldb = (N + 7) // 8 * 8
+    rm = run(bg, A, B, lda=lda, ldb=ldb, ldc=ldb)
+    Bp = bg.pack_b_bf16(dev_bf16(B, ldb))
+    pk = host_codes(bg.gemm_bf16_packed(dev_bf16(A, lda), Bp))
+    assert np.array_equal(pk, rm)
+
+
+def test_packed_c2_all_geometries_bitwise(bg, c2):
+    """Rows computed by the streaming geometry (M = 1), the medium and the large
+    geometry (larger M) must be identical: the geometry follows M, the
+    arithmetic does not."""
+    pool, Bc, A, B = c2
+    Bp = bg.pack_b_bf16(B)
+    ref = torch.cat([bg.gemm_bf16_packed(A[i:i + 1], Bp) for i in range(256)])
+    assert bool(rows_equal(ref, bg.gemm_bf16(A, B)).all())
+    for m in [1, 2, 4, 8, 16, 32, 48, 64, 100, 128, 129, 192, 200, 256]:
+        assert bool(rows_equal(bg.gemm_bf16_packed(A[:m], Bp), ref[:m]).all()), f"M={m}"
+    for s in range(3):
+        p = torch.as_tensor(inputs.permutation(256, 208 + s), device="cuda")
+        assert bool(rows_equal(bg.gemm_bf16_packed(A.index_select(0, p), Bp),
+                               ref.index_select(0, p)).all()), f"shuffle {s}"
+    C64, S = oracle.gemm_bf16(np.ascontiguousarray(pool[[0, 77, 255]]), Bc)
+    check_parity(host_codes(ref[[0, 77, 255]]), C64, S, 8192, "packed C2")
