@@ -180,6 +180,24 @@ class C3:
                                      out=self.C[:M])
 
 
+class C3P(C3):
+    """The fp8 workload on weights packed once into the MFMA order."""
+
+    def __init__(self, torch, bg, inputs):
+        super().__init__(torch, bg, inputs)
+        t0 = time.perf_counter()
+        self.Bp = [bg.pack_b_fp8(b) for b in self.B]
+        torch.cuda.synchronize()
+        self.pack_ms = (time.perf_counter() - t0) * 1e3 / len(self.B)
+        self.B = None
+
+    def launch(self, M):
+        j = self.i % self.nbuf
+        self.i += 1
+        self.bg.gemm_fp8_blockscaled_packed(self.A[j][:M], self.sA[j][:M], self.Bp[j], self.sB[j],
+                                            out=self.C[:M])
+
+
 class C4:
     """fp4 e2m1 weight-only K=4096, N=14336, e4m3 scales per 32 K, W ~ N(0,0.02)."""
     K, N = 4096, 14336
@@ -200,6 +218,23 @@ class C4:
         j = self.i % self.nbuf
         self.i += 1
         self.bg.gemm_fp4_w(self.A[j][:M], self.B[j], self.sB[j], self.N, out=self.C[:M])
+
+
+class C4P(C4):
+    """The fp4 workload on codes and scales packed once into the MFMA order."""
+
+    def __init__(self, torch, bg, inputs):
+        super().__init__(torch, bg, inputs)
+        t0 = time.perf_counter()
+        self.Bp = [bg.pack_b_fp4(b, s, self.N) for b, s in zip(self.B, self.sB)]
+        torch.cuda.synchronize()
+        self.pack_ms = (time.perf_counter() - t0) * 1e3 / len(self.B)
+        self.B = self.sB = None
+
+    def launch(self, M):
+        j = self.i % self.nbuf
+        self.i += 1
+        self.bg.gemm_fp4_w_packed(self.A[j][:M], self.Bp[j], out=self.C[:M])
 
 
 # ------------------------------------------------------------------ cpu baseline
@@ -400,10 +435,20 @@ def main():
         out["fp8_blockscaled_K7168_N2048"] = sweep(torch, c3, SWEEP_C3, bytes_fp8,
                                                    MFMA_PEAK_TFLOPS["fp8"], args.rounds)
         del c3
+        c3p = C3P(torch, bigemm, inputs)
+        out["fp8_blockscaled_packed_K7168_N2048"] = sweep(torch, c3p, SWEEP_C3, bytes_fp8,
+                                                          MFMA_PEAK_TFLOPS["fp8"], args.rounds)
+        out["fp8_blockscaled_packed_K7168_N2048"]["pack_ms_once"] = round(c3p.pack_ms, 3)
+        del c3p
         c4 = C4(torch, bigemm, inputs)
         out["fp4_weight_only_K4096_N14336"] = sweep(torch, c4, SWEEP_C4, bytes_fp4,
                                                     MFMA_PEAK_TFLOPS["bf16"], args.rounds)
         del c4
+        c4p = C4P(torch, bigemm, inputs)
+        out["fp4_weight_only_packed_K4096_N14336"] = sweep(torch, c4p, SWEEP_C4, bytes_fp4,
+                                                           MFMA_PEAK_TFLOPS["bf16"], args.rounds)
+        out["fp4_weight_only_packed_K4096_N14336"]["pack_ms_once"] = round(c4p.pack_ms, 3)
+        del c4p
         out["replay_bf16_K8192_N8192"] = replay(torch, bigemm, inputs)
 
     if not args.no_cpu_baseline:

@@ -190,6 +190,55 @@ bi_status bi_gemm_fp4_w(int64_t M, int64_t N, int64_t K,
                         const uint8_t* sB, int64_t ldsb,
                         uint16_t* C, int64_t ldc, void* stream);
 
+/*
+ * Packed quantised weights (same idea as the packed bf16 layout: weights in
+ * MFMA operand order, one contiguous run per 16-column block; identical bits
+ * to the unpacked entry points).
+ *
+ * fp8 packed layout: NB = ceil(N/16), KB = K/128; 2 KiB tile (nb, kb) at
+ * byte (nb*KB + kb)*2048, two 1 KiB halves h; in half h lane l = 16g + i
+ * holds the 16 bytes B[128kb + 32g + 16h + j][16nb + i], j = 0..15, zero
+ * past N.  The weight scales sB are not packed.  Size NB*KB*2048 bytes.
+ *
+ * fp4 packed layout: NB = ceil(N/16), KQ = ceil(K/128).  Codes: 1 KiB tile
+ * (nb, q) at byte (nb*KQ + q)*1024; lane l = 16g + i holds 4 dwords, dword t
+ * = the 8 codes of column 16nb + i at k = 128q + 32t + 8g + j, nibble j in
+ * bits 4j..4j+3.  Scales follow the codes: 64-byte tile (nb, q) at byte
+ * NB*KQ*1024 + (nb*KQ + q)*64, byte 4i + t = sB[4q + t][16nb + i].  Zero
+ * past K or N.  Size NB*KQ*1088 bytes.
+ */
+
+/* Pack row-major e4m3fn B[K,N] (pitch ldb >= N bytes; K % 128 == 0) into Bp
+ * (16-byte aligned, bp_bytes >= bi_packed_b_bytes(BI_FP8_BS, N, K)).
+ * Enqueues one kernel on `stream`. */
+bi_status bi_pack_b_fp8(int64_t N, int64_t K, const uint8_t* B, int64_t ldb,
+                        void* Bp, size_t bp_bytes, void* stream);
+
+/* bi_gemm_fp8_blockscaled with B given in the packed fp8 layout; A, sA, sB
+ * and C as there.  The launch geometry adapts to M; the per-element
+ * arithmetic does not. */
+bi_status bi_gemm_fp8_blockscaled_packed(int64_t M, int64_t N, int64_t K,
+                                         const uint8_t* A, int64_t lda,
+                                         const float* sA, int64_t ldsa,
+                                         const void* Bp, size_t bp_bytes,
+                                         const float* sB, int64_t ldsb,
+                                         uint16_t* C, int64_t ldc, void* stream);
+
+/* Pack e2m1 codes Bq[K, N/2] (pitch ldbq >= N/2) and e4m3fn scales
+ * sB[K/32, N] (pitch ldsb >= N) -- the operands of bi_gemm_fp4_w -- into Bp
+ * (16-byte aligned, bp_bytes >= bi_packed_b_bytes(BI_FP4_W, N, K)).
+ * Requires K % 32 == 0 and N even.  Enqueues one kernel on `stream`. */
+bi_status bi_pack_b_fp4(int64_t N, int64_t K, const uint8_t* Bq, int64_t ldbq,
+                        const uint8_t* sB, int64_t ldsb,
+                        void* Bp, size_t bp_bytes, void* stream);
+
+/* bi_gemm_fp4_w with codes and scales given in the packed fp4 layout; A and
+ * C as there. */
+bi_status bi_gemm_fp4_w_packed(int64_t M, int64_t N, int64_t K,
+                               const uint16_t* A, int64_t lda,
+                               const void* Bp, size_t bp_bytes,
+                               uint16_t* C, int64_t ldc, void* stream);
+
 /* The schedule (dtype, N, K) selects.  There is no M argument by design.
  * Returns BI_ERR_NULL for out == NULL, BI_ERR_UNSUPPORTED for an unknown
  * dtype, BI_ERR_SHAPE for invalid N or K. */

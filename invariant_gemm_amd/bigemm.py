@@ -51,6 +51,15 @@ lib.bi_gemm_fp8_blockscaled.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, 
                                         _vp, _i64, _vp]
 lib.bi_gemm_fp4_w.restype = _i32
 lib.bi_gemm_fp4_w.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+lib.bi_pack_b_fp8.restype = _i32
+lib.bi_pack_b_fp8.argtypes = [_i64, _i64, _vp, _i64, _vp, _sz, _vp]
+lib.bi_gemm_fp8_blockscaled_packed.restype = _i32
+lib.bi_gemm_fp8_blockscaled_packed.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz,
+                                               _vp, _i64, _vp, _i64, _vp]
+lib.bi_pack_b_fp4.restype = _i32
+lib.bi_pack_b_fp4.argtypes = [_i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
+lib.bi_gemm_fp4_w_packed.restype = _i32
+lib.bi_gemm_fp4_w_packed.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _sz, _vp, _i64, _vp]
 lib.bi_gemm_bf16_splitk.restype = _i32
 lib.bi_gemm_bf16_splitk.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz,
                                     _i32, _vp]
@@ -209,6 +218,59 @@ def gemm_fp4_w(A: torch.Tensor, Bq: torch.Tensor, sB: torch.Tensor, N: int,
     _check(lib.bi_gemm_fp4_w(M, N, K, A.data_ptr(), _ld(A), Bq.data_ptr(), _ld(Bq),
                              sB.data_ptr(), _ld(sB), C.data_ptr(), _ld(C), _stream()),
            "bi_gemm_fp4_w")
+    return C
+
+
+def pack_b_fp8(B: torch.Tensor) -> PackedWeights:
+    """Pack row-major e4m3fn B [K,N] once (the scales sB stay as they are)."""
+    B = _mat(B, _U8, "B")
+    K, N = B.shape
+    nbytes = packed_b_bytes(BI_FP8_BS, N, K)
+    buf = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=B.device)
+    _check(lib.bi_pack_b_fp8(N, K, B.data_ptr(), _ld(B), buf.data_ptr(), buf.numel(), _stream()),
+           "bi_pack_b_fp8")
+    return PackedWeights(BI_FP8_BS, K, N, buf)
+
+
+def gemm_fp8_blockscaled_packed(A: torch.Tensor, sA: torch.Tensor, Bp: PackedWeights,
+                                sB: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm_fp8_blockscaled with B packed by pack_b_fp8 (identical bits)."""
+    A = _mat(A, _U8, "A")
+    sA = _mat(sA, (torch.float32,), "sA")
+    sB = _mat(sB, (torch.float32,), "sB")
+    M, K = A.shape
+    if Bp.dtype != BI_FP8_BS or Bp.K != K:
+        raise ValueError("packed weights do not match A")
+    C = _out(M, Bp.N, A.device, out)
+    _check(lib.bi_gemm_fp8_blockscaled_packed(M, Bp.N, K, A.data_ptr(), _ld(A), sA.data_ptr(),
+                                              _ld(sA), Bp.data.data_ptr(), Bp.data.numel(),
+                                              sB.data_ptr(), _ld(sB), C.data_ptr(), _ld(C),
+                                              _stream()), "bi_gemm_fp8_blockscaled_packed")
+    return C
+
+
+def pack_b_fp4(Bq: torch.Tensor, sB: torch.Tensor, N: int) -> PackedWeights:
+    """Pack e2m1 codes Bq [K, N/2] and e4m3fn scales sB [K/32, N] once."""
+    Bq = _mat(Bq, _U8, "Bq")
+    sB = _mat(sB, _U8, "sB")
+    K = Bq.shape[0]
+    nbytes = packed_b_bytes(BI_FP4_W, N, K)
+    buf = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=Bq.device)
+    _check(lib.bi_pack_b_fp4(N, K, Bq.data_ptr(), _ld(Bq), sB.data_ptr(), _ld(sB),
+                             buf.data_ptr(), buf.numel(), _stream()), "bi_pack_b_fp4")
+    return PackedWeights(BI_FP4_W, K, N, buf)
+
+
+def gemm_fp4_w_packed(A: torch.Tensor, Bp: PackedWeights, out: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm_fp4_w with codes and scales packed by pack_b_fp4 (identical bits)."""
+    A = _mat(A, _BF16, "A")
+    M, K = A.shape
+    if Bp.dtype != BI_FP4_W or Bp.K != K:
+        raise ValueError("packed weights do not match A")
+    C = _out(M, Bp.N, A.device, out)
+    _check(lib.bi_gemm_fp4_w_packed(M, Bp.N, K, A.data_ptr(), _ld(A), Bp.data.data_ptr(),
+                                    Bp.data.numel(), C.data_ptr(), _ld(C), _stream()),
+           "bi_gemm_fp4_w_packed")
     return C
 
 

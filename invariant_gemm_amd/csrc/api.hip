@@ -220,6 +220,8 @@ size_t bi_packed_b_bytes(bi_dtype dtype, int64_t N, int64_t K)
     const int64_t nb = (N + 15) / 16;
     switch (dtype) {
     case BI_BF16: return (size_t)(nb * ((K + 31) / 32) * 1024);
+    case BI_FP8_BS: return K % 128 ? 0 : (size_t)(nb * (K / 128) * 2048);
+    case BI_FP4_W: return (K % 32 || N % 2) ? 0 : (size_t)(nb * ((K + 127) / 128) * 1088);
     default: return 0;
     }
 }
@@ -296,6 +298,104 @@ bi_status bi_gemm_fp4_w(int64_t M, int64_t N, int64_t K, const uint16_t* A, int6
         return st;
     GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, Bq, ldbq, sB, ldsb, C, ldc};
     return launched(launch_fp4w(a, s, (hipStream_t)stream));
+}
+
+bi_status bi_pack_b_fp8(int64_t N, int64_t K, const uint8_t* B, int64_t ldb, void* Bp,
+                        size_t bp_bytes, void* stream)
+{
+    bi_status st = check_dims(1, N, K);
+    if (st != BI_OK)
+        return st;
+    if (K % 128)
+        return BI_ERR_SHAPE;
+    const size_t need = bi_packed_b_bytes(BI_FP8_BS, N, K);
+    if (need == 0)
+        return BI_OK;
+    if (!B || !Bp)
+        return BI_ERR_NULL;
+    if (ldb < N)
+        return BI_ERR_STRIDE;
+    if ((uintptr_t)Bp & 15u)
+        return BI_ERR_ALIGN;
+    if (bp_bytes < need)
+        return BI_ERR_WORKSPACE;
+    return launched(launch_pack_fp8((int)N, (int)K, B, ldb, (uint8_t*)Bp, (hipStream_t)stream));
+}
+
+bi_status bi_gemm_fp8_blockscaled_packed(int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                                         int64_t lda, const float* sA, int64_t ldsa,
+                                         const void* Bp, size_t bp_bytes, const float* sB,
+                                         int64_t ldsb, uint16_t* C, int64_t ldc, void* stream)
+{
+    bi_status st = check_dims(M, N, K);
+    if (st != BI_OK)
+        return st;
+    if (K % 128)
+        return BI_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return BI_OK;
+    const int64_t kb = K / 128, nb = (N + 127) / 128;
+    if (!C || (K > 0 && (!A || !sA || !Bp || !sB)))
+        return BI_ERR_NULL;
+    if ((K > 0 && (lda < K || ldsa < kb || ldsb < nb)) || ldc < N)
+        return BI_ERR_STRIDE;
+    if (((uintptr_t)C & 1u) ||
+        (K > 0 && (!aligned16(A) || lda % 16 || !aligned16(Bp) || !aligned4(sA) || !aligned4(sB))))
+        return BI_ERR_ALIGN;
+    if (bp_bytes < bi_packed_b_bytes(BI_FP8_BS, N, K))
+        return BI_ERR_WORKSPACE;
+    if ((M + 15) / 16 * ((N + 15) / 16) > 0x7FFFFFFF)
+        return BI_ERR_UNSUPPORTED;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, sA, ldsa, Bp, 0, sB, ldsb, C, ldc};
+    return launched(launch_fp8_packed(a, (hipStream_t)stream));
+}
+
+bi_status bi_pack_b_fp4(int64_t N, int64_t K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sB,
+                        int64_t ldsb, void* Bp, size_t bp_bytes, void* stream)
+{
+    bi_status st = check_dims(1, N, K);
+    if (st != BI_OK)
+        return st;
+    if (K % 32 || N % 2)
+        return BI_ERR_SHAPE;
+    const size_t need = bi_packed_b_bytes(BI_FP4_W, N, K);
+    if (need == 0)
+        return BI_OK;
+    if (!Bq || !sB || !Bp)
+        return BI_ERR_NULL;
+    if (ldbq < N / 2 || ldsb < N)
+        return BI_ERR_STRIDE;
+    if ((uintptr_t)Bp & 15u)
+        return BI_ERR_ALIGN;
+    if (bp_bytes < need)
+        return BI_ERR_WORKSPACE;
+    return launched(launch_pack_fp4((int)N, (int)K, Bq, ldbq, sB, ldsb, (uint8_t*)Bp,
+                                    (hipStream_t)stream));
+}
+
+bi_status bi_gemm_fp4_w_packed(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                               const void* Bp, size_t bp_bytes, uint16_t* C, int64_t ldc,
+                               void* stream)
+{
+    bi_status st = check_dims(M, N, K);
+    if (st != BI_OK)
+        return st;
+    if (K % 32 || N % 2)
+        return BI_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return BI_OK;
+    if (!C || (K > 0 && (!A || !Bp)))
+        return BI_ERR_NULL;
+    if ((K > 0 && lda < K) || ldc < N)
+        return BI_ERR_STRIDE;
+    if (((uintptr_t)C & 1u) || (K > 0 && (!aligned16(A) || lda % 8 || !aligned16(Bp))))
+        return BI_ERR_ALIGN;
+    if (bp_bytes < bi_packed_b_bytes(BI_FP4_W, N, K))
+        return BI_ERR_WORKSPACE;
+    if ((M + 15) / 16 * ((N + 15) / 16) > 0x7FFFFFFF)
+        return BI_ERR_UNSUPPORTED;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, Bp, 0, nullptr, 0, C, ldc};
+    return launched(launch_fp4w_packed(a, (hipStream_t)stream));
 }
 
 int bi_splitk_choose(int64_t M, int64_t N, int64_t K)

@@ -1,0 +1,333 @@
+// gemm_fp8_packed.hip -- batch-invariant fp8 (e4m3fn) block-scaled GEMM on
+// MFMA-ordered packed weights, plus the packer.
+//
+// Packed layout (bigemm.h): NB = ceil(N/16), KB = K/128; tile (nb, kb) of
+// 2 KiB at byte (nb*KB + kb)*2048, made of two 1 KiB halves h; in half h,
+// lane l = 16g + i holds the 16 bytes B[128kb + 32g + 16h + j][16nb + i],
+// j = 0..15 (0 past N) -- the two halves of the B operand of one
+// v_mfma_scale_f32_16x16x128_f8f6f4 for that lane.  The weight scales sB
+// keep their [K/128][ceil(N/128)] fp32 layout.
+//
+// Arithmetic per output element -- the same as bi_gemm_fp8_blockscaled: for
+// each 128-long K block kb, ascending, P = v_mfma_scale_f32_16x16x128_f8f6f4
+// (unit E8M0 scales) into a zero accumulator, then
+// acc = fma(P, sA[m,kb] * sB[kb, n/128], acc), RNE to bf16 at the end.  So
+// both entry points return identical bits, and each row is independent of M,
+// its position and its batch companions.
+//
+// Workgroup: WAVES waves load one stage (A rows, B tiles of CB column blocks,
+// their scales) cooperatively into LDS; the output tile of RB x CB MFMA
+// blocks is split among the waves as (RB/WR) x (CB/WC) sub-tiles, and waves
+// beyond that count only load.  With a single 16 x 16 block (small M) all
+// waves still stream weights for it, which keeps enough bytes in flight per
+// compute unit when N/16 is below the compute unit count.
+#include "common.h"
+#include "launch.h"
+
+namespace bigemm {
+namespace {
+
+constexpr int KBK = 128;       // K per scale block = one MFMA
+constexpr int BTILE = 2048;    // packed bytes per (column block, K block)
+
+template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF>
+__global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
+    int M, int N, int K,
+    const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t ldsa,
+    const uint8_t* __restrict__ Bp, const float* __restrict__ sB, int64_t ldsb,
+    uint16_t* __restrict__ C, int64_t ldc, int m_tiles)
+{
+    constexpr int NTHR = 64 * WAVES;
+    constexpr int BM = 16 * RB;
+    constexpr int CPR = KB_ST * 8;                    // 16-byte A chunks per row per stage
+    constexpr int A_BYTES = BM * KB_ST * KBK;
+    constexpr int B_BYTES = CB * KB_ST * BTILE;
+    constexpr int A_LD = A_BYTES / (NTHR * 16);
+    constexpr int B_LD = B_BYTES / (NTHR * 16);
+    constexpr int SA_N = BM * KB_ST;
+    constexpr int SB_N = CB * KB_ST;
+    constexpr int SA_LD = (SA_N + NTHR - 1) / NTHR;
+    constexpr int SB_OFF = A_BYTES + B_BYTES + SA_LD * NTHR * 4;
+    constexpr int STAGE = SB_OFF + NTHR * 4;
+    constexpr int WGR = RB / WR;                      // compute waves along M
+    constexpr int WGC = CB / WC;                      // compute waves along N
+    static_assert(A_LD * NTHR * 16 == A_BYTES, "A stage must split evenly over the threads");
+    static_assert(B_LD * NTHR * 16 == B_BYTES, "B stage must split evenly over the threads");
+    static_assert(SB_N <= NTHR, "one weight scale per thread and stage");
+    static_assert(WGR * WR == RB && WGC * WC == CB && WGR * WGC <= WAVES, "wave tiling");
+    static_assert(PF % 2 == 0, "the LDS double buffer is indexed by stage parity");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    const int nt = tile / m_tiles;
+    const int mt = tile - nt * m_tiles;
+    const int m0 = mt * BM;
+    const int NB = (N + 15) >> 4;
+    const int nkb = K / KBK;
+    const int ncb = (N + 127) >> 7;                   // columns of sB in use
+    const int nbw = nt * CB;                          // first column block of the workgroup
+
+    const int nst = (nkb + KB_ST - 1) / KB_ST;
+    const int rows_valid = M - m0 < BM ? M - m0 : BM;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const uint32_t OOB = 0x80000000u;
+
+    // ---- load maps (per stage, relative to the stage's K origin)
+    uint32_t a_voff[A_LD];
+#pragma unroll
+    for (int j = 0; j < A_LD; ++j) {
+        const int u = j * NTHR + tid;
+        const int row = u / CPR;
+        a_voff[j] = (uint32_t)(row * lda + (((u % CPR) ^ (row & 7)) * 16));
+    }
+    // B chunk u = j*NTHR + tid: column block c = u / (KB_ST*128), byte
+    // 16*(u % (KB_ST*128)) of that block's contiguous run; LDS byte
+    // A_BYTES + 16u.  A run holds a whole number of waves' chunks, so c is
+    // the same for all lanes of a wave: computed from the wave index it stays
+    // in scalar registers, and so does the buffer resource built from it.
+    uint32_t b_voff[B_LD];
+    int b_cb[B_LD];
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j) {
+        const int u = j * NTHR + tid;
+        b_cb[j] = (j * NTHR + 64 * wave) / (KB_ST * 128);
+        b_voff[j] = (uint32_t)((u % (KB_ST * 128)) * 16);
+    }
+    // sA value v = (K block q, row) -> LDS slot v = q*BM + row
+    uint32_t sa_voff[SA_LD];
+#pragma unroll
+    for (int j = 0; j < SA_LD; ++j) {
+        const int v = j * NTHR + tid;
+        const int q = v / BM, row = v % BM;
+        sa_voff[j] = v < SA_N ? (uint32_t)((row * ldsa + q) * 4) : OOB;
+    }
+    // sB value t = (column block c, K block q) -> LDS slot t = c*KB_ST + q
+    uint32_t sb_voff;
+    {
+        const int c = tid / KB_ST, q = tid % KB_ST;
+        const int nb = nbw + c;
+        sb_voff = (tid < SB_N && nb < NB) ? (uint32_t)((q * ldsb + (16 * nb) / 128) * 4) : OOB;
+    }
+
+    // ---- compute role
+    const bool computes = wave < WGR * WGC;
+    const int wr0 = (wave / WGC) * WR;                // first row block of this wave
+    const int wc0 = (wave % WGC) * WC;                // first column block (in the workgroup)
+
+    u32x4 areg[PF][A_LD];
+    u32x4 breg[PF][B_LD];
+    float sareg[PF][SA_LD];
+    float sbreg[PF];
+    f32x4 acc[WR][WC];
+#pragma unroll
+    for (int r = 0; r < WR; ++r)
+#pragma unroll
+        for (int c = 0; c < WC; ++c)
+            acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int s, u32x4 (&ar)[A_LD], u32x4 (&br)[B_LD], float (&sar)[SA_LD], float& sbr) {
+        const bool live = s < nst;
+        const int kb0 = s * KB_ST;
+        const int kst = kb0 * KBK;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+            A + (int64_t)m0 * lda + kst,
+            live ? clamp_bytes((int64_t)(rows_valid - 1) * lda + K - kst) : 0u);
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
+            sA + (int64_t)m0 * ldsa + kb0,
+            live ? clamp_bytes(((int64_t)(rows_valid - 1) * ldsa + nkb - kb0) * 4) : 0u);
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
+            sB + (int64_t)kb0 * ldsb,
+            live ? clamp_bytes(((int64_t)(nkb - 1 - kb0) * ldsb + ncb) * 4) : 0u);
+#pragma unroll
+        for (int j = 0; j < A_LD; ++j)
+            ar[j] = buf_load16(ra, a_voff[j]);
+#pragma unroll
+        for (int j = 0; j < B_LD; ++j) {
+            const int nb = nbw + b_cb[j];
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+                Bp + ((int64_t)nb * nkb + kb0) * BTILE,
+                live && nb < NB ? clamp_bytes((int64_t)(nkb - kb0) * BTILE) : 0u);
+            br[j] = buf_load16(rb, b_voff[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < SA_LD; ++j)
+            sar[j] = __builtin_bit_cast(float,
+                                        __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)sa_voff[j], 0, 0));
+        sbr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsb, (int)sb_voff, 0, 0));
+    };
+
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+        issue(p, areg[p], breg[p], sareg[p], sbreg[p]);
+
+    const int nst_pad = (nst + PF - 1) / PF * PF;
+    for (int s0 = 0; s0 < nst_pad; s0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            const int s = s0 + p;
+            uint8_t* buf = smem + (p & 1) * STAGE;
+#pragma unroll
+            for (int j = 0; j < A_LD; ++j)
+                *reinterpret_cast<u32x4*>(buf + (j * NTHR + tid) * 16) = areg[p][j];
+#pragma unroll
+            for (int j = 0; j < B_LD; ++j)
+                *reinterpret_cast<u32x4*>(buf + A_BYTES + (j * NTHR + tid) * 16) = breg[p][j];
+#pragma unroll
+            for (int j = 0; j < SA_LD; ++j)
+                *reinterpret_cast<float*>(buf + A_BYTES + B_BYTES + (j * NTHR + tid) * 4) = sareg[p][j];
+            *reinterpret_cast<float*>(buf + SB_OFF + tid * 4) = sbreg[p];
+            issue(s + PF, areg[p], breg[p], sareg[p], sbreg[p]);
+            __syncthreads();
+            if (computes) {
+#pragma unroll
+                for (int q = 0; q < KB_ST; ++q) {
+                    if (s * KB_ST + q < nkb) {
+                        i32x8 bv[WC];
+                        float sb[WC];
+#pragma unroll
+                        for (int c = 0; c < WC; ++c) {
+                            const uint8_t* bt = buf + A_BYTES + ((wc0 + c) * KB_ST + q) * BTILE + lane * 16;
+                            const u32x4 b0 = *reinterpret_cast<const u32x4*>(bt);
+                            const u32x4 b1 = *reinterpret_cast<const u32x4*>(bt + 1024);
+                            bv[c] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                                          (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+                            sb[c] = *reinterpret_cast<const float*>(
+                                buf + SB_OFF + ((wc0 + c) * KB_ST + q) * 4);
+                        }
+#pragma unroll
+                        for (int r = 0; r < WR; ++r) {
+                            const int row = 16 * (wr0 + r) + li;
+                            const int c0 = q * 8 + 2 * lg;
+                            const u32x4 a0 = *reinterpret_cast<const u32x4*>(
+                                buf + (row * CPR + (c0 ^ (row & 7))) * 16);
+                            const u32x4 a1 = *reinterpret_cast<const u32x4*>(
+                                buf + (row * CPR + ((c0 + 1) ^ (row & 7))) * 16);
+                            const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                            const f32x4 sa4 = *reinterpret_cast<const f32x4*>(
+                                buf + A_BYTES + B_BYTES + (q * BM + 16 * (wr0 + r) + 4 * lg) * 4);
+#pragma unroll
+                            for (int c = 0; c < WC; ++c) {
+                                // fp8 e4m3 x fp8 e4m3, unit E8M0 block scales (127 = 2^0)
+                                const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                    av, bv[c], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    acc[r][c][j] = __builtin_fmaf(P[j], sa4[j] * sb[c], acc[r][c][j]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    if (computes) {
+#pragma unroll
+        for (int c = 0; c < WC; ++c) {
+            const int col = 16 * (nbw + wc0 + c) + li;
+#pragma unroll
+            for (int r = 0; r < WR; ++r) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = m0 + 16 * (wr0 + r) + 4 * lg + j;
+                    if (row < M && col < N)
+                        C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[r][c][j]);
+                }
+            }
+        }
+    }
+}
+
+// One thread per 16-byte packed chunk: u = ((nb*KB + kb)*2 + h)*64 + l.
+__global__ void pack_fp8_kernel(int N, int K, const uint8_t* __restrict__ B, int64_t ldb,
+                                uint8_t* __restrict__ Bp, int64_t nchunks)
+{
+    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= nchunks)
+        return;
+    const int KB = K / KBK;
+    const int l = (int)(u & 63);
+    const int h = (int)((u >> 6) & 1);
+    const int64_t t = u >> 7;
+    const int kb = (int)(t % KB);
+    const int nb = (int)(t / KB);
+    const int n = 16 * nb + (l & 15);
+    const int k0 = KBK * kb + 32 * (l >> 4) + 16 * h;
+    uint32_t w[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t byte = n < N ? B[(int64_t)(k0 + 4 * d + e) * ldb + n] : 0u;
+            v |= byte << (8 * e);
+        }
+        w[d] = v;
+    }
+    *reinterpret_cast<u32x4*>(Bp + u * 16) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF>
+hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
+{
+    const int n_tiles = ((a.N + 15) / 16 + CB - 1) / CB;
+    const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
+    gemm_fp8_packed_kernel<WAVES, RB, CB, WR, WC, KB_ST, PF>
+        <<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0, stream>>>(
+            a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
+            (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Launch geometry (tile sharing only: every geometry runs the same
+// per-element arithmetic).  The largest output tile that still gives each
+// compute unit a workgroup wins; below that one 16-column block per
+// workgroup, with as many 16-row blocks as M needs (up to four).
+int fp8_packed_geometry(int M, int N)
+{
+    const int nb = (N + 15) / 16;
+    const int mt64 = (M + 63) / 64;
+    if (M > 64 && mt64 * ((nb + 3) / 4) >= 256)
+        return 6;                                  // 64 x 64
+    if (M > 64 && mt64 * ((nb + 1) / 2) >= 256)
+        return 5;                                  // 64 x 32
+    if (M > 48)
+        return 4;                                  // 64 x 16
+    if (M > 32)
+        return 3;                                  // 48 x 16
+    if (M > 16)
+        return 2;                                  // 32 x 16
+    return 1;                                      // 16 x 16
+}
+
+hipError_t launch_fp8_packed(const GemmArgs& a, hipStream_t stream)
+{
+    switch (fp8_packed_geometry(a.M, a.N)) {
+    case 6: return launch_geometry<4, 4, 4, 2, 2, 1, 4>(a, stream);
+    case 5: return launch_geometry<4, 4, 2, 2, 1, 2, 4>(a, stream);
+    case 4: return launch_geometry<4, 4, 1, 1, 1, 4, 4>(a, stream);
+    case 3: return launch_geometry<4, 3, 1, 1, 1, 4, 4>(a, stream);
+    case 2: return launch_geometry<4, 2, 1, 1, 1, 4, 6>(a, stream);
+    default: return launch_geometry<4, 1, 1, 1, 1, 4, 8>(a, stream);
+    }
+}
+
+hipError_t launch_pack_fp8(int N, int K, const uint8_t* B, int64_t ldb, uint8_t* Bp,
+                           hipStream_t stream)
+{
+    const int64_t nchunks = (int64_t)((N + 15) / 16) * (K / KBK) * 128;
+    if (nchunks == 0)
+        return hipSuccess;
+    pack_fp8_kernel<<<dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, stream>>>(
+        N, K, B, ldb, Bp, nchunks);
+    return hipGetLastError();
+}
+
+}  // namespace bigemm

@@ -33,6 +33,13 @@ hipError_t launch_pack_b_bf16(int N, int K, const uint16_t* B, int64_t ldb, uint
 int packed_geometry(int M, int N);
 hipError_t launch_fp8bs(const GemmArgs& a, const Schedule& s, hipStream_t stream);
 hipError_t launch_fp4w(const GemmArgs& a, const Schedule& s, hipStream_t stream);
+hipError_t launch_fp8_packed(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_pack_fp8(int N, int K, const uint8_t* B, int64_t ldb, uint8_t* Bp,
+                           hipStream_t stream);
+int fp8_packed_geometry(int M, int N);
+hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_pack_fp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sB,
+                           int64_t ldsb, uint8_t* Bp, hipStream_t stream);
 hipError_t launch_bf16_splitk(const GemmArgs& a, const Schedule& s, float* ws, int splits,
                               hipStream_t stream);
 

@@ -150,3 +150,56 @@ def test_schedule_has_no_m_argument():
     assert lib.bi_schedule_query(7, 8192, 8192, ctypes.byref(bigemm.BiSchedule())) == UNSUP
     assert lib.bi_schedule_query(0, 8192, 8192, None) == NULL
     assert lib.bi_schedule_query(1, 8192, 100, ctypes.byref(bigemm.BiSchedule())) == SHAPE
+
+
+def test_packed_sizes():
+    nb = lambda N: (N + 15) // 16
+    assert bigemm.packed_b_bytes(bigemm.BI_BF16, 300, 100) == nb(300) * 4 * 1024
+    assert bigemm.packed_b_bytes(bigemm.BI_FP8_BS, 2048, 7168) == 128 * 56 * 2048
+    assert bigemm.packed_b_bytes(bigemm.BI_FP8_BS, 2048, 100) == 0          # K % 128
+    assert bigemm.packed_b_bytes(bigemm.BI_FP4_W, 14336, 4096) == 896 * 32 * 1088
+    assert bigemm.packed_b_bytes(bigemm.BI_FP4_W, 130, 288) == nb(130) * 3 * 1088
+    assert bigemm.packed_b_bytes(bigemm.BI_FP4_W, 131, 288) == 0            # odd N
+    assert bigemm.packed_b_bytes(bigemm.BI_FP4_W, 130, 48) == 0             # K % 32
+    assert bigemm.packed_b_bytes(7, 16, 16) == 0
+    assert bigemm.packed_b_bytes(bigemm.BI_BF16, -1, 16) == 0
+
+
+def test_packed_validation():
+    need = lambda dt, N, K: bigemm.packed_b_bytes(dt, N, K)
+    # bf16
+    f = lambda M, N, K, A=P, lda=None, Bp=P, nb=None, C=P, ldc=None: lib.bi_gemm_bf16_packed(
+        M, N, K, A, K if lda is None else lda, Bp, need(0, N, K) if nb is None else nb, C,
+        N if ldc is None else ldc, None)
+    assert f(8, 64, 64, nb=need(0, 64, 64) - 1) == WS
+    assert f(8, 64, 64, Bp=P + 8) == ALIGN
+    assert f(8, 64, 64, Bp=None) == NULL
+    assert f(0, 64, 64, A=None, Bp=None, C=None) == OK
+    # fp8
+    g = lambda M, N, K, A=P, lda=None, sA=P, Bp=P, nb=None, sB=P, ldsb=None, C=P: \
+        lib.bi_gemm_fp8_blockscaled_packed(M, N, K, A, K if lda is None else lda, sA, max(K // 128, 1),
+                                           Bp, need(1, N, K) if nb is None else nb, sB,
+                                           (N + 127) // 128 if ldsb is None else ldsb, C, N, None)
+    assert g(4, 64, 100) == SHAPE
+    assert g(4, 64, 256, nb=need(1, 64, 256) - 16) == WS
+    assert g(4, 64, 256, sA=None) == NULL
+    assert g(4, 300, 256, ldsb=2) == STRIDE
+    assert g(4, 64, 256, lda=264) == ALIGN
+    assert g(4, 64, 256, sB=P + 2) == ALIGN
+    assert g(0, 64, 256, A=None, sA=None, Bp=None, sB=None, C=None) == OK
+    assert lib.bi_pack_b_fp8(64, 100, P, 64, P, 1 << 20, None) == SHAPE
+    assert lib.bi_pack_b_fp8(64, 256, P, 32, P, 1 << 20, None) == STRIDE
+    assert lib.bi_pack_b_fp8(64, 256, P, 64, P, need(1, 64, 256) - 1, None) == WS
+    assert lib.bi_pack_b_fp8(64, 256, None, 64, P, 1 << 20, None) == NULL
+    # fp4
+    h = lambda M, N, K, A=P, Bp=P, nb=None, C=P: lib.bi_gemm_fp4_w_packed(
+        M, N, K, A, K, Bp, need(2, N, K) if nb is None else nb, C, N, None)
+    assert h(4, 64, 48) == SHAPE
+    assert h(4, 63, 64) == SHAPE
+    assert h(4, 64, 64, nb=need(2, 64, 64) - 1) == WS
+    assert h(4, 64, 64, Bp=P + 4) == ALIGN
+    assert h(4, 64, 64, Bp=None) == NULL
+    assert lib.bi_pack_b_fp4(64, 64, P, 32, P, 64, P, need(2, 64, 64) - 1, None) == WS
+    assert lib.bi_pack_b_fp4(64, 64, P, 16, P, 64, P, 1 << 20, None) == STRIDE
+    assert lib.bi_pack_b_fp4(64, 64, P, 32, None, 64, P, 1 << 20, None) == NULL
+    assert lib.bi_pack_b_fp4(64, 48, P, 32, P, 64, P, 1 << 20, None) == SHAPE
