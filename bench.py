@@ -71,19 +71,40 @@ def roof(M, N, K, nbytes, t_us, mfma_peak):
             "bound": "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= f / (mfma_peak * 1e12) else "mfma"}
 
 
+def capture(torch, fn, n):
+    """A HIP graph of n calls of fn (each call enqueues library kernels on
+    torch's current stream).  Replaying it puts the launches on the GPU
+    back-to-back, so a timing measures the kernels and not the host's
+    per-call launch rate (several microseconds per ctypes call)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def time_launches(torch, fn, reps, rounds):
-    """Median and min per-launch time (us) over `rounds` rounds of `reps`
-    back-to-back launches, measured with HIP events on the launch stream."""
+    """Median and min per-launch time (us) over `rounds` replays of a graph of
+    `reps` back-to-back launches, measured with HIP events on the stream the
+    kernels run on."""
+    g = capture(torch, fn, reps)
     per = []
     for _ in range(rounds):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(reps):
-            fn()
+        g.replay()
         e1.record()
         e1.synchronize()
         per.append(e0.elapsed_time(e1) * 1e3 / reps)
+    del g
     per.sort()
     return per[len(per) // 2], per[0]
 
@@ -321,14 +342,23 @@ def replay(torch, bg, inputs, steps=1000):
     As = [P.index_select(0, b) for b in batches]
     C = torch.empty((256, N), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
+    it = iter(As)
+
+    def one():
+        A = next(it)
+        bg.gemm_bf16(A, B, out=C[:A.shape[0]])
+
+    # the warm-up call inside capture() consumes the first batch: time the rest
+    g = capture(torch, one, steps - 1)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for A in As:
-        bg.gemm_bf16(A, B, out=C[:A.shape[0]])
+    g.replay()
     e1.record()
     e1.synchronize()
     ms = e0.elapsed_time(e1)
+    As = As[1:]
+    steps -= 1
     rows = sum(a.shape[0] for a in As)
     return {"steps": steps, "rows": rows, "ms": round(ms, 3),
             "tflops": round(flops(rows, N, K) / (ms * 1e-3) / 1e12, 2),
@@ -372,14 +402,17 @@ def main():
     for _ in range(args.warmup):
         wl.step()
     torch.cuda.synchronize()
+    # the timed region replays a graph of exactly `steps` steps (9 launches
+    # each, every launch on the next rotated copy of A and B)
+    g = capture(torch, wl.step, args.steps)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(args.steps):
-        wl.step()
+    g.replay()
     e1.record()
     torch.cuda.synchronize()
+    del g
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
     log(f"timed {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)")

@@ -13,15 +13,14 @@
 // 32-long K block kb, ascending, P = v_mfma_f32_16x16x32_bf16(A, e2m1 -> bf16
 // exact, 0) then acc = fma(P, e4m3(sB[kb,n]), acc).  Identical bits to the
 // unpacked entry point; rows independent of M, position and companions.
-// Launch geometries (as for bf16): streaming (2 waves x 16 columns, BM 16),
-// large (4 waves x 2 column blocks, BM 64).
+// Launch geometries: streaming (2 waves x 16 columns, BM 16), medium
+// (4 waves x 16 columns, BM 64), large (4 waves x 32 columns, BM 64).
 #include "common.h"
 #include "launch.h"
 
 namespace bigemm {
 namespace {
 
-constexpr int KSTEP = 32;     // = scale block
 
 template <int BYTE>
 __device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w)
@@ -49,10 +48,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     constexpr int NTHR = 64 * WAVES;
     constexpr int BM = 16 * RB;
     constexpr int BKS = QS * 128;
-    constexpr int KS_ST = QS * 4;
     constexpr int CPR = BKS * 2 / 16;
     constexpr int A_STAGE = BM * BKS * 2;
     constexpr int A_LD = A_STAGE / (NTHR * 16);
+    // K steps per product group of the small-tile path: 4 or 2 steps
+    constexpr int SG = RB * CB >= 2 ? 2 : 4;
     static_assert(A_LD * NTHR * 16 == A_STAGE, "A stage must split evenly over the threads");
     static_assert(PF % 2 == 0, "the LDS double buffer is indexed by stage parity");
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * A_STAGE];
@@ -66,7 +66,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     const int m0 = mt * BM;
     const int NB = (N + 15) >> 4;
     const int KQ = (K + 127) / 128;
-    const int nkb = K / KSTEP;
     const int nb0 = nt * (WAVES * CB) + wave * CB;
     const uint8_t* scales = Bp + (int64_t)NB * KQ * 1024;
 
@@ -145,32 +144,83 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
             for (int j = 0; j < A_LD; ++j)
                 *reinterpret_cast<u32x4*>(abuf + (j * NTHR + tid) * 16) = areg[p][j];
             __syncthreads();
+            if constexpr (RB * CB <= 2) {
+                // Small tiles.  Per group of SG K steps: (1) the block
+                // products P, each into its own registers, so the LDS reads,
+                // conversions and MFMAs of the group overlap; (2) the ordered
+                // accumulation acc = fma(P, scale, acc), steps ascending.  No
+                // per-step guard: steps past K have zero A (cleared above),
+                // zero codes and zero scales, and fma(+0, +0, acc) leaves acc
+                // unchanged (acc is never -0).
 #pragma unroll
-            for (int q = 0; q < QS; ++q) {
+                for (int q = 0; q < QS; ++q) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int ks = 4 * q + t;
-                    if (s * KS_ST + ks < nkb) {
-                        u32x4 bfrag[CB];
-                        float sc[CB];
+                    for (int t0 = 0; t0 < 4; t0 += SG) {
+                        f32x4 P[SG][RB][CB];
+                        float sc[SG][CB];
 #pragma unroll
-                        for (int c = 0; c < CB; ++c) {
-                            const uint32_t w = qreg[p][q][c][t];
-                            bfrag[c] = u32x4{e2m1x2_to_bf16x2<0>(w), e2m1x2_to_bf16x2<1>(w),
-                                             e2m1x2_to_bf16x2<2>(w), e2m1x2_to_bf16x2<3>(w)};
-                            sc[c] = e4m3_to_f32((sreg[p][q][c] >> (8 * t)) & 0xFFu);
-                        }
-#pragma unroll
-                        for (int r = 0; r < RB; ++r) {
-                            const int row = 16 * r + li;
-                            const u32x4 afrag = *reinterpret_cast<const u32x4*>(
-                                abuf + (row * CPR + ((ks * 4 + lg) ^ (row & 7))) * 16);
+                        for (int tt = 0; tt < SG; ++tt) {
+                            const int t = t0 + tt;
+                            const int ks = 4 * q + t;
+                            u32x4 bfrag[CB];
 #pragma unroll
                             for (int c = 0; c < CB; ++c) {
-                                const f32x4 P = mfma_bf16(afrag, bfrag[c], f32x4{0.f, 0.f, 0.f, 0.f});
+                                const uint32_t w = qreg[p][q][c][t];
+                                bfrag[c] = u32x4{e2m1x2_to_bf16x2<0>(w), e2m1x2_to_bf16x2<1>(w),
+                                                 e2m1x2_to_bf16x2<2>(w), e2m1x2_to_bf16x2<3>(w)};
+                                sc[tt][c] = e4m3_to_f32((sreg[p][q][c] >> (8 * t)) & 0xFFu);
+                            }
 #pragma unroll
-                                for (int j = 0; j < 4; ++j)
-                                    acc[r][c][j] = __builtin_fmaf(P[j], sc[c], acc[r][c][j]);
+                            for (int r = 0; r < RB; ++r) {
+                                const int row = 16 * r + li;
+                                const u32x4 afrag = *reinterpret_cast<const u32x4*>(
+                                    abuf + (row * CPR + ((ks * 4 + lg) ^ (row & 7))) * 16);
+#pragma unroll
+                                for (int c = 0; c < CB; ++c)
+                                    P[tt][r][c] = mfma_bf16(afrag, bfrag[c], f32x4{0.f, 0.f, 0.f, 0.f});
+                            }
+                        }
+#pragma unroll
+                        for (int tt = 0; tt < SG; ++tt)
+#pragma unroll
+                            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                                for (int c = 0; c < CB; ++c)
+#pragma unroll
+                                    for (int j = 0; j < 4; ++j)
+                                        acc[r][c][j] = __builtin_fmaf(P[tt][r][c][j], sc[tt][c], acc[r][c][j]);
+                    }
+                }
+            } else {
+                // Large tiles: RB*CB independent products per K step already
+                // keep the MFMA unit busy; steps past K are skipped.
+#pragma unroll
+                for (int q = 0; q < QS; ++q) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int ks = 4 * q + t;
+                        if (s * 4 * QS + ks < K / 32) {
+                            u32x4 bfrag[CB];
+                            float sc[CB];
+#pragma unroll
+                            for (int c = 0; c < CB; ++c) {
+                                const uint32_t w = qreg[p][q][c][t];
+                                bfrag[c] = u32x4{e2m1x2_to_bf16x2<0>(w), e2m1x2_to_bf16x2<1>(w),
+                                                 e2m1x2_to_bf16x2<2>(w), e2m1x2_to_bf16x2<3>(w)};
+                                sc[c] = e4m3_to_f32((sreg[p][q][c] >> (8 * t)) & 0xFFu);
+                            }
+#pragma unroll
+                            for (int r = 0; r < RB; ++r) {
+                                const int row = 16 * r + li;
+                                const u32x4 afrag = *reinterpret_cast<const u32x4*>(
+                                    abuf + (row * CPR + ((ks * 4 + lg) ^ (row & 7))) * 16);
+#pragma unroll
+                                for (int c = 0; c < CB; ++c) {
+                                    const f32x4 P = mfma_bf16(afrag, bfrag[c], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                                    for (int j = 0; j < 4; ++j)
+                                        acc[r][c][j] = __builtin_fmaf(P[j], sc[c], acc[r][c][j]);
+                                }
                             }
                         }
                     }
@@ -251,15 +301,18 @@ hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 
 }  // namespace
 
+// Launch geometry (tile sharing only: the per-element arithmetic is the same
+// for all): 64 x 128 tiles once they still give each compute unit a
+// workgroup, 64 x 64 from 17 rows, else two waves of 16 x 16 streaming.
 hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream)
 {
-    switch (packed_geometry(a.M, a.N)) {
-    case 4: return launch_geometry<4, 2, 4, 1, 4>(a, stream);
-    case 3: return launch_geometry<4, 1, 4, 1, 4>(a, stream);
-    case 2: return launch_geometry<2, 1, 4, 1, 4>(a, stream);
-    case 1: return launch_geometry<2, 1, 2, 1, 6>(a, stream);
-    default: return launch_geometry<2, 1, 1, 2, 4>(a, stream);
-    }
+    const int nb = (a.N + 15) / 16;
+    const int mt64 = (a.M + 63) / 64;
+    if (a.M >= 64 && mt64 * ((nb + 7) / 8) >= 256)
+        return launch_geometry<4, 2, 4, 1, 2>(a, stream);
+    if (a.M > 16)
+        return launch_geometry<4, 1, 4, 1, 4>(a, stream);
+    return launch_geometry<2, 1, 1, 2, 4>(a, stream);
 }
 
 hipError_t launch_pack_fp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sB,

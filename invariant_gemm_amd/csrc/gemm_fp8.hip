@@ -164,6 +164,20 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(
         for (int p = 0; p < PF; ++p) {
             const int s = s0 + p;
             uint8_t* buf = smem + (p & 1) * STAGE;
+            if ((s + 1) * KB_PER_ST > nkb) {
+                // K tail: blocks past K must contribute exactly zero.  B and sB
+                // read as zero there; A and sA may hold anything in their row
+                // pitch, so they are cleared.
+                const int qv = nkb - s * KB_PER_ST;
+#pragma unroll
+                for (int j = 0; j < A_LD; ++j) {
+                    const int c = j * 256 + tid;
+                    if (((c & 15) ^ ((c >> 4) & 7)) >= 8 * qv)
+                        areg[p][j] = u32x4{0u, 0u, 0u, 0u};
+                }
+                if ((tid >> 6) >= qv)
+                    sareg[p] = 0.f;
+            }
 #pragma unroll
             for (int j = 0; j < A_LD; ++j)
                 *reinterpret_cast<u32x4*>(buf + (j * 256 + tid) * 16) = areg[p][j];
@@ -173,29 +187,34 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(
             issue(s + PF, areg[p], breg[p], sareg[p], sbreg[p]);
             __syncthreads();
             if (active) {
+                // (1) the stage's block products, each into its own registers
+                // (their LDS reads and MFMAs overlap), then (2) the ordered
+                // accumulation.  No per-block guard: blocks past K are
+                // all-zero and fma(+0, +0, acc) == acc (acc is never -0).
+                f32x4 P[KB_PER_ST];
 #pragma unroll
                 for (int kb = 0; kb < KB_PER_ST; ++kb) {
-                    if (s * KB_PER_ST + kb < nkb) {
-                        const u32x4 a0 = *reinterpret_cast<const u32x4*>(buf + a_rd[kb][0]);
-                        const u32x4 a1 = *reinterpret_cast<const u32x4*>(buf + a_rd[kb][1]);
-                        const u32x2 b0 = ds_read_tr8(buf + b_rd[kb][0]);
-                        const u32x2 b1 = ds_read_tr8(buf + b_rd[kb][1]);
-                        const u32x2 b2 = ds_read_tr8(buf + b_rd[kb][2]);
-                        const u32x2 b3 = ds_read_tr8(buf + b_rd[kb][3]);
-                        const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                                          (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-                        const i32x8 bv = {(int)b0[0], (int)b0[1], (int)b1[0], (int)b1[1],
-                                          (int)b2[0], (int)b2[1], (int)b3[0], (int)b3[1]};
-                        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                        // fp8 e4m3 x fp8 e4m3, unit E8M0 block scales (127 = 2^0)
-                        const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            av, bv, z, 0, 0, 0, 127, 0, 127);
-                        const f32x4 sa4 = *reinterpret_cast<const f32x4*>(buf + sa_rd + kb * BM * 4);
-                        const float sb = *reinterpret_cast<const float*>(buf + sb_rd + kb * 4);
+                    const u32x4 a0 = *reinterpret_cast<const u32x4*>(buf + a_rd[kb][0]);
+                    const u32x4 a1 = *reinterpret_cast<const u32x4*>(buf + a_rd[kb][1]);
+                    const u32x2 b0 = ds_read_tr8(buf + b_rd[kb][0]);
+                    const u32x2 b1 = ds_read_tr8(buf + b_rd[kb][1]);
+                    const u32x2 b2 = ds_read_tr8(buf + b_rd[kb][2]);
+                    const u32x2 b3 = ds_read_tr8(buf + b_rd[kb][3]);
+                    const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                      (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                    const i32x8 bv = {(int)b0[0], (int)b0[1], (int)b1[0], (int)b1[1],
+                                      (int)b2[0], (int)b2[1], (int)b3[0], (int)b3[1]};
+                    // fp8 e4m3 x fp8 e4m3, unit E8M0 block scales (127 = 2^0)
+                    P[kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                }
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            acc[j] = __builtin_fmaf(P[j], sa4[j] * sb, acc[j]);
-                    }
+                for (int kb = 0; kb < KB_PER_ST; ++kb) {
+                    const f32x4 sa4 = *reinterpret_cast<const f32x4*>(buf + sa_rd + kb * BM * 4);
+                    const float sb = *reinterpret_cast<const float*>(buf + sb_rd + kb * 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[j] = __builtin_fmaf(P[kb][j], sa4[j] * sb, acc[j]);
                 }
             }
         }

@@ -97,6 +97,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
         b_cb[j] = (j * NTHR + 64 * wave) / (KB_ST * 128);
         b_voff[j] = (uint32_t)((u % (KB_ST * 128)) * 16);
     }
+    // Every load below is issued unconditionally, in the same order in every
+    // stage, so the compiler's wait counts keep PF stages in flight (a
+    // conditional load would make it assume the shortest history).
     // sA value v = (K block q, row) -> LDS slot v = q*BM + row
     uint32_t sa_voff[SA_LD];
 #pragma unroll
@@ -170,6 +173,24 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
         for (int p = 0; p < PF; ++p) {
             const int s = s0 + p;
             uint8_t* buf = smem + (p & 1) * STAGE;
+            if ((s + 1) * KB_ST > nkb) {
+                // K tail: the stage's blocks at kb >= K/128 must contribute
+                // exactly zero.  B and sB read as zero there (outside their
+                // buffer extents); A and sA may hold anything in their row
+                // pitch, so they are cleared here.
+                const int qv = nkb - s * KB_ST;              // valid blocks of this stage
+#pragma unroll
+                for (int j = 0; j < A_LD; ++j) {
+                    const int u = j * NTHR + tid;
+                    const int cg = (u % CPR) ^ ((u / CPR) & 7);   // chunk loaded into this register
+                    if (cg >= 8 * qv)
+                        areg[p][j] = u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int j = 0; j < SA_LD; ++j)
+                    if ((j * NTHR + tid) / BM >= qv)
+                        sareg[p][j] = 0.f;
+            }
 #pragma unroll
             for (int j = 0; j < A_LD; ++j)
                 *reinterpret_cast<u32x4*>(buf + (j * NTHR + tid) * 16) = areg[p][j];
@@ -183,43 +204,57 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
             issue(s + PF, areg[p], breg[p], sareg[p], sbreg[p]);
             __syncthreads();
             if (computes) {
+                // Two phases per stage.  (1) every block product P of the
+                // stage, each into its own registers, so that the LDS reads
+                // and MFMAs of different blocks overlap; (2) the ordered
+                // accumulation acc = fma(P, sA*sB, acc), blocks ascending.
+                // No per-block guard: blocks past K are all-zero (tail
+                // clearing above) and fma(+0, +0, acc) == acc bit for bit, as
+                // acc can never be -0.
+                f32x4 P[KB_ST][WR][WC];
 #pragma unroll
                 for (int q = 0; q < KB_ST; ++q) {
-                    if (s * KB_ST + q < nkb) {
-                        i32x8 bv[WC];
-                        float sb[WC];
+                    i32x8 bv[WC];
 #pragma unroll
-                        for (int c = 0; c < WC; ++c) {
-                            const uint8_t* bt = buf + A_BYTES + ((wc0 + c) * KB_ST + q) * BTILE + lane * 16;
-                            const u32x4 b0 = *reinterpret_cast<const u32x4*>(bt);
-                            const u32x4 b1 = *reinterpret_cast<const u32x4*>(bt + 1024);
-                            bv[c] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
-                                          (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-                            sb[c] = *reinterpret_cast<const float*>(
-                                buf + SB_OFF + ((wc0 + c) * KB_ST + q) * 4);
-                        }
+                    for (int c = 0; c < WC; ++c) {
+                        const uint8_t* bt = buf + A_BYTES + ((wc0 + c) * KB_ST + q) * BTILE + lane * 16;
+                        const u32x4 b0 = *reinterpret_cast<const u32x4*>(bt);
+                        const u32x4 b1 = *reinterpret_cast<const u32x4*>(bt + 1024);
+                        bv[c] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                                      (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+                    }
 #pragma unroll
-                        for (int r = 0; r < WR; ++r) {
-                            const int row = 16 * (wr0 + r) + li;
-                            const int c0 = q * 8 + 2 * lg;
-                            const u32x4 a0 = *reinterpret_cast<const u32x4*>(
-                                buf + (row * CPR + (c0 ^ (row & 7))) * 16);
-                            const u32x4 a1 = *reinterpret_cast<const u32x4*>(
-                                buf + (row * CPR + ((c0 + 1) ^ (row & 7))) * 16);
-                            const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                                              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-                            const f32x4 sa4 = *reinterpret_cast<const f32x4*>(
-                                buf + A_BYTES + B_BYTES + (q * BM + 16 * (wr0 + r) + 4 * lg) * 4);
+                    for (int r = 0; r < WR; ++r) {
+                        const int row = 16 * (wr0 + r) + li;
+                        const int c0 = q * 8 + 2 * lg;
+                        const u32x4 a0 = *reinterpret_cast<const u32x4*>(
+                            buf + (row * CPR + (c0 ^ (row & 7))) * 16);
+                        const u32x4 a1 = *reinterpret_cast<const u32x4*>(
+                            buf + (row * CPR + ((c0 + 1) ^ (row & 7))) * 16);
+                        const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                          (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
 #pragma unroll
-                            for (int c = 0; c < WC; ++c) {
-                                // fp8 e4m3 x fp8 e4m3, unit E8M0 block scales (127 = 2^0)
-                                const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                                    av, bv[c], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                        for (int c = 0; c < WC; ++c)
+                            // fp8 e4m3 x fp8 e4m3, unit E8M0 block scales (127 = 2^0)
+                            P[q][r][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                av, bv[c], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                    }
+                }
 #pragma unroll
-                                for (int j = 0; j < 4; ++j)
-                                    acc[r][c][j] = __builtin_fmaf(P[j], sa4[j] * sb[c], acc[r][c][j]);
-                            }
-                        }
+                for (int q = 0; q < KB_ST; ++q) {
+                    float sb[WC];
+#pragma unroll
+                    for (int c = 0; c < WC; ++c)
+                        sb[c] = *reinterpret_cast<const float*>(buf + SB_OFF + ((wc0 + c) * KB_ST + q) * 4);
+#pragma unroll
+                    for (int r = 0; r < WR; ++r) {
+                        const f32x4 sa4 = *reinterpret_cast<const f32x4*>(
+                            buf + A_BYTES + B_BYTES + (q * BM + 16 * (wr0 + r) + 4 * lg) * 4);
+#pragma unroll
+                        for (int c = 0; c < WC; ++c)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                acc[r][c][j] = __builtin_fmaf(P[q][r][c][j], sa4[j] * sb[c], acc[r][c][j]);
                     }
                 }
             }
@@ -287,35 +322,30 @@ hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 }  // namespace
 
 // Launch geometry (tile sharing only: every geometry runs the same
-// per-element arithmetic).  The largest output tile that still gives each
-// compute unit a workgroup wins; below that one 16-column block per
-// workgroup, with as many 16-row blocks as M needs (up to four).
+// per-element arithmetic).  64 x 64 tiles once they still give each compute
+// unit a workgroup, 64 x 32 above 128 rows, 64 x 16 (eight waves) from 17
+// rows, and for M <= 16 one 16 x 16 block per workgroup with eight waves
+// streaming its weights.
 int fp8_packed_geometry(int M, int N)
 {
     const int nb = (N + 15) / 16;
     const int mt64 = (M + 63) / 64;
     if (M > 64 && mt64 * ((nb + 3) / 4) >= 256)
-        return 6;                                  // 64 x 64
-    if (M > 64 && mt64 * ((nb + 1) / 2) >= 256)
-        return 5;                                  // 64 x 32
-    if (M > 48)
-        return 4;                                  // 64 x 16
-    if (M > 32)
-        return 3;                                  // 48 x 16
+        return 3;                                  // 64 x 64
+    if (M > 128)
+        return 2;                                  // 64 x 32
     if (M > 16)
-        return 2;                                  // 32 x 16
-    return 1;                                      // 16 x 16
+        return 1;                                  // 64 x 16
+    return 0;                                      // 16 x 16
 }
 
 hipError_t launch_fp8_packed(const GemmArgs& a, hipStream_t stream)
 {
     switch (fp8_packed_geometry(a.M, a.N)) {
-    case 6: return launch_geometry<4, 4, 4, 2, 2, 1, 4>(a, stream);
-    case 5: return launch_geometry<4, 4, 2, 2, 1, 2, 4>(a, stream);
-    case 4: return launch_geometry<4, 4, 1, 1, 1, 4, 4>(a, stream);
-    case 3: return launch_geometry<4, 3, 1, 1, 1, 4, 4>(a, stream);
-    case 2: return launch_geometry<4, 2, 1, 1, 1, 4, 6>(a, stream);
-    default: return launch_geometry<4, 1, 1, 1, 1, 4, 8>(a, stream);
+    case 3: return launch_geometry<4, 4, 4, 2, 2, 2, 2>(a, stream);
+    case 2: return launch_geometry<4, 4, 2, 2, 1, 2, 4>(a, stream);
+    case 1: return launch_geometry<8, 4, 1, 1, 1, 4, 4>(a, stream);
+    default: return launch_geometry<8, 1, 1, 1, 1, 8, 4>(a, stream);
     }
 }
 

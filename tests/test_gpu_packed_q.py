@@ -167,3 +167,62 @@ def test_fp4_packed_c4_invariance(bg, c4p):
     rows = np.array([1, 300])
     C64, S = oracle.gemm_fp4w(np.ascontiguousarray(A[rows]), Bq, sB, N)
     check_parity(host_codes(ref[rows]), C64, S, 4096, "C4 packed sampled rows")
+
+
+# ------------------------------------------------------------------ K tails with poisoned pitch padding
+
+
+def test_fp8_k_tail_ignores_pitch_padding(bg):
+    """K = 384 leaves the last pipeline stage partly past K at every geometry.
+    The row pitches of A and sA are padded with NaN codes / NaN scales, which
+    must never reach the result (blocks past K contribute exact zeros)."""
+    for M, N, K in ((5, 272, 384), (70, 144, 640), (300, 2048, 384)):
+        qA, sA, qB, sB = fp8_case(M, N, K, 950 + M)
+        Ap = np.full((M, K + 128), 0x7F, np.uint8)          # e4m3fn NaN past K
+        Ap[:, :K] = qA
+        sAp = np.full((M, K // 128 + 3), np.nan, np.float32)
+        sAp[:, :K // 128] = sA
+        A = torch.from_numpy(Ap).cuda()[:, :K]
+        sAd = torch.from_numpy(sAp).cuda()[:, :K // 128]
+        B, sBd = dev_u8(qB, pad16(N)), dev_f32(sB)
+        C64, S = oracle.gemm_fp8bs(qA, sA, qB, sB)
+        got = host_codes(bg.gemm_fp8_blockscaled(A, sAd, B, sBd))
+        check_parity(got, C64, S, K, f"fp8 tail M{M} N{N} K{K}")
+        got_p = host_codes(bg.gemm_fp8_blockscaled_packed(A, sAd, bg.pack_b_fp8(B), sBd))
+        assert np.array_equal(got_p, got)
+
+
+def test_fp4_k_tail_ignores_pitch_padding(bg):
+    """K = 288 (not a multiple of either kernel's stage) with A's row pitch
+    padded with bf16 NaN."""
+    for M, N, K in ((3, 130, 288), (40, 1024, 160), (513, 256, 96)):
+        Ah = inputs.normal_bf16((M, K), 1.0, 960 + M)
+        Ap = np.full((M, K + 64), 0x7FC0, np.uint16)
+        Ap[:, :K] = Ah
+        A = torch.from_numpy(Ap.view(np.int16)).view(torch.bfloat16).cuda()[:, :K]
+        Bq, sB = inputs.quant_fp4_weights(inputs.normal_f32((K, N), 0.02, 961 + N))
+        Bd, sBd = dev_u8(Bq, pad16(N // 2)), dev_u8(sB, pad16(N))
+        C64, S = oracle.gemm_fp4w(Ah, Bq, sB, N)
+        got = host_codes(bg.gemm_fp4_w(A, Bd, sBd, N))
+        check_parity(got, C64, S, K, f"fp4 tail M{M} N{N} K{K}")
+        got_p = host_codes(bg.gemm_fp4_w_packed(A, bg.pack_b_fp4(Bd, sBd, N)))
+        assert np.array_equal(got_p, got)
+
+
+def test_bf16_k_tail_ignores_pitch_padding(bg):
+    # the same property for the three bf16 layouts (K = 200: a partial 32-step)
+    M, N, K = 19, 272, 200
+    Ah = inputs.normal_bf16((M, K), 1.0, 971)
+    Bh = inputs.normal_bf16((K, N), 0.02, 972)
+    Ap = np.full((M, K + 56), 0x7FC0, np.uint16)
+    Ap[:, :K] = Ah
+    Btp = np.full((N, K + 56), 0x7FC0, np.uint16)
+    Btp[:, :K] = Bh.T
+    A = torch.from_numpy(Ap.view(np.int16)).view(torch.bfloat16).cuda()[:, :K]
+    Bt = torch.from_numpy(Btp.view(np.int16)).view(torch.bfloat16).cuda()[:, :K]
+    B = dev_bf16(Bh)
+    C64, S = oracle.gemm_bf16(Ah, Bh)
+    got = host_codes(bg.gemm_bf16(A, B))
+    check_parity(got, C64, S, K, "bf16 tail")
+    assert np.array_equal(host_codes(bg.gemm_bf16_bt(A, Bt)), got)
+    assert np.array_equal(host_codes(bg.gemm_bf16_packed(A, bg.pack_b_bf16(B))), got)
