@@ -5,11 +5,13 @@
 
 Headline workload (one "step"): the bf16 projection GEMM, K = N = 8192,
 weights B ~ N(0, 0.02), activations A ~ N(0, 1), swept over
-M = 1, 2, 4, ..., 256 -- nine launches of bi_gemm_bf16, one per M.  Every
-launch reads a different copy of (A, B) from a rotation of more than 1 GiB,
-so B comes from HBM and not from the 256 MB Infinity Cache.  Inputs are
-resident in HBM before the timed region starts.  `value` is whole-job TFLOP/s
-over the timed steps (2MNK per launch).
+M = 1, 2, 4, ..., 256 -- nine launches of bi_gemm_bf16_packed, one per M, on
+weights packed once (outside the timed region) into the MFMA operand order;
+the packed path returns the same bits as bi_gemm_bf16 on the row-major
+weights.  Every launch reads a different copy of (A, B) from a rotation of
+more than 1 GiB, so B comes from HBM and not from the 256 MB Infinity Cache.
+Inputs are resident in HBM before the timed region starts.  `value` is
+whole-job TFLOP/s over the timed steps (2MNK per launch).
 
 The same JSON line carries, per M: launch time, TFLOP/s, algorithmic GB/s and
 the fractions of the HBM and MFMA roofs and of the attainable roof
@@ -285,15 +287,23 @@ def cpu_baseline(budget_s=12.0):
 
 # ------------------------------------------------------------------ traffic evidence
 
-def traffic_from_profiles(kernel_src: str):
+def kernel_sha256(paths) -> str:
+    """SHA-256 over the kernel's source files, in order."""
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def traffic_from_profiles(kernel_src):
     """Measured HBM bytes per launch of the headline sweep, from the committed
     rocprofv3 --pmc summary, if that summary was taken on the current kernel
     source; else None."""
-    p = os.path.join(ROOT, "profiles", "gemm_bf16_c2_traffic.json")
+    p = os.path.join(ROOT, "profiles", "gemm_bf16_packed_c2_traffic.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    h = kernel_sha256(kernel_src)
     if d.get("kernel_sha256") != h:
         return None
     return d.get("hbm_bytes_per_launch")
@@ -391,7 +401,7 @@ def main():
     dev = torch.cuda.get_device_properties(0)
     log(f"device: {dev.name}, CUs {dev.multi_processor_count}")
 
-    wl = C2(torch, bigemm, inputs)
+    wl = C2P(torch, bigemm, inputs)
     if args.pmc_probe:
         pmc_probe(torch, wl)
         return
@@ -419,7 +429,8 @@ def main():
 
     tflops = step_flops / (ms * 1e-3) / 1e12
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    kernel_src = os.path.join(ROOT, "invariant_gemm_amd", "csrc", "gemm_bf16.hip")
+    kernel_src = [os.path.join(ROOT, "invariant_gemm_amd", "csrc", f)
+                  for f in ("gemm_bf16_packed.hip", "common.h")]
     out = {
         "metric": "TFLOP/s and HBM GB/s vs roofline per M (1..512), bitwise-invariant rows",
         "value": round(tflops, 3),
@@ -434,36 +445,43 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": "bf16 projection GEMM C=A.B, K=N=8192, M sweep 1,2,4,...,256 "
-                               f"(one launch per M); B row-major, rotated over {wl.nbuf} HBM copies",
-                   "launches_per_step": len(SWEEP_C2), "K": K, "N": N, "M": SWEEP_C2},
+                               "(one launch per M); B packed once into MFMA operand order "
+                               f"({wl.pack_ms:.2f} ms per matrix, outside the timed region), "
+                               f"rotated over {wl.nbuf} HBM copies",
+                   "launches_per_step": len(SWEEP_C2), "K": K, "N": N, "M": SWEEP_C2,
+                   "entry_point": "bi_gemm_bf16_packed"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profiles(kernel_src),
-                     "kernel": "gemm_bf16_kernel (bi_gemm_bf16)",
+                     "kernel": "gemm_bf16_packed_kernel (bi_gemm_bf16_packed, all launch geometries)",
                      "algorithmic_bytes_per_launch": step_bytes / len(SWEEP_C2)},
     }
 
     if not args.quick:
         out["per_m"] = sweep(torch, wl, SWEEP_C2, bytes_bf16, MFMA_PEAK_TFLOPS["bf16"], args.rounds)
+        packed_us = {m: v["us"] for m, v in out["per_m"].items()}
+        del wl
+        c2 = C2(torch, bigemm, inputs)
+        out["bf16_rowmajor_K8192_N8192"] = sweep(torch, c2, SWEEP_C2, bytes_bf16,
+                                                 MFMA_PEAK_TFLOPS["bf16"], args.rounds)
+        # the gap against the non-invariant split-K variant of the same
+        # (row-major) kernel, and against the packed invariant path
         ws = torch.empty(256 * N, dtype=torch.float32, device="cuda")
         gap = {}
         for M in SWEEP_C2:
-            med, _ = time_launches(torch, lambda: wl.launch_splitk(M, ws), reps=wl.nbuf,
+            med, _ = time_launches(torch, lambda: c2.launch_splitk(M, ws), reps=c2.nbuf,
                                    rounds=max(3, args.rounds // 2))
             gap[str(M)] = {"splits": bigemm.splitk_choose(M, N, K), "us": round(med, 2),
-                           "invariant_over_splitk_time": round(out["per_m"][str(M)]["us"] / med, 3)}
+                           "invariant_over_splitk_time":
+                               round(out["bf16_rowmajor_K8192_N8192"][str(M)]["us"] / med, 3),
+                           "packed_invariant_over_splitk_time": round(packed_us[str(M)] / med, 3)}
         out["splitk_gap"] = gap
         del ws
-        del wl
+        del c2
         c2t = C2T(torch, bigemm, inputs)
         out["bf16_bt_K8192_N8192"] = sweep(torch, c2t, SWEEP_C2, bytes_bf16,
                                            MFMA_PEAK_TFLOPS["bf16"], args.rounds)
         del c2t
-        c2p = C2P(torch, bigemm, inputs)
-        out["bf16_packed_K8192_N8192"] = sweep(torch, c2p, SWEEP_C2, bytes_bf16,
-                                               MFMA_PEAK_TFLOPS["bf16"], args.rounds)
-        out["bf16_packed_K8192_N8192"]["pack_ms_once"] = round(c2p.pack_ms, 3)
-        del c2p
         c3 = C3(torch, bigemm, inputs)
         out["fp8_blockscaled_K7168_N2048"] = sweep(torch, c3, SWEEP_C3, bytes_fp8,
                                                    MFMA_PEAK_TFLOPS["fp8"], args.rounds)

@@ -49,6 +49,21 @@ __device__ __forceinline__ int xcd_remap(int b, int G)
     return (b % kXcds) * (G8 / kXcds) + b / kXcds;
 }
 
+// XOR swizzle of the 16-byte chunks of an LDS tile with CPR chunks per row
+// (CPR a power of two): chunk c of row r is stored at r*CPR + (c ^ swz(r)).
+// Sixteen consecutive rows read at one logical chunk then fall into sixteen
+// distinct 16-byte bank groups, so a 16-lane ds_read_b128 phase is free of
+// bank conflicts for any row pitch.
+template <int CPR>
+__device__ __forceinline__ int swz(int row)
+{
+    static_assert((CPR & (CPR - 1)) == 0 && CPR >= 2, "chunks per row: a power of two");
+    if constexpr (CPR >= 16)
+        return row & 15;
+    else
+        return (row / (16 / CPR)) & (CPR - 1);
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void* p)
 {
     return *reinterpret_cast<const u32x4*>(p);

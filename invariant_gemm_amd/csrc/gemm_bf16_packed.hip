@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
     for (int j = 0; j < A_LD; ++j) {
         const int c = j * NTHR + tid;
         const int row = c / CPR;
-        a_voff[j] = (uint32_t)(row * lda + (((c % CPR) ^ (row & 7)) * 8)) * 2u;
+        a_voff[j] = (uint32_t)(row * lda + (((c % CPR) ^ swz<CPR>(row)) * 8)) * 2u;
     }
 
     u32x4 areg[PF][A_LD];
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
 #pragma unroll
                 for (int j = 0; j < A_LD; ++j) {
                     const int c = j * NTHR + tid;
-                    const int kc = (c % CPR) ^ ((c / CPR) & 7);
+                    const int kc = (c % CPR) ^ swz<CPR>(c / CPR);
                     areg[p][j] = keep_first(areg[p][j], K - (kst + 8 * kc));
                 }
             }
@@ -144,18 +144,26 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
             for (int j = 0; j < A_LD; ++j)
                 *reinterpret_cast<u32x4*>(abuf + (j * NTHR + tid) * 16) = areg[p][j];
             __syncthreads();
+            // all A fragments of the stage first (their LDS latency overlaps),
+            // then the MFMA chain in K order
+            u32x4 afrag[KS_ST][RB];
 #pragma unroll
-            for (int ks = 0; ks < KS_ST; ++ks) {
+            for (int ks = 0; ks < KS_ST; ++ks)
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
                     const int row = 16 * r + li;
-                    const u32x4 afrag = *reinterpret_cast<const u32x4*>(
-                        abuf + (row * CPR + ((ks * 4 + lg) ^ (row & 7))) * 16);
+                    afrag[ks][r] = *reinterpret_cast<const u32x4*>(
+                        abuf + (row * CPR + ((ks * 4 + lg) ^ swz<CPR>(row))) * 16);
+                }
+            // keep the scheduler from sinking the reads back next to their uses
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS_ST; ++ks)
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
 #pragma unroll
                     for (int c = 0; c < CB; ++c)
-                        acc[r][c] = mfma_bf16(afrag, breg[p][ks][c], acc[r][c]);
-                }
-            }
+                        acc[r][c] = mfma_bf16(afrag[ks][r], breg[p][ks][c], acc[r][c]);
             issue(s + PF, areg[p], breg[p]);
         }
     }

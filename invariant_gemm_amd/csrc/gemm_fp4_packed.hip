@@ -79,7 +79,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     for (int j = 0; j < A_LD; ++j) {
         const int c = j * NTHR + tid;
         const int row = c / CPR;
-        a_voff[j] = (uint32_t)(row * lda + (((c % CPR) ^ (row & 7)) * 8)) * 2u;
+        a_voff[j] = (uint32_t)(row * lda + (((c % CPR) ^ swz<CPR>(row)) * 8)) * 2u;
     }
 
     u32x4 areg[PF][A_LD];
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
 #pragma unroll
                 for (int j = 0; j < A_LD; ++j) {
                     const int c = j * NTHR + tid;
-                    const int kc = (c % CPR) ^ ((c / CPR) & 7);
+                    const int kc = (c % CPR) ^ swz<CPR>(c / CPR);
                     if (kst + 8 * kc >= K)
                         areg[p][j] = u32x4{0u, 0u, 0u, 0u};
                 }
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                             for (int r = 0; r < RB; ++r) {
                                 const int row = 16 * r + li;
                                 const u32x4 afrag = *reinterpret_cast<const u32x4*>(
-                                    abuf + (row * CPR + ((ks * 4 + lg) ^ (row & 7))) * 16);
+                                    abuf + (row * CPR + ((ks * 4 + lg) ^ swz<CPR>(row))) * 16);
 #pragma unroll
                                 for (int c = 0; c < CB; ++c)
                                     P[tt][r][c] = mfma_bf16(afrag, bfrag[c], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                             for (int r = 0; r < RB; ++r) {
                                 const int row = 16 * r + li;
                                 const u32x4 afrag = *reinterpret_cast<const u32x4*>(
-                                    abuf + (row * CPR + ((ks * 4 + lg) ^ (row & 7))) * 16);
+                                    abuf + (row * CPR + ((ks * 4 + lg) ^ swz<CPR>(row))) * 16);
 #pragma unroll
                                 for (int c = 0; c < CB; ++c) {
                                     const f32x4 P = mfma_bf16(afrag, bfrag[c], f32x4{0.f, 0.f, 0.f, 0.f});

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     for (int j = 0; j < A_LD; ++j) {
         const int u = j * NTHR + tid;
         const int row = u / CPR;
-        a_voff[j] = (uint32_t)(row * lda + (((u % CPR) ^ (row & 7)) * 16));
+        a_voff[j] = (uint32_t)(row * lda + (((u % CPR) ^ swz<CPR>(row)) * 16));
     }
     // B chunk u = j*NTHR + tid: column block c = u / (KB_ST*128), byte
     // 16*(u % (KB_ST*128)) of that block's contiguous run; LDS byte
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
 #pragma unroll
                 for (int j = 0; j < A_LD; ++j) {
                     const int u = j * NTHR + tid;
-                    const int cg = (u % CPR) ^ ((u / CPR) & 7);   // chunk loaded into this register
+                    const int cg = (u % CPR) ^ swz<CPR>(u / CPR);   // chunk loaded into this register
                     if (cg >= 8 * qv)
                         areg[p][j] = u32x4{0u, 0u, 0u, 0u};
                 }
@@ -228,9 +228,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
                         const int row = 16 * (wr0 + r) + li;
                         const int c0 = q * 8 + 2 * lg;
                         const u32x4 a0 = *reinterpret_cast<const u32x4*>(
-                            buf + (row * CPR + (c0 ^ (row & 7))) * 16);
+                            buf + (row * CPR + (c0 ^ swz<CPR>(row))) * 16);
                         const u32x4 a1 = *reinterpret_cast<const u32x4*>(
-                            buf + (row * CPR + ((c0 + 1) ^ (row & 7))) * 16);
+                            buf + (row * CPR + ((c0 + 1) ^ swz<CPR>(row))) * 16);
                         const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
                                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
 #pragma unroll

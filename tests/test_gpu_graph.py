@@ -20,7 +20,11 @@ def bg():
     return bigemm
 
 
-def replay_matches_eager(calls, outs, extra=()):
+def replay_matches_eager(calls, outs, extra=(), inexact=()):
+    """`inexact`: indices of outputs whose bits legitimately vary from run to
+    run (the split-K comparator's atomics); those are compared within a
+    tolerance instead, which still catches a skipped zero-fill (NaN) or a
+    doubled accumulation."""
     for f in calls:
         f()
     torch.cuda.synchronize()
@@ -42,8 +46,11 @@ def replay_matches_eager(calls, outs, extra=()):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for o, e in zip(outs, ref):
-            assert torch.equal(o.view(torch.int16), e.view(torch.int16)), f"replay {r} differs"
+        for i, (o, e) in enumerate(zip(outs, ref)):
+            if i in inexact:
+                assert torch.allclose(o.float(), e.float(), rtol=2**-7, atol=1e-3), f"replay {r}: output {i}"
+            else:
+                assert torch.equal(o.view(torch.int16), e.view(torch.int16)), f"replay {r}: output {i} differs"
 
 
 def test_graph_replay_all_entry_points(bg):
@@ -71,7 +78,7 @@ def test_graph_replay_all_entry_points(bg):
         lambda: bg.gemm_fp4_w_packed(A, Bp4, out=outs[6]),
         lambda: bg.gemm_bf16_splitk(A, B, ws, 4, out=outs[7]),
     ]
-    replay_matches_eager(calls, outs, extra=[ws])
+    replay_matches_eager(calls, outs, extra=[ws], inexact=(7,))
     # identical bits across the three bf16 layouts and across packed/unpacked
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
