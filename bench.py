@@ -330,6 +330,61 @@ def pmc_probe(torch, wl):
     log("pmc probe done: copy", COPY_BYTES, "bytes x3, then 3 launches per M", SWEEP_C2)
 
 
+def pmc_summary(fetch_dir: str, write_dir: str):
+    """Turn the counter CSVs of the two `rocprofv3 --pmc` runs of
+    `--pmc-probe` (FETCH_SIZE, then WRITE_SIZE) into HBM bytes per launch of
+    the headline sweep.  Each counter is calibrated on the probe's copy of
+    COPY_BYTES (which must read and write exactly that many bytes)."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = int(r["Dispatch_Id"])
+                name, v = vals.get(key, (r["Kernel_Name"], 0.0))
+                vals[key] = (name, v + float(r["Counter_Value"]))
+        return [vals[k] for k in sorted(vals)]
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = per_dispatch(d, counter)
+        first = next(i for i, (n, _) in enumerate(rows) if "gemm_bf16_packed_kernel" in n)
+        # the probe's three calibration copies are the last copy dispatches
+        # before the first GEMM (set-up clones of A and B come earlier)
+        copies = [v for n, v in rows[:first] if "copy" in n.lower()][-3:]
+        gemms = [v for n, v in rows if "gemm_bf16_packed_kernel" in n]
+        if len(copies) != 3 or len(gemms) != 3 * len(SWEEP_C2):
+            raise SystemExit(f"{counter}: {len(copies)} copy and {len(gemms)} GEMM dispatches "
+                             f"(expected 3 and {3 * len(SWEEP_C2)})")
+        copy_kib = sorted(copies)[len(copies) // 2]
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        per_m = {}
+        for i, M in enumerate(SWEEP_C2):
+            v = sorted(gemms[3 * i:3 * i + 3])[1]
+            per_m[str(M)] = round(v * 1024.0 * factor)
+        out[counter] = {"copy_kib_per_dispatch": copy_kib, "scale_factor": round(factor, 4),
+                        "bytes_per_launch": per_m}
+    K, N = C2.K, C2.N
+    fetch = out["FETCH_SIZE"]["bytes_per_launch"]
+    write = out["WRITE_SIZE"]["bytes_per_launch"]
+    per_m = {m: {"hbm_bytes": fetch[m] + write[m], "fetch_bytes": fetch[m], "write_bytes": write[m],
+                 "algorithmic_bytes": bytes_bf16(int(m), N, K)} for m in fetch}
+    total = sum(v["hbm_bytes"] for v in per_m.values())
+    src = [os.path.join(ROOT, "invariant_gemm_amd", "csrc", f) for f in ("gemm_bf16_packed.hip", "common.h")]
+    return {"kernel": "gemm_bf16_packed_kernel (bi_gemm_bf16_packed)",
+            "kernel_sha256": kernel_sha256(src),
+            "workload": "bf16 K=N=8192, M = 1,2,4,...,256, B packed, rotated copies",
+            "hbm_bytes_per_launch": round(total / len(per_m)),
+            "algorithmic_bytes_per_launch": round(sum(v["algorithmic_bytes"] for v in per_m.values())
+                                                  / len(per_m)),
+            "per_m": per_m, "calibration": {k: {kk: vv for kk, vv in v.items() if kk != "bytes_per_launch"}
+                                            for k, v in out.items()}}
+
+
 # ------------------------------------------------------------------ legs
 
 def sweep(torch, wl, Ms, nbytes_fn, peak, rounds):
@@ -387,7 +442,13 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline only, no extra legs")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only run a known-size copy plus 3 launches per M (for rocprofv3 --pmc)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise the FETCH_SIZE and WRITE_SIZE runs of --pmc-probe (no GPU)")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        print(json.dumps(pmc_summary(*args.pmc_summary), indent=1))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the batch-invariant GEMM is timed on a single "
