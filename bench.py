@@ -260,6 +260,45 @@ class C4P(C4):
         self.bg.gemm_fp4_w_packed(self.A[j][:M], self.Bp[j], out=self.C[:M])
 
 
+class MoE:
+    """Grouped (mixture-of-experts) bf16 GEMM: E = 8 experts, K = 7168,
+    N = 2048, T tokens routed top-1 uniformly (seeded), rows grouped by
+    expert; packed expert weights rotated over HBM copies."""
+    E, K, N = 8, 7168, 2048
+    SWEEP = [1, 8, 64, 512]
+
+    def __init__(self, torch, bg, inputs):
+        self.torch, self.bg = torch, bg
+        A = inputs.normal_bf16((max(self.SWEEP), self.K), 1.0, 601)
+        self.A = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).cuda()
+        Bs = [torch.from_numpy(inputs.normal_bf16((self.K, self.N), 0.02, 602 + e).view(np.int16))
+              .view(torch.bfloat16).cuda() for e in range(self.E)]
+        one = bg.pack_b_bf16_grouped(Bs)
+        del Bs
+        self.nbuf = rotation(one.data.numel())
+        self.Bp = [one] + [bg.PackedWeights(one.dtype, one.K, one.N, one.data.clone())
+                           for _ in range(self.nbuf - 1)]
+        for b in self.Bp:
+            b.groups = self.E
+        self.routes = {}
+        for T in self.SWEEP:
+            expert = inputs.route_tokens(T, self.E, 603 + T, 0.0)
+            order, offsets = inputs.group_by_expert(expert, self.E)
+            self.routes[T] = (self.A[:T].index_select(0, torch.as_tensor(order, device="cuda")),
+                              torch.as_tensor(offsets, device="cuda"), int(np.count_nonzero(np.diff(offsets))))
+        self.C = torch.empty((max(self.SWEEP), self.N), dtype=torch.bfloat16, device="cuda")
+        self.i = 0
+
+    def launch(self, T):
+        j = self.i % self.nbuf
+        self.i += 1
+        A, off, _ = self.routes[T]
+        self.bg.gemm_bf16_grouped_packed(A, off, self.Bp[j], out=self.C[:T])
+
+    def nbytes(self, T, N, K):
+        return self.routes[T][2] * K * N * 2 + 2 * T * K + 2 * T * N
+
+
 # ------------------------------------------------------------------ cpu baseline
 
 def cpu_baseline(budget_s=12.0):
@@ -561,6 +600,10 @@ def main():
                                                            MFMA_PEAK_TFLOPS["bf16"], args.rounds)
         out["fp4_weight_only_packed_K4096_N14336"]["pack_ms_once"] = round(c4p.pack_ms, 3)
         del c4p
+        moe = MoE(torch, bigemm, inputs)
+        out["moe_grouped_bf16_E8_K7168_N2048"] = sweep(torch, moe, MoE.SWEEP, moe.nbytes,
+                                                       MFMA_PEAK_TFLOPS["bf16"], args.rounds)
+        del moe
         out["replay_bf16_K8192_N8192"] = replay(torch, bigemm, inputs)
 
     if not args.no_cpu_baseline:

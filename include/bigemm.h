@@ -149,6 +149,30 @@ bi_status bi_gemm_bf16_packed(int64_t M, int64_t N, int64_t K,
                               uint16_t* C, int64_t ldc, void* stream);
 
 /*
+ * Grouped GEMM for mixture-of-experts layers: rows of A are grouped by
+ * expert, and group g is multiplied by its own weight matrix B_g.
+ *   offsets : device int32 [G + 1], offsets[0] = 0 <= offsets[1] <= ... <=
+ *             offsets[G] = M; rows [offsets[g], offsets[g+1]) of A and C
+ *             belong to group g (a group may be empty)
+ *   A       : bf16 [M,K], lda >= K, lda % 8 == 0
+ *   Bp      : G packed bf16 matrices [K,N] (bi_pack_b_bf16 layout), each
+ *             bi_packed_b_bytes(BI_BF16, N, K) bytes, back to back
+ *   C       : bf16 [M,N], ldc >= N
+ * Each row's arithmetic is exactly that of bi_gemm_bf16 with its group's
+ * weights, so a token's output is bit-identical whatever the routing of the
+ * other tokens -- how many share its expert, or the other experts' loads.
+ * The offsets are read on the device (no host synchronisation); they are
+ * clamped into [0, M] and made non-decreasing, so a malformed table cannot
+ * cause an out-of-bounds access, but rows it leaves uncovered are not
+ * written.  One kernel on `stream`.
+ */
+bi_status bi_gemm_bf16_grouped_packed(int64_t G, const int32_t* offsets,
+                                      int64_t M, int64_t N, int64_t K,
+                                      const uint16_t* A, int64_t lda,
+                                      const void* Bp, size_t bp_bytes,
+                                      uint16_t* C, int64_t ldc, void* stream);
+
+/*
  * fp8 e4m3fn (OCP, "fn": no infinities) with fp32 block scales -> bf16.
  * The fused dequantisation of section 3.2 of the lshu.cn article: the scales
  * are applied inside the K loop, never in a separate pass.

@@ -51,6 +51,9 @@ lib.bi_gemm_fp8_blockscaled.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, 
                                         _vp, _i64, _vp]
 lib.bi_gemm_fp4_w.restype = _i32
 lib.bi_gemm_fp4_w.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+lib.bi_gemm_bf16_grouped_packed.restype = _i32
+lib.bi_gemm_bf16_grouped_packed.argtypes = [_i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _sz, _vp,
+                                            _i64, _vp]
 lib.bi_pack_b_fp8.restype = _i32
 lib.bi_pack_b_fp8.argtypes = [_i64, _i64, _vp, _i64, _vp, _sz, _vp]
 lib.bi_gemm_fp8_blockscaled_packed.restype = _i32
@@ -184,6 +187,40 @@ def gemm_bf16_packed(A: torch.Tensor, Bp: PackedWeights, out: torch.Tensor | Non
     _check(lib.bi_gemm_bf16_packed(M, Bp.N, K, A.data_ptr(), _ld(A), Bp.data.data_ptr(),
                                    Bp.data.numel(), C.data_ptr(), _ld(C), _stream()),
            "bi_gemm_bf16_packed")
+    return C
+
+
+def pack_b_bf16_grouped(Bs) -> PackedWeights:
+    """Pack G row-major bf16 matrices [K,N] (one per group) back to back."""
+    Bs = [_mat(B, _BF16, "B") for B in Bs]
+    K, N = Bs[0].shape
+    if any(tuple(B.shape) != (K, N) for B in Bs):
+        raise ValueError("all groups' weight matrices must have the same shape")
+    one = packed_b_bytes(BI_BF16, N, K)
+    buf = torch.empty(max(one * len(Bs), 16), dtype=torch.uint8, device=Bs[0].device)
+    for g, B in enumerate(Bs):
+        _check(lib.bi_pack_b_bf16(N, K, B.data_ptr(), _ld(B), buf.data_ptr() + g * one, one, _stream()),
+               "bi_pack_b_bf16")
+    pw = PackedWeights(BI_BF16, K, N, buf)
+    pw.groups = len(Bs)
+    return pw
+
+
+def gemm_bf16_grouped_packed(A: torch.Tensor, offsets: torch.Tensor, Bp: PackedWeights,
+                             out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rows [offsets[g], offsets[g+1]) of A times group g's packed weights."""
+    A = _mat(A, _BF16, "A")
+    M, K = A.shape
+    if Bp.dtype != BI_BF16 or Bp.K != K or not hasattr(Bp, "groups"):
+        raise ValueError("grouped packed weights do not match A")
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1 \
+            or offsets.numel() != Bp.groups + 1 or (offsets.numel() > 1 and offsets.stride(0) != 1):
+        raise ValueError("offsets: a contiguous int32 device tensor of G + 1 entries")
+    C = _out(M, Bp.N, A.device, out)
+    _check(lib.bi_gemm_bf16_grouped_packed(Bp.groups, offsets.data_ptr(), M, Bp.N, K, A.data_ptr(),
+                                           _ld(A), Bp.data.data_ptr(), Bp.data.numel(),
+                                           C.data_ptr(), _ld(C), _stream()),
+           "bi_gemm_bf16_grouped_packed")
     return C
 
 

@@ -269,6 +269,38 @@ bi_status bi_gemm_bf16_packed(int64_t M, int64_t N, int64_t K, const uint16_t* A
     return launched(launch_bf16_packed(a, (hipStream_t)stream));
 }
 
+bi_status bi_gemm_bf16_grouped_packed(int64_t G, const int32_t* offsets, int64_t M, int64_t N,
+                                      int64_t K, const uint16_t* A, int64_t lda, const void* Bp,
+                                      size_t bp_bytes, uint16_t* C, int64_t ldc, void* stream)
+{
+    bi_status st = check_dims(M, N, K);
+    if (st != BI_OK)
+        return st;
+    if (G < 0)
+        return BI_ERR_SHAPE;
+    if (G > 65536)
+        return BI_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0)
+        return BI_OK;
+    if (G == 0)
+        return BI_ERR_SHAPE;                          // rows but no group to own them
+    if (!offsets || !C || (K > 0 && (!A || !Bp)))
+        return BI_ERR_NULL;
+    if ((K > 0 && lda < K) || ldc < N)
+        return BI_ERR_STRIDE;
+    if (((uintptr_t)C & 1u) || ((uintptr_t)offsets & 3u) ||
+        (K > 0 && (!aligned16(A) || lda % 8 || !aligned16(Bp))))
+        return BI_ERR_ALIGN;
+    const size_t one = bi_packed_b_bytes(BI_BF16, N, K);
+    if (bp_bytes / (size_t)G < one)
+        return BI_ERR_WORKSPACE;
+    if (((M + 15) / 16 + G) * ((N + 31) / 32) > 0x7FFFFFFF)
+        return BI_ERR_UNSUPPORTED;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, Bp, 0, nullptr, 0, C, ldc};
+    GroupArgs g{offsets, (int)G, (int64_t)one};
+    return launched(launch_bf16_grouped_packed(a, g, (hipStream_t)stream));
+}
+
 bi_status bi_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
                                   const float* sA, int64_t ldsa, const uint8_t* B, int64_t ldb,
                                   const float* sB, int64_t ldsb, uint16_t* C, int64_t ldc,

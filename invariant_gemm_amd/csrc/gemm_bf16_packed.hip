@@ -46,12 +46,20 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
 
 // WAVES waves; wave w owns column blocks nb0 + w*CB .. +CB-1; the workgroup
 // owns RB row blocks (BM = 16*RB rows).  Stage = KS_ST K steps.
-template <int WAVES, int CB, int RB, int KS_ST, int PF>
+//
+// GROUPED: rows [offsets[g], offsets[g+1]) of A and C belong to group g and
+// use the g-th packed matrix (b_stride bytes apart).  Row slot mt enumerates
+// the groups' row tiles in order; a workgroup finds its group by walking the
+// offsets, and slots past the last tile exit at once.  A row's arithmetic is
+// the same as in the ungrouped kernel, so it does not depend on how many rows
+// the other groups -- or its own group -- hold.
+template <int WAVES, int CB, int RB, int KS_ST, int PF, bool GROUPED>
 __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
     int M, int N, int K,
     const uint16_t* __restrict__ A, int64_t lda,
     const uint8_t* __restrict__ Bp,
-    uint16_t* __restrict__ C, int64_t ldc, int m_tiles)
+    uint16_t* __restrict__ C, int64_t ldc, int m_tiles,
+    const int32_t* __restrict__ offsets, int n_groups, int64_t b_stride)
 {
     constexpr int NTHR = 64 * WAVES;
     constexpr int BM = 16 * RB;
@@ -69,14 +77,34 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
     const int tile = xcd_remap(blockIdx.x, gridDim.x);
     const int nt = tile / m_tiles;
     const int mt = tile - nt * m_tiles;
-    const int m0 = mt * BM;
+    int m0 = mt * BM;
+    int row_end = M;                                  // rows [m0, row_end) are this tile's
+    if constexpr (GROUPED) {
+        // offsets are clamped into [0, M] and made monotone here, so no
+        // table can send a load or store outside A or C
+        int first = 0, g = 0, lo = 0, hi = 0;
+        for (; g < n_groups; ++g) {
+            lo = min(max(offsets[g], lo), M);
+            hi = min(max(offsets[g + 1], lo), M);
+            const int tiles_g = (hi - lo + BM - 1) / BM;
+            if (mt < first + tiles_g)
+                break;
+            first += tiles_g;
+            lo = hi;
+        }
+        if (g == n_groups)
+            return;                                   // an unused slot (uniform per workgroup)
+        m0 = lo + (mt - first) * BM;
+        row_end = hi;
+        Bp += g * b_stride;
+    }
     const int NB = (N + 15) >> 4;
     const int KS = (K + KSTEP - 1) / KSTEP;
     const int nb0 = nt * (WAVES * CB) + wave * CB;    // first column block of this wave
 
     const int nst = (K + BKS - 1) / BKS;
     const int kpad = (K + 7) & ~7;
-    const int rows_valid = M - m0 < BM ? M - m0 : BM;
+    const int rows_valid = row_end - m0 < BM ? row_end - m0 : BM;
     const int li = lane & 15;
     const int lg = lane >> 4;
 
@@ -176,7 +204,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = m0 + 16 * r + 4 * lg + j;
-                if (row < M && col < N)
+                if (row < row_end && col < N)
                     C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[r][c][j]);
             }
         }
@@ -209,13 +237,22 @@ __global__ void pack_b_bf16_kernel(int N, int K, const uint16_t* __restrict__ B,
 }
 
 template <int WAVES, int CB, int RB, int KS_ST, int PF>
-hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
+hipError_t launch_geometry(const GemmArgs& a, const GroupArgs* grp, hipStream_t stream)
 {
     const int n_tiles = ((a.N + 15) / 16 + WAVES * CB - 1) / (WAVES * CB);
-    const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-    gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF><<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0,
-                                                       stream>>>(
-        a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
+    const dim3 block(64 * WAVES);
+    if (grp) {
+        // row slots: every group adds at most one partial tile
+        const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB) + grp->n_groups;
+        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, true><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
+            a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles,
+            grp->offsets, grp->n_groups, grp->b_stride);
+    } else {
+        const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
+        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, false><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
+            a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles,
+            nullptr, 0, 0);
+    }
     return hipGetLastError();
 }
 
@@ -244,15 +281,32 @@ int packed_geometry(int M, int N)
     return 0;                                               // streaming, BM 16
 }
 
+namespace {
+
+hipError_t launch_packed(const GemmArgs& a, const GroupArgs* grp, int geometry, hipStream_t stream)
+{
+    switch (geometry) {
+    case 4: return launch_geometry<4, 2, 4, 4, 4>(a, grp, stream);
+    case 3: return launch_geometry<4, 1, 4, 4, 4>(a, grp, stream);
+    case 2: return launch_geometry<2, 1, 4, 2, 8>(a, grp, stream);
+    case 1: return launch_geometry<2, 1, 2, 4, 6>(a, grp, stream);
+    default: return launch_geometry<2, 1, 1, 8, 4>(a, grp, stream);
+    }
+}
+
+}  // namespace
+
 hipError_t launch_bf16_packed(const GemmArgs& a, hipStream_t stream)
 {
-    switch (packed_geometry(a.M, a.N)) {
-    case 4: return launch_geometry<4, 2, 4, 4, 4>(a, stream);
-    case 3: return launch_geometry<4, 1, 4, 4, 4>(a, stream);
-    case 2: return launch_geometry<2, 1, 4, 2, 8>(a, stream);
-    case 1: return launch_geometry<2, 1, 2, 4, 6>(a, stream);
-    default: return launch_geometry<2, 1, 1, 8, 4>(a, stream);
-    }
+    return launch_packed(a, nullptr, packed_geometry(a.M, a.N), stream);
+}
+
+// Grouped launch: the geometry follows the mean rows per group (any choice
+// gives the same bits).
+hipError_t launch_bf16_grouped_packed(const GemmArgs& a, const GroupArgs& g, hipStream_t stream)
+{
+    const int mean = (a.M + g.n_groups - 1) / g.n_groups;
+    return launch_packed(a, &g, packed_geometry(mean > 0 ? mean : 1, a.N), stream);
 }
 
 hipError_t launch_pack_b_bf16(int N, int K, const uint16_t* B, int64_t ldb, uint8_t* Bp,

@@ -25,12 +25,20 @@ struct GemmArgs {
     uint16_t* C;    int64_t ldc;
 };
 
+// Groups of rows for the grouped (mixture-of-experts) GEMM.
+struct GroupArgs {
+    const int32_t* offsets;  // device, n_groups + 1 row offsets
+    int n_groups;
+    int64_t b_stride;        // bytes between consecutive groups' packed weights
+};
+
 hipError_t launch_bf16(const GemmArgs& a, const Schedule& s, hipStream_t stream);
 hipError_t launch_bf16_bt(const GemmArgs& a, const Schedule& s, hipStream_t stream);
 hipError_t launch_bf16_packed(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_pack_b_bf16(int N, int K, const uint16_t* B, int64_t ldb, uint8_t* Bp,
                               hipStream_t stream);
 int packed_geometry(int M, int N);
+hipError_t launch_bf16_grouped_packed(const GemmArgs& a, const GroupArgs& g, hipStream_t stream);
 hipError_t launch_fp8bs(const GemmArgs& a, const Schedule& s, hipStream_t stream);
 hipError_t launch_fp4w(const GemmArgs& a, const Schedule& s, hipStream_t stream);
 hipError_t launch_fp8_packed(const GemmArgs& a, hipStream_t stream);

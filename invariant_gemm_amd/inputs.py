@@ -153,3 +153,21 @@ def replay_batches(pool: int, steps: int, max_batch: int, seed: int):
         b = int(g.integers(1, max_batch + 1))
         out.append(g.choice(pool, size=b, replace=False))
     return out
+
+
+def route_tokens(n_tokens: int, n_experts: int, seed: int, skew: float = 0.0) -> np.ndarray:
+    """Expert id per token for a synthetic top-1 routing: probabilities
+    proportional to (rank + 1)^-skew over a seeded random expert order
+    (skew 0 = uniform; large skew piles most tokens onto a few experts)."""
+    g = rng(seed)
+    w = (np.arange(n_experts) + 1.0) ** -skew
+    p = w[g.permutation(n_experts)]
+    return g.choice(n_experts, size=n_tokens, p=p / p.sum())
+
+
+def group_by_expert(expert: np.ndarray, n_experts: int):
+    """Stable order of the tokens by expert and the row offsets per expert."""
+    order = np.argsort(expert, kind="stable")
+    counts = np.bincount(expert, minlength=n_experts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return order, offsets

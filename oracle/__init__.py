@@ -138,6 +138,25 @@ def gemm_bf16(A: np.ndarray, B: np.ndarray):
     return C, S
 
 
+def gemm_bf16_grouped(A: np.ndarray, offsets, Bs):
+    """Grouped (mixture-of-experts) GEMM by its definition: rows
+    [offsets[g], offsets[g+1]) of A times Bs[g], one plain GEMM per group.
+    Returns (C, S) fp64 [M,N]."""
+    A = _rows(A, np.uint16, "A")
+    offsets = [int(o) for o in offsets]
+    if len(offsets) != len(Bs) + 1 or offsets[0] != 0 or offsets[-1] != A.shape[0] \
+            or any(b < a for a, b in zip(offsets, offsets[1:])):
+        raise ValueError("offsets must run from 0 to M, non-decreasing, one more than groups")
+    N = Bs[0].shape[1]
+    C = np.zeros((A.shape[0], N), np.float64)
+    S = np.zeros((A.shape[0], N), np.float64)
+    for g, B in enumerate(Bs):
+        lo, hi = offsets[g], offsets[g + 1]
+        if hi > lo:
+            C[lo:hi], S[lo:hi] = gemm_bf16(np.ascontiguousarray(A[lo:hi]), B)
+    return C, S
+
+
 def gemm_fp8bs(qA: np.ndarray, sA: np.ndarray, qB: np.ndarray, sB: np.ndarray):
     """qA uint8 e4m3fn [M,K], sA fp32 [M,K/128], qB uint8 e4m3fn [K,N],
     sB fp32 [K/128, ceil(N/128)] -> (C, S) fp64 [M,N]."""

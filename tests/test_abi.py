@@ -203,3 +203,17 @@ def test_packed_validation():
     assert lib.bi_pack_b_fp4(64, 64, P, 16, P, 64, P, 1 << 20, None) == STRIDE
     assert lib.bi_pack_b_fp4(64, 64, P, 32, None, 64, P, 1 << 20, None) == NULL
     assert lib.bi_pack_b_fp4(64, 48, P, 32, P, 64, P, 1 << 20, None) == SHAPE
+
+
+def test_grouped_validation():
+    need = bigemm.packed_b_bytes(bigemm.BI_BF16, 64, 64)
+    f = lambda G, M, N=64, K=64, off=P, A=P, Bp=P, nb=None, C=P: lib.bi_gemm_bf16_grouped_packed(
+        G, off, M, N, K, A, K, Bp, need * G if nb is None else nb, C, N, None)
+    assert f(-1, 8) == SHAPE
+    assert f(0, 8) == SHAPE                    # rows but no group
+    assert f(0, 0) == OK
+    assert f(3, 0, off=None, A=None, Bp=None, C=None) == OK
+    assert f(3, 8, off=None) == NULL
+    assert f(3, 8, nb=need * 3 - 1) == WS
+    assert f(3, 8, off=P + 2) == ALIGN
+    assert f(1 << 20, 8) == UNSUP

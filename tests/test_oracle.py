@@ -327,3 +327,26 @@ def test_fp4_exact_vs_fraction():
                 b = Fraction(E2M1[int(codes[k, j])]) * Fraction(float(_e4m3_f64(sB[k // 32:k // 32 + 1, j:j + 1])[0, 0]))
                 exp += _frac_bf16(A[i, k]) * b
             assert abs(Fraction(C[i, j]) - exp) <= Fraction(K * 2.0**-52) * Fraction(S[i, j]), (i, j)
+
+
+def test_grouped_exact_vs_fraction():
+    # grouped GEMM = one GEMM per group of rows, including an empty group
+    from fractions import Fraction
+    g = np.random.default_rng(11)
+    K, N = 6, 3
+    A = inputs.f32_to_bf16_codes(g.integers(-4, 5, size=(7, K)).astype(np.float32) / 4)
+    Bs = [inputs.f32_to_bf16_codes(g.integers(-4, 5, size=(K, N)).astype(np.float32) / 8)
+          for _ in range(3)]
+    offsets = [0, 2, 2, 7]
+    C, S = oracle.gemm_bf16_grouped(A, offsets, Bs)
+    Af = inputs.bf16_codes_to_f32(A)
+    for gi, B in enumerate(Bs):
+        Bf = inputs.bf16_codes_to_f32(B)
+        for m in range(offsets[gi], offsets[gi + 1]):
+            for n in range(N):
+                exact = sum(Fraction(float(Af[m, k])) * Fraction(float(Bf[k, n])) for k in range(K))
+                assert C[m, n] == float(exact)
+                assert S[m, n] == float(sum(abs(Fraction(float(Af[m, k])) * Fraction(float(Bf[k, n])))
+                                            for k in range(K)))
+    with pytest.raises(ValueError):
+        oracle.gemm_bf16_grouped(A, [0, 3, 2, 7], Bs)
