@@ -171,3 +171,21 @@ def group_by_expert(expert: np.ndarray, n_experts: int):
     counts = np.bincount(expert, minlength=n_experts)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     return order, offsets
+
+
+def quant_mxfp4_weights(w: np.ndarray, block_k: int = 32):
+    """Weights [K,N] -> (Bq uint8 [K, N/2] packed e2m1, sE uint8 E8M0 [K/block_k, N]),
+    the OCP MX scheme: per block of 32 along K and column, the shared scale is
+    2^(floor(log2(amax)) - 2) (2 = the largest e2m1 exponent), clamped to the
+    E8M0 range (1 for an all-zero block); codes are RNE e2m1 of w / scale,
+    saturating at +-6."""
+    K, N = w.shape
+    wb = w.reshape(K // block_k, block_k, N).astype(np.float32)
+    amax = np.abs(wb).max(axis=1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0)
+    e = np.clip(e, -127, 127).astype(np.int32)
+    scale = np.ldexp(np.float32(1.0), e).astype(np.float32)
+    codes = _e2m1_codes((wb / scale[:, None, :]).reshape(K, N))
+    Bq = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return Bq, (e + 127).astype(np.uint8)

@@ -71,6 +71,10 @@ def _load():
     lib.ora_gemm_fp8bs.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, i64]
     lib.ora_gemm_fp4w.restype = None
     lib.ora_gemm_fp4w.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, vp, i64]
+    lib.ora_dec_e8m0.restype = ctypes.c_double
+    lib.ora_dec_e8m0.argtypes = [ctypes.c_uint8]
+    lib.ora_gemm_w4a8.restype = None
+    lib.ora_gemm_w4a8.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, i64]
     _lib = lib
     return lib
 
@@ -103,6 +107,10 @@ def dec_e4m3fn(code: int) -> float:
 
 def dec_e2m1(code: int) -> float:
     return _load().ora_dec_e2m1(int(code))
+
+
+def dec_e8m0(code: int) -> float:
+    return _load().ora_dec_e8m0(int(code))
 
 
 def rne_bf16(x: float) -> int:
@@ -196,4 +204,28 @@ def gemm_fp4w(A: np.ndarray, Bq: np.ndarray, sB: np.ndarray, N: int):
     if M and N:
         _load().ora_gemm_fp4w(M, N, K, _p(A), _ld(A), _p(Bq), _ld(Bq),
                               _p(sB), _ld(sB), _p(C), _p(S), N)
+    return C, S
+
+
+def gemm_w4a8(qA: np.ndarray, sA: np.ndarray, Bq: np.ndarray, sE: np.ndarray, N: int):
+    """fp8 activations x OCP MXFP4 weights.  qA uint8 e4m3fn [M,K], sA fp32
+    [M,K/128] (one scale per 1x128 block), Bq uint8 packed e2m1 [K, N/2],
+    sE uint8 E8M0 [K/32, N] (one power-of-two scale per 32 K per column)
+    -> (C, S) fp64 [M,N]."""
+    qA = _rows(qA, np.uint8, "qA")
+    sA = _rows(sA, np.float32, "sA")
+    Bq = _rows(Bq, np.uint8, "Bq")
+    sE = _rows(sE, np.uint8, "sE")
+    M, K = qA.shape
+    if Bq.shape[0] != K or Bq.shape[1] * 2 < N or K % 128:
+        raise ValueError("bad Bq / K")
+    if sA.shape[0] < M or sA.shape[1] < K // 128:
+        raise ValueError("sA too small")
+    if sE.shape[0] < K // 32 or sE.shape[1] < N:
+        raise ValueError("sE too small")
+    C = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64)
+    if M and N:
+        _load().ora_gemm_w4a8(M, N, K, _p(qA), _ld(qA), _p(sA), _ld(sA), _p(Bq), _ld(Bq),
+                              _p(sE), _ld(sE), _p(C), _p(S), N)
     return C, S

@@ -191,6 +191,49 @@ void ora_gemm_fp8bs(int64_t M, int64_t N, int64_t K,
     }
 }
 
+/* E8M0 (OCP MX shared scale): 2^(e - 127); e = 255 is NaN. */
+double ora_dec_e8m0(uint8_t e)
+{
+    if (e == 255)
+        return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+/* W4A8: a = dec_e4m3fn(qA[m,k]) * sA[m, k/128];
+ *       b = dec_e2m1(code(k,n)) * dec_e8m0(sE[k/32, n])   (OCP MXFP4 weights). */
+void ora_gemm_w4a8(int64_t M, int64_t N, int64_t K,
+                   const uint8_t* qA, int64_t lda, const float* sA, int64_t ldsa,
+                   const uint8_t* Bq, int64_t ldbq, const uint8_t* sE, int64_t ldse,
+                   double* C, double* S, int64_t ldc)
+{
+    int64_t nchunks = (N + ORA_NCHUNK - 1) / ORA_NCHUNK;
+    int64_t ntask = M * nchunks;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < ntask; ++t) {
+        int64_t m = t / nchunks;
+        int64_t n0 = (t % nchunks) * ORA_NCHUNK;
+        int64_t n1 = n0 + ORA_NCHUNK < N ? n0 + ORA_NCHUNK : N;
+        double* c = C + m * ldc;
+        double* s = S + m * ldc;
+        for (int64_t n = n0; n < n1; ++n) {
+            c[n] = 0.0;
+            s[n] = 0.0;
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            double a = ora_dec_e4m3fn(qA[m * lda + k]) * (double)sA[m * ldsa + k / 128];
+            const uint8_t* brow = Bq + k * ldbq;
+            const uint8_t* srow = sE + (k / 32) * ldse;
+            for (int64_t n = n0; n < n1; ++n) {
+                uint8_t code = (uint8_t)((brow[n / 2] >> (4 * (n & 1))) & 15);
+                double b = ora_dec_e2m1(code) * ora_dec_e8m0(srow[n]);
+                double p = a * b;
+                c[n] += p;
+                s[n] += fabs(p);
+            }
+        }
+    }
+}
+
 /* fp4 weight-only: a = dec_bf16(A[m,k]); b = dec_e2m1(code(k,n)) * dec_e4m3fn(sB[k/32, n]).
  * code(k,n) is the low nibble of byte Bq[k, n/2] for even n, the high nibble for odd n. */
 void ora_gemm_fp4w(int64_t M, int64_t N, int64_t K,

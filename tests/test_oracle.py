@@ -350,3 +350,64 @@ def test_grouped_exact_vs_fraction():
                                             for k in range(K)))
     with pytest.raises(ValueError):
         oracle.gemm_bf16_grouped(A, [0, 3, 2, 7], Bs)
+
+
+# ------------------------------------------------------------------ W4A8 (fp8 x OCP MXFP4)
+
+
+def test_e8m0_exhaustive_vs_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    got = np.array([oracle.dec_e8m0(c) for c in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+
+
+def test_w4a8_exact_vs_fraction():
+    g = np.random.default_rng(21)
+    M, N, K = 3, 6, 128
+    qA = g.integers(0, 256, size=(M, K)).astype(np.uint8)
+    qA[(qA & 0x7F) == 0x7F] = 0x38                      # no NaN codes
+    sA = np.ldexp(1.0, g.integers(-3, 4, size=(M, 1))).astype(np.float32)
+    codes = g.integers(0, 16, size=(K, N)).astype(np.uint8)
+    Bq = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    sE = g.integers(120, 135, size=(K // 32, N)).astype(np.uint8)
+    C, S = oracle.gemm_w4a8(qA, sA, Bq, sE, N)
+    e4 = torch.from_numpy(qA).view(torch.float8_e4m3fn).double().numpy()
+    for m in range(M):
+        for n in range(N):
+            exact = Fraction(0)
+            total = Fraction(0)
+            for k in range(K):
+                a = Fraction(float(e4[m, k])) * Fraction(float(sA[m, 0]))
+                b = Fraction(E2M1[int(codes[k, n])]) * Fraction(2) ** (int(sE[k // 32, n]) - 127)
+                exact += a * b
+                total += abs(a * b)
+            assert C[m, n] == float(exact) and S[m, n] == float(total)
+
+
+def test_w4a8_vs_dequantised_numpy():
+    M, N, K = 5, 34, 256
+    qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((M, K), 1.0, 31))
+    Bq, sE = inputs.quant_mxfp4_weights(inputs.normal_f32((K, N), 0.02, 32))
+    C, S = oracle.gemm_w4a8(qA, sA, Bq, sE, N)
+    a = torch.from_numpy(qA).view(torch.float8_e4m3fn).double().numpy() * np.repeat(sA, 128, axis=1)
+    codes = inputs.unpack_fp4(Bq)
+    e2m1 = np.array([E2M1[c] for c in range(16)])
+    b = e2m1[codes] * np.repeat(torch.from_numpy(sE).view(torch.float8_e8m0fnu).double().numpy(), 32, axis=0)
+    ref = a @ b
+    assert np.all(np.abs(C - ref) <= 1e-12 * (np.abs(a) @ np.abs(b)) + 1e-300)
+    assert np.allclose(S, np.abs(a) @ np.abs(b), rtol=1e-12, atol=0)
+
+
+def test_w4a8_scale_block_indexing():
+    # one weight block carries a huge scale: it must show up exactly in
+    # columns n and rows k of that block only
+    M, N, K = 2, 4, 256
+    qA = np.full((M, K), 0x38, np.uint8)                  # all 1.0
+    sA = np.ones((M, K // 128), np.float32)
+    Bq = np.full((K, N // 2), 0x22, np.uint8)             # every weight code 2 (= 1.0)
+    sE = np.full((K // 32, N), 127, np.uint8)
+    sE[5, 3] = 137                                        # block k in [160, 192), column 3: x 2^10
+    C, _ = oracle.gemm_w4a8(qA, sA, Bq, sE, N)
+    assert np.array_equal(C[:, :3], np.full((M, 3), 256.0))
+    assert np.array_equal(C[:, 3], np.full(M, 224.0 + 32 * 1024.0))
