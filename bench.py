@@ -260,6 +260,35 @@ class C4P(C4):
         self.bg.gemm_fp4_w_packed(self.A[j][:M], self.Bp[j], out=self.C[:M])
 
 
+def bytes_w4a8(M, N, K):
+    return M * K + 4 * M * (K // 128) + K * N // 2 + (K // 32) * N + 2 * M * N
+
+
+class W4A8:
+    """fp8 e4m3 activations (1x128 fp32 scales) x OCP MXFP4 weights, the fp4
+    weight shape K=4096, N=14336; weights ~ N(0,0.02) before quantisation."""
+    K, N = 4096, 14336
+    SWEEP = [1, 8, 64, 512]
+
+    def __init__(self, torch, bg, inputs):
+        self.bg = bg
+        qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((512, self.K), 1.0, 701))
+        Bq, sE = inputs.quant_mxfp4_weights(inputs.normal_f32((self.K, self.N), 0.02, 702))
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        one = bg.pack_b_mxfp4(t(Bq), t(sE), self.N)
+        self.nbuf = rotation(one.data.numel())
+        self.Bp = [one] + [bg.PackedWeights(one.dtype, one.K, one.N, one.data.clone())
+                           for _ in range(self.nbuf - 1)]
+        self.A, self.sA = t(qA), t(sA)
+        self.C = torch.empty((512, self.N), dtype=torch.bfloat16, device="cuda")
+        self.i = 0
+
+    def launch(self, M):
+        j = self.i % self.nbuf
+        self.i += 1
+        self.bg.gemm_w4a8_packed(self.A[:M], self.sA[:M], self.Bp[j], out=self.C[:M])
+
+
 class MoE:
     """Grouped (mixture-of-experts) bf16 GEMM: E = 8 experts, K = 7168,
     N = 2048, T tokens routed top-1 uniformly (seeded), rows grouped by
@@ -600,6 +629,10 @@ def main():
                                                            MFMA_PEAK_TFLOPS["bf16"], args.rounds)
         out["fp4_weight_only_packed_K4096_N14336"]["pack_ms_once"] = round(c4p.pack_ms, 3)
         del c4p
+        w48 = W4A8(torch, bigemm, inputs)
+        out["w4a8_mxfp4_K4096_N14336"] = sweep(torch, w48, W4A8.SWEEP, bytes_w4a8,
+                                               MFMA_PEAK_TFLOPS["fp8"], args.rounds)
+        del w48
         moe = MoE(torch, bigemm, inputs)
         out["moe_grouped_bf16_E8_K7168_N2048"] = sweep(torch, moe, MoE.SWEEP, moe.nbytes,
                                                        MFMA_PEAK_TFLOPS["bf16"], args.rounds)

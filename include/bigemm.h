@@ -69,7 +69,9 @@ typedef enum bi_status {
 typedef enum bi_dtype {
     BI_BF16 = 0,            /* bf16 A x bf16 B                                    */
     BI_FP8_BS = 1,          /* e4m3fn A (1x128 fp32 scales) x e4m3fn B (128x128)  */
-    BI_FP4_W = 2            /* bf16 A x e2m1 B with e4m3fn scales per 32 along K  */
+    BI_FP4_W = 2,           /* bf16 A x e2m1 B with e4m3fn scales per 32 along K  */
+    BI_W4A8 = 3             /* e4m3fn A (fp32 scale per 1x128) x OCP MXFP4 B
+                               (e2m1 with an E8M0 scale per 32 along K)          */
 } bi_dtype;
 
 /* Introspection only: the schedule a (dtype, N, K) triple runs with. */
@@ -262,6 +264,41 @@ bi_status bi_gemm_fp4_w_packed(int64_t M, int64_t N, int64_t K,
                                const uint16_t* A, int64_t lda,
                                const void* Bp, size_t bp_bytes,
                                uint16_t* C, int64_t ldc, void* stream);
+
+/*
+ * W4A8: fp8 activations x OCP MXFP4 weights -> bf16, on the mixed-format
+ * scaled MFMA (A e4m3fn, B e2m1, the weights' E8M0 block scale applied by the
+ * MFMA itself).
+ *   A  : e4m3fn [M,K], row pitch lda >= K bytes (lda % 16 == 0)
+ *   sA : fp32 [M, K/128], ldsa >= K/128; scale of A[m, 128j .. 128j+127]
+ *   Bp : packed MXFP4 weights (bi_pack_b_mxfp4), bp_bytes >=
+ *        bi_packed_b_bytes(BI_W4A8, N, K)
+ *   C  : bf16 [M,N], ldc >= N
+ * Requires K % 128 == 0 and N even.  Value: C[m,n] = sum_kb sA[m,kb] *
+ * P_kb[m,n], P_kb = sum_{k in kb} dec(A[m,k]) * e2m1(code(k,n)) *
+ * 2^(sE[k/32,n] - 127) formed by one MFMA per 128-K block, added as
+ * acc = fma(P_kb, sA, acc) with kb ascending.
+ *
+ * MXFP4 packed layout: NB = ceil(N/16), KB = K/128.  Codes: 1 KiB tile
+ * (nb, kb) at byte (nb*KB + kb)*1024; lane l = 16g + i holds the 32 codes of
+ * column 16nb + i at k = 128kb + 32g + j (one MX block), code j in byte j/2,
+ * even j in the low nibble.  Scales: 64-byte tile (nb, kb) at byte NB*KB*1024 +
+ * (nb*KB + kb)*64, byte l = sE[4kb + g][16nb + i].  Zero past N.  Size
+ * NB*KB*1088 bytes.
+ */
+
+/* Pack e2m1 codes Bq[K, N/2] (pitch ldbq >= N/2, two codes per byte, even
+ * column in the low nibble) and E8M0 scales sE[K/32, N] (pitch ldse >= N)
+ * into Bp.  Requires K % 128 == 0 and N even.  One kernel on `stream`. */
+bi_status bi_pack_b_mxfp4(int64_t N, int64_t K, const uint8_t* Bq, int64_t ldbq,
+                          const uint8_t* sE, int64_t ldse,
+                          void* Bp, size_t bp_bytes, void* stream);
+
+bi_status bi_gemm_w4a8_packed(int64_t M, int64_t N, int64_t K,
+                              const uint8_t* A, int64_t lda,
+                              const float* sA, int64_t ldsa,
+                              const void* Bp, size_t bp_bytes,
+                              uint16_t* C, int64_t ldc, void* stream);
 
 /* The schedule (dtype, N, K) selects.  There is no M argument by design.
  * Returns BI_ERR_NULL for out == NULL, BI_ERR_UNSUPPORTED for an unknown

@@ -28,7 +28,7 @@ _i64, _vp, _i32, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_s
 
 STATUS = {0: "BI_OK", 1: "BI_ERR_NULL", 2: "BI_ERR_SHAPE", 3: "BI_ERR_STRIDE",
           4: "BI_ERR_ALIGN", 5: "BI_ERR_UNSUPPORTED", 6: "BI_ERR_LAUNCH", 7: "BI_ERR_WORKSPACE"}
-BI_BF16, BI_FP8_BS, BI_FP4_W = 0, 1, 2
+BI_BF16, BI_FP8_BS, BI_FP4_W, BI_W4A8 = 0, 1, 2, 3
 
 
 class BiSchedule(ctypes.Structure):
@@ -54,6 +54,10 @@ lib.bi_gemm_fp4_w.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
 lib.bi_gemm_bf16_grouped_packed.restype = _i32
 lib.bi_gemm_bf16_grouped_packed.argtypes = [_i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _sz, _vp,
                                             _i64, _vp]
+lib.bi_pack_b_mxfp4.restype = _i32
+lib.bi_pack_b_mxfp4.argtypes = [_i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
+lib.bi_gemm_w4a8_packed.restype = _i32
+lib.bi_gemm_w4a8_packed.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp, _i64, _vp]
 lib.bi_pack_b_fp8.restype = _i32
 lib.bi_pack_b_fp8.argtypes = [_i64, _i64, _vp, _i64, _vp, _sz, _vp]
 lib.bi_gemm_fp8_blockscaled_packed.restype = _i32
@@ -308,6 +312,33 @@ def gemm_fp4_w_packed(A: torch.Tensor, Bp: PackedWeights, out: torch.Tensor | No
     _check(lib.bi_gemm_fp4_w_packed(M, Bp.N, K, A.data_ptr(), _ld(A), Bp.data.data_ptr(),
                                     Bp.data.numel(), C.data_ptr(), _ld(C), _stream()),
            "bi_gemm_fp4_w_packed")
+    return C
+
+
+def pack_b_mxfp4(Bq: torch.Tensor, sE: torch.Tensor, N: int) -> PackedWeights:
+    """Pack OCP MXFP4 weights: e2m1 codes Bq [K, N/2] and E8M0 scales sE [K/32, N]."""
+    Bq = _mat(Bq, _U8, "Bq")
+    sE = _mat(sE, _U8 + (getattr(torch, "float8_e8m0fnu", torch.uint8),), "sE")
+    K = Bq.shape[0]
+    nbytes = packed_b_bytes(BI_W4A8, N, K)
+    buf = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=Bq.device)
+    _check(lib.bi_pack_b_mxfp4(N, K, Bq.data_ptr(), _ld(Bq), sE.data_ptr(), _ld(sE),
+                               buf.data_ptr(), buf.numel(), _stream()), "bi_pack_b_mxfp4")
+    return PackedWeights(BI_W4A8, K, N, buf)
+
+
+def gemm_w4a8_packed(A: torch.Tensor, sA: torch.Tensor, Bp: PackedWeights,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = (A * sA) . MXFP4(B): e4m3fn activations with 1x128 fp32 scales, packed MXFP4 weights."""
+    A = _mat(A, _U8, "A")
+    sA = _mat(sA, (torch.float32,), "sA")
+    M, K = A.shape
+    if Bp.dtype != BI_W4A8 or Bp.K != K:
+        raise ValueError("packed weights do not match A")
+    C = _out(M, Bp.N, A.device, out)
+    _check(lib.bi_gemm_w4a8_packed(M, Bp.N, K, A.data_ptr(), _ld(A), sA.data_ptr(), _ld(sA),
+                                   Bp.data.data_ptr(), Bp.data.numel(), C.data_ptr(), _ld(C),
+                                   _stream()), "bi_gemm_w4a8_packed")
     return C
 
 

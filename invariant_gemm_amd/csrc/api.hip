@@ -32,6 +32,9 @@ Schedule schedule_for(bi_dtype dt, int64_t N, int64_t K)
     case BI_FP4_W:
         s = Schedule{/*id*/ 3, /*rb*/ 2, /*pf*/ 8, /*bm*/ 64, /*bn*/ 32, /*bk*/ 128, /*kblock*/ 32};
         break;
+    case BI_W4A8:
+        s = Schedule{/*id*/ 4, /*rb*/ 1, /*pf*/ 4, /*bm*/ 64, /*bn*/ 16, /*bk*/ 128, /*kblock*/ 128};
+        break;
     }
     return s;
 }
@@ -162,19 +165,20 @@ bi_status bi_schedule_query(bi_dtype dtype, int64_t N, int64_t K, bi_schedule* o
 {
     if (!out)
         return BI_ERR_NULL;
-    if (dtype != BI_BF16 && dtype != BI_FP8_BS && dtype != BI_FP4_W)
+    if (dtype != BI_BF16 && dtype != BI_FP8_BS && dtype != BI_FP4_W && dtype != BI_W4A8)
         return BI_ERR_UNSUPPORTED;
     if (N < 0 || K < 0)
         return BI_ERR_SHAPE;
     if (N > BI_MAX_DIM || K > BI_MAX_DIM)
         return BI_ERR_UNSUPPORTED;
-    if ((dtype == BI_FP8_BS && K % 128) || (dtype == BI_FP4_W && (K % 32 || N % 2)))
+    if ((dtype == BI_FP8_BS && K % 128) || (dtype == BI_FP4_W && (K % 32 || N % 2)) ||
+        (dtype == BI_W4A8 && (K % 128 || N % 2)))
         return BI_ERR_SHAPE;
     const Schedule s = schedule_for(dtype, N, K);
     memset(out, 0, sizeof *out);
     out->mfma_m = 16;
     out->mfma_n = 16;
-    out->mfma_k = dtype == BI_FP8_BS ? 128 : 32;
+    out->mfma_k = (dtype == BI_FP8_BS || dtype == BI_W4A8) ? 128 : 32;
     out->bm = s.bm;
     out->bn = s.bn;
     out->bk = s.bk;
@@ -222,6 +226,7 @@ size_t bi_packed_b_bytes(bi_dtype dtype, int64_t N, int64_t K)
     case BI_BF16: return (size_t)(nb * ((K + 31) / 32) * 1024);
     case BI_FP8_BS: return K % 128 ? 0 : (size_t)(nb * (K / 128) * 2048);
     case BI_FP4_W: return (K % 32 || N % 2) ? 0 : (size_t)(nb * ((K + 127) / 128) * 1088);
+    case BI_W4A8: return (K % 128 || N % 2) ? 0 : (size_t)(nb * (K / 128) * 1088);
     default: return 0;
     }
 }
@@ -428,6 +433,58 @@ bi_status bi_gemm_fp4_w_packed(int64_t M, int64_t N, int64_t K, const uint16_t* 
         return BI_ERR_UNSUPPORTED;
     GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, Bp, 0, nullptr, 0, C, ldc};
     return launched(launch_fp4w_packed(a, (hipStream_t)stream));
+}
+
+bi_status bi_pack_b_mxfp4(int64_t N, int64_t K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sE,
+                          int64_t ldse, void* Bp, size_t bp_bytes, void* stream)
+{
+    bi_status st = check_dims(1, N, K);
+    if (st != BI_OK)
+        return st;
+    if (K % 128 || N % 2)
+        return BI_ERR_SHAPE;
+    const size_t need = bi_packed_b_bytes(BI_W4A8, N, K);
+    if (need == 0)
+        return BI_OK;
+    if (need > 0x7FFFFFFFu)
+        return BI_ERR_UNSUPPORTED;
+    if (!Bq || !sE || !Bp)
+        return BI_ERR_NULL;
+    if (ldbq < N / 2 || ldse < N)
+        return BI_ERR_STRIDE;
+    if ((uintptr_t)Bp & 15u)
+        return BI_ERR_ALIGN;
+    if (bp_bytes < need)
+        return BI_ERR_WORKSPACE;
+    return launched(launch_pack_mxfp4((int)N, (int)K, Bq, ldbq, sE, ldse, (uint8_t*)Bp,
+                                      (hipStream_t)stream));
+}
+
+bi_status bi_gemm_w4a8_packed(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                              const float* sA, int64_t ldsa, const void* Bp, size_t bp_bytes,
+                              uint16_t* C, int64_t ldc, void* stream)
+{
+    bi_status st = check_dims(M, N, K);
+    if (st != BI_OK)
+        return st;
+    if (K % 128 || N % 2)
+        return BI_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return BI_OK;
+    if (!C || (K > 0 && (!A || !sA || !Bp)))
+        return BI_ERR_NULL;
+    if ((K > 0 && (lda < K || ldsa < K / 128)) || ldc < N)
+        return BI_ERR_STRIDE;
+    if (((uintptr_t)C & 1u) ||
+        (K > 0 && (!aligned16(A) || lda % 16 || !aligned16(Bp) || !aligned4(sA))))
+        return BI_ERR_ALIGN;
+    const size_t need = bi_packed_b_bytes(BI_W4A8, N, K);
+    if (bp_bytes < need)
+        return BI_ERR_WORKSPACE;
+    if (need > 0x7FFFFFFFu || (M + 15) / 16 * ((N + 15) / 16) > 0x7FFFFFFF)
+        return BI_ERR_UNSUPPORTED;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, sA, ldsa, Bp, 0, nullptr, 0, C, ldc};
+    return launched(launch_w4a8_packed(a, (hipStream_t)stream));
 }
 
 int bi_splitk_choose(int64_t M, int64_t N, int64_t K)

@@ -46,6 +46,9 @@ hipError_t launch_pack_fp8(int N, int K, const uint8_t* B, int64_t ldb, uint8_t*
                            hipStream_t stream);
 int fp8_packed_geometry(int M, int N);
 hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_pack_mxfp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sE,
+                             int64_t ldse, uint8_t* Bp, hipStream_t stream);
 hipError_t launch_pack_fp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sB,
                            int64_t ldsb, uint8_t* Bp, hipStream_t stream);
 hipError_t launch_bf16_splitk(const GemmArgs& a, const Schedule& s, float* ws, int splits,

@@ -217,3 +217,23 @@ def test_grouped_validation():
     assert f(3, 8, nb=need * 3 - 1) == WS
     assert f(3, 8, off=P + 2) == ALIGN
     assert f(1 << 20, 8) == UNSUP
+
+
+def test_w4a8_validation():
+    need = lambda N, K: bigemm.packed_b_bytes(bigemm.BI_W4A8, N, K)
+    assert need(2048, 7168) == 128 * 56 * 1088 and need(64, 100) == 0 and need(63, 128) == 0
+    f = lambda M, N, K, A=P, lda=None, sA=P, Bp=P, nb=None, C=P: lib.bi_gemm_w4a8_packed(
+        M, N, K, A, K if lda is None else lda, sA, max(K // 128, 1), Bp,
+        need(N, K) if nb is None else nb, C, N, None)
+    assert f(4, 64, 100) == SHAPE
+    assert f(4, 63, 128) == SHAPE
+    assert f(4, 64, 128, sA=None) == NULL
+    assert f(4, 64, 128, nb=need(64, 128) - 1) == WS
+    assert f(4, 64, 128, lda=136) == ALIGN
+    assert f(4, 64, 128, sA=P + 2) == ALIGN
+    assert f(0, 64, 128, A=None, sA=None, Bp=None, C=None) == OK
+    assert lib.bi_pack_b_mxfp4(64, 100, P, 32, P, 64, P, 1 << 20, None) == SHAPE
+    assert lib.bi_pack_b_mxfp4(64, 128, P, 16, P, 64, P, 1 << 20, None) == STRIDE
+    assert lib.bi_pack_b_mxfp4(64, 128, P, 32, P, 64, P, need(64, 128) - 1, None) == WS
+    s = bigemm.schedule(bigemm.BI_W4A8, 14336, 4096)
+    assert s["mfma_k"] == 128
