@@ -320,18 +320,17 @@ hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 }  // namespace
 
 // Launch geometry (tile sharing only; the per-element arithmetic is the same
-// for all): as for the fp8 packed GEMM.
+// for all), from a sweep on the K = 4096, N = 14336 weight shape: for
+// M <= 16 four waves each stream their own 16-column block and share one
+// staged activation tile; 64 x 64 tiles above that, with one K block per
+// stage once M > 128.
 hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream)
 {
-    const int nb = (a.N + 15) / 16;
-    const int mt64 = (a.M + 63) / 64;
-    if (a.M > 64 && mt64 * ((nb + 3) / 4) >= 256)
-        return launch_geometry<4, 4, 4, 2, 2, 2, 2>(a, stream);      // 64 x 64
     if (a.M > 128)
-        return launch_geometry<4, 4, 2, 2, 1, 2, 4>(a, stream);      // 64 x 32
+        return launch_geometry<4, 4, 4, 2, 2, 1, 4>(a, stream);
     if (a.M > 16)
-        return launch_geometry<4, 4, 1, 1, 1, 4, 4>(a, stream);      // 64 x 16
-    return launch_geometry<8, 1, 1, 1, 1, 8, 4>(a, stream);          // 16 x 16, streaming
+        return launch_geometry<4, 4, 4, 2, 2, 2, 2>(a, stream);
+    return launch_geometry<4, 1, 4, 1, 1, 4, 4>(a, stream);
 }
 
 hipError_t launch_pack_mxfp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sE,
