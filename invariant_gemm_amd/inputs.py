@@ -189,3 +189,25 @@ def quant_mxfp4_weights(w: np.ndarray, block_k: int = 32):
     codes = _e2m1_codes((wb / scale[:, None, :]).reshape(K, N))
     Bq = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
     return Bq, (e + 127).astype(np.uint8)
+
+
+# ------------------------------------------------------------ decode attention
+
+BF16_NAN = 0x7FC0
+
+
+def seq_lens(batch: int, lmax: int, seed: int, lo: int = 1) -> np.ndarray:
+    """Ragged decode lengths: int32 [batch], uniform in [lo, lmax]."""
+    return rng(seed).integers(lo, lmax + 1, size=batch).astype(np.int32)
+
+
+def kv_cache(batch: int, h_kv: int, lmax: int, d: int, seed: int, lens=None,
+             sigma: float = 1.0, pad: int = BF16_NAN) -> np.ndarray:
+    """One cache tensor, bf16 codes [batch][h_kv][lmax][d] ~ N(0, sigma^2).
+    Positions at or past lens[b] hold the code ``pad`` (NaN by default), so a
+    kernel that reads past a sequence's length shows it in its output."""
+    c = normal_bf16((batch, h_kv, lmax, d), sigma, seed)
+    if lens is not None:
+        for b, n in enumerate(np.asarray(lens)):
+            c[b, :, int(n):, :] = pad
+    return c

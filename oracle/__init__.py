@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the batch-invariant GEMM -- TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle for the batch-invariant GEMM and decode attention -- TEST INFRASTRUCTURE ONLY.
 
 Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
 of ``bench.py`` may import this package.  The product library never loads it,
@@ -75,6 +75,9 @@ def _load():
     lib.ora_dec_e8m0.argtypes = [ctypes.c_uint8]
     lib.ora_gemm_w4a8.restype = None
     lib.ora_gemm_w4a8.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, vp, i64]
+    lib.ora_decode_attn.restype = None
+    lib.ora_decode_attn.argtypes = [i64, i64, i64, i64, i64, vp, vp, vp, vp,
+                                    ctypes.c_double, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -229,3 +232,33 @@ def gemm_w4a8(qA: np.ndarray, sA: np.ndarray, Bq: np.ndarray, sE: np.ndarray, N:
         _load().ora_gemm_w4a8(M, N, K, _p(qA), _ld(qA), _p(sA), _ld(sA), _p(Bq), _ld(Bq),
                               _p(sE), _ld(sE), _p(C), _p(S), N)
     return C, S
+
+
+def decode_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, lens, scale: float,
+                     weights: bool = False):
+    """Decode attention by its definition (scaled dot-product attention,
+    Vaswani et al. 2017, equation 1, with grouped-query heads): query head h of
+    sequence b attends to keys/values [0, lens[b]) of KV head h // (Hq/Hkv).
+
+    Q uint16 bf16 codes [B,Hq,D]; K, V uint16 bf16 codes [B,Hkv,Lmax,D];
+    lens int [B].  Returns O fp64 [B,Hq,D], and with ``weights`` also
+    W fp64 [B,Hq,Lmax] (normalised softmax weights, 0 past the length) and
+    A fp64 [B,Hq,Lmax] (sum_d |q_d k_jd|, the scale of a score's rounding)."""
+    Q = np.ascontiguousarray(Q, np.uint16)
+    K = np.ascontiguousarray(K, np.uint16)
+    V = np.ascontiguousarray(V, np.uint16)
+    B, Hq, D = Q.shape
+    B2, Hkv, Lmax, D2 = K.shape
+    if V.shape != K.shape or B2 != B or D2 != D or Hkv == 0 or Hq % Hkv:
+        raise ValueError("shapes: Q [B,Hq,D], K and V [B,Hkv,Lmax,D], Hq a multiple of Hkv")
+    lens = np.ascontiguousarray(lens, np.int32)
+    if lens.shape != (B,) or np.any(lens < 0) or np.any(lens > Lmax):
+        raise ValueError("lens must be [B] in [0, Lmax]")
+    O = np.empty((B, Hq, D), np.float64)
+    W = np.empty((B, Hq, Lmax), np.float64) if weights else None
+    A = np.empty((B, Hq, Lmax), np.float64) if weights else None
+    if B and Hq and D:
+        _load().ora_decode_attn(B, Hq, Hkv, D, Lmax, _p(Q), _p(K), _p(V), _p(lens),
+                                float(scale), _p(O), _p(W) if weights else None,
+                                _p(A) if weights else None)
+    return (O, W, A) if weights else O

@@ -1,5 +1,6 @@
 /*
- * oracle.c -- fp64 CPU oracle for the batch-invariant GEMM.
+ * oracle.c -- fp64 CPU oracle for the batch-invariant GEMM and for the
+ * decode attention that the same pages pair with it (at the end of the file).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
  * call this file: only the test suite, the smoke check and the CPU-baseline
@@ -28,6 +29,7 @@
  * threading does not change any result.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -266,5 +268,81 @@ void ora_gemm_fp4w(int64_t M, int64_t N, int64_t K,
                 s[n] += fabs(p);
             }
         }
+    }
+}
+
+/* ------------------------------------------------------- decode attention */
+
+/* Decode attention: one query token per sequence attends to the first
+ * lens[b] cached keys of its sequence.  The pages name this operation (the
+ * dual-kernel decode attention of the QbitAI article on V4's batch
+ * invariance, the part on split-KV, and section 4.1 of the lshu.cn article)
+ * but print no formula, so this is the textbook scaled dot-product attention
+ * (Vaswani et al. 2017, equation 1) with grouped-query heads (Ainslie et al.
+ * 2023): query head h reads KV head h / G, G = Hq / Hkv.
+ *
+ *   z_j = scale * sum_d q[d] * k_j[d]             j < L = lens[b]
+ *   w_j = exp(z_j - max_i z_i) / sum_i exp(z_i - max_i z_i)
+ *   o[d] = sum_j w_j * v_j[d]
+ *
+ * Layouts: Q and O [B][Hq][D]; K and V [B][Hkv][Lmax][D]; all bf16 codes,
+ * row-major.  O is returned in binary64.  Optional outputs (NULL to skip):
+ * W [B][Hq][Lmax] the normalised weights w_j (0 for j >= L) and
+ * A [B][Hq][Lmax] the absolute dot products sum_d |q[d] * k_j[d]|, which
+ * scale the rounding error of a binary32 score.  L = 0 gives o = 0.
+ * Subtracting the maximum does not change w_j; it only keeps exp in range. */
+void ora_decode_attn(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Lmax,
+                     const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                     const int32_t* lens, double scale,
+                     double* O, double* W, double* A)
+{
+    int64_t G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < B * Hq; ++t) {
+        int64_t b = t / Hq, h = t % Hq, kvh = h / G;
+        int64_t L = lens[b];
+        const uint16_t* q = Q + t * D;
+        const uint16_t* kb = K + (b * Hkv + kvh) * Lmax * D;
+        const uint16_t* vb = V + (b * Hkv + kvh) * Lmax * D;
+        double* o = O + t * D;
+        double* w = W ? W + t * Lmax : NULL;
+        double* a = A ? A + t * Lmax : NULL;
+        double s_stack[64];
+        double* s = L <= 64 ? s_stack : (double*)malloc((size_t)L * sizeof(double));
+        double smax = -INFINITY, den = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            o[d] = 0.0;
+        if (w)
+            for (int64_t j = 0; j < Lmax; ++j)
+                w[j] = 0.0;
+        if (a)
+            for (int64_t j = 0; j < Lmax; ++j)
+                a[j] = 0.0;
+        for (int64_t j = 0; j < L; ++j) {
+            double acc = 0.0, aabs = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                double p = ora_dec_bf16(q[d]) * ora_dec_bf16(kb[j * D + d]);
+                acc += p;
+                aabs += fabs(p);
+            }
+            s[j] = scale * acc;
+            if (a)
+                a[j] = aabs;
+            if (s[j] > smax)
+                smax = s[j];
+        }
+        for (int64_t j = 0; j < L; ++j) {
+            s[j] = exp(s[j] - smax);
+            den += s[j];
+        }
+        for (int64_t j = 0; j < L; ++j) {
+            double wj = s[j] / den;
+            if (w)
+                w[j] = wj;
+            for (int64_t d = 0; d < D; ++d)
+                o[d] += wj * ora_dec_bf16(vb[j * D + d]);
+        }
+        if (s != s_stack)
+            free(s);
     }
 }
