@@ -300,6 +300,72 @@ bi_status bi_gemm_w4a8_packed(int64_t M, int64_t N, int64_t K,
                               const void* Bp, size_t bp_bytes,
                               uint16_t* C, int64_t ldc, void* stream);
 
+/*
+ * Batch-invariant decode attention, in two kernels with identical results.
+ *
+ * The pages pair the batch-invariant GEMM with a "dual-kernel" decode
+ * attention: one program for a GPU the batch keeps busy and one for a GPU it
+ * does not, bit-identical to each other (the QbitAI article on V4's batch
+ * invariance, its part on split-KV; section 4.1 of the lshu.cn article).
+ * One query token per sequence attends to the first seq_lens[b] keys of its
+ * sequence (scaled dot-product attention, grouped-query heads: query head h
+ * reads KV head h / (Hq / Hkv)):
+ *   o = sum_j softmax_j(scale * q . k_j) v_j
+ * The reduction order is fixed by the sequence length alone: 64-key
+ * sub-chunks at fixed positions, each reduced by one wave (exp2 of the
+ * scaled score minus the sub-chunk max, rounded to bf16, then P . V by
+ * MFMA in fp32), merged left to right into 256-key groups, and the groups
+ * merged left to right.  BI_ATTN_SINGLE walks a sequence's groups in one
+ * workgroup; BI_ATTN_SPLIT gives each group its own workgroup (split-KV) and
+ * merges the stored group states in a second kernel.  A sequence's output is
+ * the same bits whatever the batch around it and whichever kernel runs.
+ *
+ *   Q, O     : bf16 [B][Hq][D], contiguous, 16-byte aligned
+ *   K, V     : bf16 [B][Hkv][Lmax][D], contiguous, 16-byte aligned (the
+ *              cache; only rows j < seq_lens[b] are read, the rest may hold
+ *              anything, NaN included)
+ *   seq_lens : device int32 [B], read on the device and clamped into
+ *              [0, Lmax]; a sequence of length 0 gets o = 0
+ *   scale    : softmax scale (typically 1/sqrt(D)); the kernels use
+ *              fp32(scale * log2 e) and exp2
+ *   D        : must be BI_ATTN_HEAD_DIM; Hq = G * Hkv with 1 <= G <= 16
+ *   kernel   : BI_ATTN_AUTO, BI_ATTN_SINGLE or BI_ATTN_SPLIT
+ *   workspace: device buffer (16-byte aligned) of at least
+ *              bi_decode_attention_workspace_bytes(...) for BI_ATTN_SPLIT;
+ *              BI_ATTN_AUTO runs the single-pass kernel when it is missing
+ *              or too small.  The caller owns it; it holds nothing between
+ *              calls.
+ * Errors: BI_ERR_SHAPE (negative size, Hq not a multiple of Hkv),
+ * BI_ERR_UNSUPPORTED (D != 128, G > 16, Lmax > BI_ATTN_MAX_LEN, grid too
+ * large, unknown kernel), BI_ERR_NULL, BI_ERR_ALIGN, BI_ERR_WORKSPACE (split
+ * kernel without enough workspace).  B == 0 or Hq == 0 is a no-op.
+ * Enqueues one kernel (single pass) or two (split, merge) on `stream`.
+ */
+#define BI_ATTN_HEAD_DIM 128
+#define BI_ATTN_MAX_GROUP 16
+#define BI_ATTN_MAX_LEN (1 << 22)
+
+typedef enum {
+    BI_ATTN_AUTO = 0,
+    BI_ATTN_SINGLE = 1,
+    BI_ATTN_SPLIT = 2
+} bi_attn_kernel;
+
+/* Workspace bytes BI_ATTN_SPLIT needs: B * Hkv * ceil(Lmax / 256) group
+ * states of G * 128 + 2 * G floats each (o, m, l), rounded up to a multiple
+ * of 4 floats.  0 for invalid sizes. */
+size_t bi_decode_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax);
+
+/* The kernel BI_ATTN_AUTO picks for these sizes (given enough workspace):
+ * the split kernel while the (sequence, KV head) pairs alone cannot give
+ * every compute unit a workgroup and a sequence spans more than one group. */
+int bi_decode_attention_choice(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax);
+
+bi_status bi_decode_attention_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Lmax,
+                                   const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                   const int32_t* seq_lens, float scale, uint16_t* O,
+                                   void* workspace, size_t ws_bytes, int kernel, void* stream);
+
 /* The schedule (dtype, N, K) selects.  There is no M argument by design.
  * Returns BI_ERR_NULL for out == NULL, BI_ERR_UNSUPPORTED for an unknown
  * dtype, BI_ERR_SHAPE for invalid N or K. */

@@ -78,6 +78,13 @@ lib.bi_status_str.restype = ctypes.c_char_p
 lib.bi_status_str.argtypes = [_i32]
 lib.bi_version.restype = ctypes.c_char_p
 lib.bi_version.argtypes = []
+lib.bi_decode_attention_workspace_bytes.restype = _sz
+lib.bi_decode_attention_workspace_bytes.argtypes = [_i64, _i64, _i64, _i64]
+lib.bi_decode_attention_choice.restype = _i32
+lib.bi_decode_attention_choice.argtypes = [_i64, _i64, _i64, _i64]
+lib.bi_decode_attention_bf16.restype = _i32
+lib.bi_decode_attention_bf16.argtypes = [_i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
+                                         ctypes.c_float, _vp, _vp, _sz, _i32, _vp]
 
 
 class BigemmError(RuntimeError):
@@ -360,3 +367,50 @@ def gemm_bf16_splitk(A: torch.Tensor, B: torch.Tensor, workspace: torch.Tensor, 
                                    C.data_ptr(), _ld(C), workspace.data_ptr(),
                                    workspace.numel() * 4, splits, _stream()), "bi_gemm_bf16_splitk")
     return C
+
+
+# ----------------------------------------------------------- decode attention
+
+ATTN_AUTO, ATTN_SINGLE, ATTN_SPLIT = 0, 1, 2
+_ATTN_KERNELS = {"auto": ATTN_AUTO, "single": ATTN_SINGLE, "split": ATTN_SPLIT}
+
+
+def decode_attention_workspace_bytes(B: int, Hq: int, Hkv: int, Lmax: int) -> int:
+    return int(lib.bi_decode_attention_workspace_bytes(B, Hq, Hkv, Lmax))
+
+
+def decode_attention_choice(B: int, Hq: int, Hkv: int, Lmax: int) -> str:
+    k = int(lib.bi_decode_attention_choice(B, Hq, Hkv, Lmax))
+    return {ATTN_SINGLE: "single", ATTN_SPLIT: "split"}[k]
+
+
+def decode_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens: torch.Tensor,
+                     scale: float, kernel: str = "auto", workspace: torch.Tensor | None = None,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """Batch-invariant decode attention via bi_decode_attention_bf16.
+
+    Q [B,Hq,128] bf16; K, V [B,Hkv,Lmax,128] bf16 (contiguous); seq_lens int32 [B]
+    on the device.  kernel: "auto", "single" or "split" (identical results).
+    A workspace is allocated here when none is given and the split kernel may run."""
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if t.dtype not in _BF16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name}: expected a contiguous bf16 device tensor")
+    if Q.dim() != 3 or K.dim() != 4 or V.shape != K.shape:
+        raise ValueError("Q [B,Hq,D], K and V [B,Hkv,Lmax,D]")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or seq_lens.dim() != 1:
+        raise TypeError("seq_lens: int32 device vector")
+    B, Hq, D = Q.shape
+    Hkv, Lmax = K.shape[1], K.shape[2]
+    k = _ATTN_KERNELS[kernel]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=Q.device)
+    need = decode_attention_workspace_bytes(B, Hq, Hkv, Lmax)
+    if workspace is None and k != ATTN_SINGLE and need:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=Q.device)
+    wp, wb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
+        if workspace is not None else (None, 0)
+    _check(lib.bi_decode_attention_bf16(B, Hq, Hkv, D, Lmax, Q.data_ptr(), K.data_ptr(),
+                                        V.data_ptr(), seq_lens.data_ptr(), float(scale),
+                                        out.data_ptr(), wp, wb, k, _stream()),
+           "bi_decode_attention_bf16")
+    return out

@@ -161,6 +161,85 @@ const char* bi_status_str(bi_status s)
 
 const char* bi_version(void) { return "libbigemm 0.1.0 gfx950"; }
 
+// ------------------------------------------------------------ decode attention
+
+namespace {
+
+// Compute units of an MI355X: below this many (sequence, KV head) pairs the
+// single-pass kernel leaves compute units idle.
+constexpr int64_t kAttnSplitBelow = 256;
+
+bi_status attn_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t* G)
+{
+    if (B < 0 || Hq < 0 || Hkv < 0 || Lmax < 0)
+        return BI_ERR_SHAPE;
+    if (B > BI_MAX_DIM || Hq > BI_MAX_DIM || Lmax > BI_ATTN_MAX_LEN)
+        return BI_ERR_UNSUPPORTED;
+    if (B == 0 || Hq == 0) {
+        *G = 0;
+        return BI_OK;
+    }
+    if (Hkv == 0 || Hq % Hkv)
+        return BI_ERR_SHAPE;
+    *G = Hq / Hkv;
+    if (*G > BI_ATTN_MAX_GROUP)
+        return BI_ERR_UNSUPPORTED;
+    if (B * Hq > 0x7FFFFFFF || B * Hkv * attn_groups(Lmax) > 0x7FFFFFFF)
+        return BI_ERR_UNSUPPORTED;
+    return BI_OK;
+}
+
+}  // namespace
+
+size_t bi_decode_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax)
+{
+    int64_t G = 0;
+    if (attn_sizes(B, Hq, Hkv, Lmax, &G) != BI_OK || G == 0)
+        return 0;
+    return (size_t)attn_ws_floats(B, Hkv, G, Lmax) * sizeof(float);
+}
+
+int bi_decode_attention_choice(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax)
+{
+    (void)Hq;
+    return (B * Hkv < kAttnSplitBelow && attn_groups(Lmax) > 1) ? BI_ATTN_SPLIT : BI_ATTN_SINGLE;
+}
+
+bi_status bi_decode_attention_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Lmax,
+                                   const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                   const int32_t* seq_lens, float scale, uint16_t* O,
+                                   void* workspace, size_t ws_bytes, int kernel, void* stream)
+{
+    int64_t G = 0;
+    bi_status st = attn_sizes(B, Hq, Hkv, Lmax, &G);
+    if (st != BI_OK)
+        return st;
+    if (D < 0)
+        return BI_ERR_SHAPE;
+    if (D != BI_ATTN_HEAD_DIM || kernel < BI_ATTN_AUTO || kernel > BI_ATTN_SPLIT)
+        return BI_ERR_UNSUPPORTED;
+    if (B == 0 || Hq == 0)
+        return BI_OK;
+    if (!Q || !O || !seq_lens || (Lmax > 0 && (!K || !V)))
+        return BI_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(O) || ((uintptr_t)seq_lens & 3u) ||
+        (Lmax > 0 && (!aligned16(K) || !aligned16(V))))
+        return BI_ERR_ALIGN;
+    const size_t need = (size_t)attn_ws_floats(B, Hkv, G, Lmax) * sizeof(float);
+    const bool ws_ok = need == 0 || (workspace && ws_bytes >= need);
+    if (kernel == BI_ATTN_SPLIT && !ws_ok)
+        return BI_ERR_WORKSPACE;
+    if (ws_ok && need > 0 && !aligned16(workspace))
+        return BI_ERR_ALIGN;
+    bool split = kernel == BI_ATTN_SPLIT;
+    if (kernel == BI_ATTN_AUTO)
+        split = ws_ok && bi_decode_attention_choice(B, Hq, Hkv, Lmax) == BI_ATTN_SPLIT;
+    const float c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
+    AttnArgs a{B, Hq, Hkv, G, Lmax, Q, K, V, seq_lens, c, O, (float*)workspace};
+    return launched(launch_attn_decode(a, split, (hipStream_t)stream));
+}
+
+
 bi_status bi_schedule_query(bi_dtype dtype, int64_t N, int64_t K, bi_schedule* out)
 {
     if (!out)

@@ -54,4 +54,19 @@ hipError_t launch_pack_fp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const 
 hipError_t launch_bf16_splitk(const GemmArgs& a, const Schedule& s, float* ws, int splits,
                               hipStream_t stream);
 
+// Decode attention (head dimension 128).  c = scale * log2(e) in fp32.
+struct AttnArgs {
+    int64_t B, Hq, Hkv, G, Lmax;
+    const uint16_t* Q;
+    const uint16_t* K;
+    const uint16_t* V;
+    const int32_t* lens;
+    float c;
+    uint16_t* O;
+    float* ws;
+};
+int64_t attn_groups(int64_t Lmax);
+int64_t attn_ws_floats(int64_t B, int64_t Hkv, int64_t G, int64_t Lmax);
+hipError_t launch_attn_decode(const AttnArgs& a, bool split, hipStream_t stream);
+
 }  // namespace bigemm

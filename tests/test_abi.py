@@ -237,3 +237,28 @@ def test_w4a8_validation():
     assert lib.bi_pack_b_mxfp4(64, 128, P, 32, P, 64, P, need(64, 128) - 1, None) == WS
     s = bigemm.schedule(bigemm.BI_W4A8, 14336, 4096)
     assert s["mfma_k"] == 128
+
+
+def test_decode_attention_validation():
+    need = lambda B, Hq, Hkv, L: lib.bi_decode_attention_workspace_bytes(B, Hq, Hkv, L)
+    assert need(1, 64, 8, 4096) == 8 * 16 * (8 * 128 + 16) * 4
+    assert need(3, 6, 3, 257) == 3 * 3 * 2 * (2 * 128 + 4) * 4
+    assert need(1, 6, 4, 64) == 0 and need(1, 64, 2, 64) == 0   # bad group / G > 16
+
+    def f(B=2, Hq=16, Hkv=2, D=128, L=512, Q=P, K=P, V=P, lens=P, O=P, ws=P, nb=None, kernel=2):
+        nb = need(B, Hq, Hkv, L) if nb is None else nb
+        return lib.bi_decode_attention_bf16(B, Hq, Hkv, D, L, Q, K, V, lens, 0.1, O, ws, nb,
+                                            kernel, None)
+    assert f(B=-1) == SHAPE and f(L=-1) == SHAPE and f(D=-1) == SHAPE
+    assert f(Hq=15) == SHAPE and f(Hkv=0) == SHAPE
+    assert f(D=64) == UNSUP and f(Hq=34) == UNSUP and f(L=(1 << 22) + 1) == UNSUP
+    assert f(kernel=3) == UNSUP and f(kernel=-1) == UNSUP
+    assert f(B=0, Q=None, K=None, V=None, lens=None, O=None, ws=None) == OK
+    assert f(Hq=0, Hkv=0, Q=None, O=None) == OK
+    assert f(Q=None) == NULL and f(lens=None) == NULL and f(K=None) == NULL
+    assert f(Q=P + 8) == ALIGN and f(V=P + 2) == ALIGN and f(lens=P + 2) == ALIGN
+    assert f(ws=None) == WS and f(nb=need(2, 16, 2, 512) - 1) == WS
+    assert f(ws=P + 4) == ALIGN
+    assert bigemm.decode_attention_choice(1, 64, 8, 4096) == "split"
+    assert bigemm.decode_attention_choice(32, 64, 8, 4096) == "single"
+    assert bigemm.decode_attention_choice(1, 64, 8, 256) == "single"    # one group: nothing to split
