@@ -24,6 +24,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -465,6 +466,75 @@ def sweep(torch, wl, Ms, nbytes_fn, peak, rounds):
     return out
 
 
+def decode_attention(torch, bg, rounds, L=4096, Hq=64, Hkv=8, Bs=(1, 16, 64)):
+    """Dual-kernel decode attention, one query token per sequence over a
+    4096-key bf16 cache (Hq = 64 query heads, Hkv = 8 KV heads, D = 128): per
+    batch size the single-pass kernel, the split-KV kernel (+ merge) and the
+    one the library picks.  The cache of the largest batch (1.07 GB of K and
+    V) is filled once with seeded N(0,1) values; smaller batches rotate over
+    its sequences so every launch reads HBM.  Bytes: K and V of every
+    sequence plus Q and O."""
+    D = 128
+    Bmax = max(Bs)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20260)
+    Kc = torch.randn((Bmax, Hkv, L, D), generator=g, device="cuda").to(torch.bfloat16)
+    Vc = torch.randn((Bmax, Hkv, L, D), generator=g, device="cuda").to(torch.bfloat16)
+    Qa = torch.randn((Bmax, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    lens = torch.full((Bmax,), L, dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    res = {}
+    for B in Bs:
+        nrot = Bmax // B
+        views = [(Qa[i * B:(i + 1) * B], Kc[i * B:(i + 1) * B], Vc[i * B:(i + 1) * B])
+                 for i in range(nrot)]
+        ws = torch.empty(bg.decode_attention_workspace_bytes(B, Hq, Hkv, L) // 4,
+                         dtype=torch.float32, device="cuda")
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+        nbytes = 2 * B * Hkv * L * D * 2 + 2 * B * Hq * D * 2
+        row = {"bytes": nbytes, "auto_picks": bg.decode_attention_choice(B, Hq, Hkv, L)}
+        for kern in ("single", "split"):
+            i = [0]
+
+            def fn():
+                q, k, v = views[i[0] % nrot]
+                i[0] += 1
+                bg.decode_attention(q, k, v, lens[:B], scale, kernel=kern, workspace=ws, out=out)
+            med, mn = time_launches(torch, fn, reps=max(nrot, 16), rounds=max(3, rounds // 2))
+            gbs = nbytes / (med * 1e-6) / 1e9
+            row[kern] = {"us": round(med, 2), "us_min": round(mn, 2), "gbs": round(gbs, 1),
+                         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        row["auto"] = row[row["auto_picks"]]
+        res[str(B)] = row
+        del ws, out
+    del Kc, Vc, Qa
+    torch.cuda.empty_cache()
+    return res
+
+
+def attention_probe(torch, bg, L=4096, Hq=64, Hkv=8):
+    """Three eager single-pass launches at B = 64, then three split launches
+    at B = 1 (each followed by its merge), on distinct cache slices."""
+    D = 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261)
+    Kc = torch.randn((67, Hkv, L, D), generator=g, device="cuda").to(torch.bfloat16)
+    Vc = torch.randn((67, Hkv, L, D), generator=g, device="cuda").to(torch.bfloat16)
+    Q = torch.randn((64, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    lens = torch.full((64,), L, dtype=torch.int32, device="cuda")
+    for i in range(3):
+        bg.decode_attention(Q, Kc[i:i + 64], Vc[i:i + 64], lens, 0.088, kernel="single")
+    torch.cuda.synchronize()
+    log("probe: 3 x single-pass B=64 done")
+    ws = torch.empty(bg.decode_attention_workspace_bytes(1, Hq, Hkv, L) // 4, dtype=torch.float32,
+                     device="cuda")
+    for i in range(3):
+        bg.decode_attention(Q[:1], Kc[64 + i:65 + i], Vc[64 + i:65 + i], lens[:1], 0.088,
+                            kernel="split", workspace=ws)
+    torch.cuda.synchronize()
+    log("probe: 3 x split B=1 done")
+
+
 def replay(torch, bg, inputs, steps=1000):
     """Dynamic-batching replay on the bf16 projection shape: pool of 4096 rows,
     `steps` batches of 1..256 distinct rows; GPU time of the GEMM launches."""
@@ -510,6 +580,11 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline only, no extra legs")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only run a known-size copy plus 3 launches per M (for rocprofv3 --pmc)")
+    ap.add_argument("--attention", action="store_true",
+                    help="only the decode-attention leg (one JSON object)")
+    ap.add_argument("--attention-probe", action="store_true",
+                    help="eager decode-attention launches for rocprofv3 --pmc: B = 64 single "
+                         "pass x3, then B = 1 split x3 (L = 4096, Hq = 64, Hkv = 8)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise the FETCH_SIZE and WRITE_SIZE runs of --pmc-probe (no GPU)")
     args = ap.parse_args()
@@ -530,6 +605,12 @@ def main():
     dev = torch.cuda.get_device_properties(0)
     log(f"device: {dev.name}, CUs {dev.multi_processor_count}")
 
+    if args.attention:
+        print(json.dumps(decode_attention(torch, bigemm, args.rounds)), flush=True)
+        return
+    if args.attention_probe:
+        attention_probe(torch, bigemm)
+        return
     wl = C2P(torch, bigemm, inputs)
     if args.pmc_probe:
         pmc_probe(torch, wl)
@@ -638,6 +719,7 @@ def main():
                                                        MFMA_PEAK_TFLOPS["bf16"], args.rounds)
         del moe
         out["replay_bf16_K8192_N8192"] = replay(torch, bigemm, inputs)
+        out["decode_attention_L4096_Hq64_Hkv8_D128"] = decode_attention(torch, bigemm, args.rounds)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

@@ -360,35 +360,45 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
 
 // Folds the group states of one (sequence, query head) in ascending group
 // order and writes the output row.  Grid B*Hq, 128 threads (one per d).
-// Loads are issued eight groups at a time ahead of their merges.
+// Group states are loaded eight at a time ahead of their merges; the first
+// eight are requested together with the sequence length (indices clamped to
+// the workspace's capacity, ngm, so no load waits for the length).
 __global__ __launch_bounds__(128) void attn_merge_kernel(
     int Hq, int Hkv, int G, int Lmax, int ngm, const int32_t* __restrict__ lens,
     const float* __restrict__ ws, uint16_t* __restrict__ O)
 {
+    constexpr int kBatch = 8;
     const int d = threadIdx.x;
     const int bq = blockIdx.x;
     const int b = bq / Hq;
     const int hq = bq - b * Hq;
     const int kvh = hq / G;
     const int h = hq - kvh * G;
-    const int L = min(max(lens[b], 0), Lmax);
-    const int ng = (L + kGroup - 1) / kGroup;
     const int n_el = G * kD;
     const int64_t stride = ws_stride(G);
     const float* src = ws + ((int64_t)b * Hkv + kvh) * ngm * stride;
+    const int lraw = lens[b];
 
     float m = 0.f, l = 0.f, o = 0.f;
-    for (int t0 = 0; t0 < ng; t0 += 8) {
-        float bm[8], bl[8], bo[8];
+    float bm[kBatch], bl[kBatch], bo[kBatch];
+    auto load = [&](int t0, int last) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t base = (int64_t)min(t0 + i, ng - 1) * stride;
+        for (int i = 0; i < kBatch; ++i) {
+            const int64_t base = (int64_t)min(t0 + i, last) * stride;
             bo[i] = src[base + h * kD + d];
             bm[i] = src[base + n_el + h];
             bl[i] = src[base + n_el + G + h];
         }
+    };
+    if (ngm > 0)
+        load(0, ngm - 1);
+    const int L = min(max(lraw, 0), Lmax);
+    const int ng = (L + kGroup - 1) / kGroup;
+    for (int t0 = 0; t0 < ng; t0 += kBatch) {
+        if (t0 > 0)
+            load(t0, ng - 1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < kBatch; ++i) {
             if (t0 + i >= ng)
                 break;
             if (t0 + i == 0) {
