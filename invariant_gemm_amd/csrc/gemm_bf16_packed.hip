@@ -288,8 +288,8 @@ hipError_t launch_packed(const GemmArgs& a, const GroupArgs* grp, int geometry, 
     switch (geometry) {
     case 4: return launch_geometry<4, 2, 4, 4, 4>(a, grp, stream);
     case 3: return launch_geometry<4, 1, 4, 4, 4>(a, grp, stream);
-    case 2: return launch_geometry<2, 1, 4, 2, 8>(a, grp, stream);
-    case 1: return launch_geometry<2, 1, 2, 4, 6>(a, grp, stream);
+    case 2: return launch_geometry<2, 1, 4, 4, 4>(a, grp, stream);
+    case 1: return launch_geometry<2, 1, 2, 8, 2>(a, grp, stream);
     default: return launch_geometry<2, 1, 1, 8, 4>(a, grp, stream);
     }
 }
