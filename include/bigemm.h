@@ -357,8 +357,10 @@ typedef enum {
 size_t bi_decode_attention_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax);
 
 /* The kernel BI_ATTN_AUTO picks for these sizes (given enough workspace):
- * the split kernel while the (sequence, KV head) pairs alone cannot give
- * every compute unit a workgroup and a sequence spans more than one group. */
+ * the split kernel while there are fewer than 192 (sequence, KV head) pairs
+ * -- too few workgroups for the single-pass kernel to keep the 256 compute
+ * units busy -- and a sequence spans more than one 256-key group; the
+ * single-pass kernel otherwise.  Both return the same bits. */
 int bi_decode_attention_choice(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax);
 
 bi_status bi_decode_attention_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Lmax,

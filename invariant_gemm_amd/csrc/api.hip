@@ -165,9 +165,11 @@ const char* bi_version(void) { return "libbigemm 0.1.0 gfx950"; }
 
 namespace {
 
-// Compute units of an MI355X: below this many (sequence, KV head) pairs the
-// single-pass kernel leaves compute units idle.
-constexpr int64_t kAttnSplitBelow = 256;
+// Below this many (sequence, KV head) pairs the single-pass kernel (one
+// workgroup per pair) leaves too many of the MI355X's 256 compute units idle
+// and the split-KV kernel is faster; measured crossover at 4096 keys between
+// 128 pairs (split faster) and 192 pairs (single pass faster).
+constexpr int64_t kAttnSplitBelow = 192;
 
 bi_status attn_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax, int64_t* G)
 {

@@ -35,6 +35,8 @@
 // product once the key order inside each 32-key block is permuted the same
 // way for P and V (V is read from LDS with the transposing ds_read_b64_tr_b16,
 // whose row addresses follow that permutation).
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -45,6 +47,7 @@ constexpr int kD = 128;                    // head dimension
 constexpr int kSub = 64;                   // keys per sub-chunk (one wave)
 constexpr int kGroup = 4 * kSub;           // keys per group (one workgroup)
 constexpr int kGmax = 16;                  // query heads per KV head, at most
+constexpr int64_t kSplitTarget = 512;      // split workgroups to aim for (2 per compute unit)
 constexpr int KP = kD * 2 + 16;            // LDS bytes per K / V row (padded)
 constexpr int kWaveLds = kSub * KP;        // one wave's V rows: 17408 B
 constexpr int kPartM = kGmax * kD;         // float offset of m in a sub-partial
@@ -198,15 +201,18 @@ __device__ __forceinline__ void fold_group(const float* const sp[4], int nsub, i
 // NW = 8, SPLIT = false: grid B*Hkv; one workgroup per (sequence, KV head)
 //     walks its groups two at a time (waves 0-3: group 2i, waves 4-7: group
 //     2i+1) and merges them into its running state in order; writes O.
-// NW = 4, SPLIT = true: grid B*Hkv*ngm; one workgroup per (sequence, KV
-//     head, group) writes that group's state to ws.
+// NW = 4, SPLIT = true: grid B*Hkv*ceil(ngm/gpw); one workgroup per
+//     (sequence, KV head, run of gpw consecutive groups) walks its groups one
+//     at a time and writes each group's state to ws.  gpw only decides which
+//     workgroup computes a group, never how.
 // Each wave owns a sub-chunk: its K rows go from memory straight into MFMA
 // operand registers, its V rows through registers into its LDS slot (then
 // the slot holds the wave's sub-partial for the fold).  The next sub-chunk's
 // loads are issued as soon as the registers they land in are free.
 template <int NW, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
-    int Hq, int Hkv, int G, int Lmax, int ngm,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_decode_kernel(
+    int Hq, int Hkv, int G, int Lmax, int ngm, int gpw,
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const int32_t* __restrict__ lens, float c,
     uint16_t* __restrict__ O, float* __restrict__ ws)
@@ -223,13 +229,14 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
     const int half = wave >> 2;                  // which group of the step
     const int wsub = wave & 3;                   // which sub-chunk of the group
 
-    const int bh = SPLIT ? (int)(blockIdx.x / ngm) : (int)blockIdx.x;
+    const int wps = SPLIT ? (ngm + gpw - 1) / gpw : 1;     // workgroups per (sequence, KV head)
+    const int bh = (int)(blockIdx.x / wps);
     const int b = bh / Hkv;
     const int kvh = bh - b * Hkv;
     const int L = min(max(lens[b], 0), Lmax);
     const int ng = (L + kGroup - 1) / kGroup;
-    int t = SPLIT ? (int)(blockIdx.x - (unsigned)bh * ngm) : 0;
-    const int t_end = SPLIT ? t + 1 : ng;
+    int t = SPLIT ? (int)(blockIdx.x - (unsigned)bh * wps) * gpw : 0;
+    const int t_end = SPLIT ? min(t + gpw, ng) : ng;
     if (SPLIT && t >= ng)
         return;
 
@@ -283,7 +290,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             *reinterpret_cast<u32x4*>(vl + (4 * r + lg) * KP + 16 * li) = vr[r];
-        const bool more = !SPLIT && t + GPS < t_end;
+        const bool more = t + GPS < t_end;
         if (more)
             load_v(t + GPS);
 
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_kernel(
                 f32x4 go;
                 fold_group(sp, nsub, e, h, gm, gl, go);
                 if constexpr (SPLIT) {
-                    float* dst = ws + ((int64_t)bh * ngm + t) * stride;
+                    float* dst = ws + ((int64_t)bh * ngm + t + gi) * stride;
                     *reinterpret_cast<f32x4*>(dst + e) = go;
                     if ((e & (kD - 1)) == 0) {
                         dst[n_el + h] = gm;
@@ -428,14 +435,20 @@ hipError_t launch_attn_decode(const AttnArgs& a, bool split, hipStream_t stream)
     const int64_t bh = a.B * a.Hkv;
     if (!split) {
         hipLaunchKernelGGL((attn_decode_kernel<8, false>), dim3((unsigned)bh), dim3(512), 0, stream,
-                           (int)a.Hq, (int)a.Hkv, (int)a.G, (int)a.Lmax, ngm, a.Q, a.K, a.V,
+                           (int)a.Hq, (int)a.Hkv, (int)a.G, (int)a.Lmax, ngm, 1, a.Q, a.K, a.V,
                            a.lens, a.c, a.O, nullptr);
         return hipGetLastError();
     }
     if (ngm > 0) {
-        hipLaunchKernelGGL((attn_decode_kernel<4, true>), dim3((unsigned)(bh * ngm)), dim3(256), 0,
-                           stream, (int)a.Hq, (int)a.Hkv, (int)a.G, (int)a.Lmax, ngm, a.Q, a.K,
-                           a.V, a.lens, a.c, a.O, a.ws);
+        // groups per workgroup: one while the groups alone leave compute
+        // units without two workgroups each, more (walked with prefetch)
+        // once they do
+        const int64_t groups = bh * ngm;
+        const int gpw = (int)std::min<int64_t>(std::max<int64_t>(groups / kSplitTarget, 1), ngm);
+        const int64_t wps = (ngm + gpw - 1) / gpw;
+        hipLaunchKernelGGL((attn_decode_kernel<4, true>), dim3((unsigned)(bh * wps)), dim3(256), 0,
+                           stream, (int)a.Hq, (int)a.Hkv, (int)a.G, (int)a.Lmax, ngm, gpw, a.Q,
+                           a.K, a.V, a.lens, a.c, a.O, a.ws);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
