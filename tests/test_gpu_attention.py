@@ -108,6 +108,22 @@ def test_single_and_split_are_bit_identical():
         assert np.array_equal(a, b), f"trial {trial}: B={B} G={G} Hkv={Hkv} Lmax={Lmax}"
 
 
+def test_split_runs_of_groups_with_ragged_lengths():
+    # 40 sequences x 8 KV heads x 8 groups = 2560 groups: the split kernel gives
+    # each workgroup a run of 5 consecutive groups (walked with prefetch), so
+    # runs end inside and past ragged lengths; bits must not change
+    Hq, Hkv, Lmax = 32, 8, 2048
+    lens = inputs.seq_lens(40, Lmax, 4500, lo=0)
+    lens[:4] = [0, 1, 1280, 1281]                    # empty, tiny, run boundaries
+    Q, K, V = _case(40, Hq, Hkv, Lmax, 4501, lens)
+    a = _run(Q, K, V, lens, 0.1, "split")
+    assert np.array_equal(a, _run(Q, K, V, lens, 0.1, "single"))
+    for b in (1, 2, 3, 20):
+        alone = _run(Q[b:b + 1], K[b:b + 1], V[b:b + 1], lens[b:b + 1], 0.1, "split")
+        assert np.array_equal(alone[0], a[b]), f"sequence {b}"
+    _check_parity(a, Q, K, V, lens, 0.1, seqs=[0, 1, 2, 3, 20])
+
+
 def test_batch_invariance_across_batch_size_position_and_kernel():
     # a pool of 40 sequences, computed as one batch (the library picks the
     # single-pass kernel: 320 (sequence, KV head) pairs), each alone (it picks
