@@ -21,6 +21,12 @@
 // beyond that count only load.  With a single 16 x 16 block (small M) all
 // waves still stream weights for it, which keeps enough bytes in flight per
 // compute unit when N/16 is below the compute unit count.
+//
+// HALF (small M only): a workgroup owns 8 of a block's 16 columns, so N/8
+// workgroups share the weights.  It loads only those columns' bytes; MFMA
+// output columns are independent, so the block's other 8 columns are fed
+// the same bytes again and simply not stored -- each stored column sees
+// exactly the operands, K order and scales of the full-block path.
 #include "common.h"
 #include "launch.h"
 
@@ -30,7 +36,7 @@ namespace {
 constexpr int KBK = 128;       // K per scale block = one MFMA
 constexpr int BTILE = 2048;    // packed bytes per (column block, K block)
 
-template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF>
+template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool HALF>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     int M, int N, int K,
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t ldsa,
@@ -41,7 +47,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     constexpr int BM = 16 * RB;
     constexpr int CPR = KB_ST * 8;                    // 16-byte A chunks per row per stage
     constexpr int A_BYTES = BM * KB_ST * KBK;
-    constexpr int B_BYTES = CB * KB_ST * BTILE;
+    constexpr int B_BYTES = CB * KB_ST * BTILE / (HALF ? 2 : 1);
+    static_assert(!HALF || (RB == 1 && CB == 1 && WR == 1 && WC == 1), "half blocks: one 16-row block");
     constexpr int A_LD = A_BYTES / (NTHR * 16);
     constexpr int B_LD = B_BYTES / (NTHR * 16);
     constexpr int SA_N = BM * KB_ST;
@@ -62,8 +69,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = xcd_remap(blockIdx.x, gridDim.x);
-    const int nt = tile / m_tiles;
-    const int mt = tile - nt * m_tiles;
+    const int ntile = tile / m_tiles;
+    const int mt = tile - ntile * m_tiles;
+    const int nt = HALF ? ntile >> 1 : ntile;          // column tile
+    const int ch = HALF ? ntile & 1 : 0;               // which 8 columns of the block
     const int m0 = mt * BM;
     const int NB = (N + 15) >> 4;
     const int nkb = K / KBK;
@@ -89,13 +98,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     // A_BYTES + 16u.  A run holds a whole number of waves' chunks, so c is
     // the same for all lanes of a wave: computed from the wave index it stays
     // in scalar registers, and so does the buffer resource built from it.
+    // HALF: chunk u = (K block q, half h, lane group g, column i8) of the 8
+    // columns, taken from lane 16g + 8ch + i8 of the packed tile.
     uint32_t b_voff[B_LD];
     int b_cb[B_LD];
 #pragma unroll
     for (int j = 0; j < B_LD; ++j) {
         const int u = j * NTHR + tid;
-        b_cb[j] = (j * NTHR + 64 * wave) / (KB_ST * 128);
-        b_voff[j] = (uint32_t)((u % (KB_ST * 128)) * 16);
+        if constexpr (HALF) {
+            b_cb[j] = 0;
+            const int q = u >> 6, r = u & 63;
+            b_voff[j] = (uint32_t)(q * BTILE + (r >> 5) * 1024 + (16 * ((r >> 3) & 3) + 8 * ch + (r & 7)) * 16);
+        } else {
+            b_cb[j] = (j * NTHR + 64 * wave) / (KB_ST * 128);
+            b_voff[j] = (uint32_t)((u % (KB_ST * 128)) * 16);
+        }
     }
     // Every load below is issued unconditionally, in the same order in every
     // stage, so the compiler's wait counts keep PF stages in flight (a
@@ -217,9 +234,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
                     i32x8 bv[WC];
 #pragma unroll
                     for (int c = 0; c < WC; ++c) {
-                        const uint8_t* bt = buf + A_BYTES + ((wc0 + c) * KB_ST + q) * BTILE + lane * 16;
+                        const uint8_t* bt = HALF
+                            ? buf + A_BYTES + (q * 64 + 8 * lg + (li & 7)) * 16
+                            : buf + A_BYTES + ((wc0 + c) * KB_ST + q) * BTILE + lane * 16;
                         const u32x4 b0 = *reinterpret_cast<const u32x4*>(bt);
-                        const u32x4 b1 = *reinterpret_cast<const u32x4*>(bt + 1024);
+                        const u32x4 b1 = *reinterpret_cast<const u32x4*>(bt + (HALF ? 512 : 1024));
                         bv[c] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
                                       (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
                     }
@@ -264,13 +283,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     if (computes) {
 #pragma unroll
         for (int c = 0; c < WC; ++c) {
-            const int col = 16 * (nbw + wc0 + c) + li;
+            const int col = HALF ? 16 * nbw + 8 * ch + li : 16 * (nbw + wc0 + c) + li;
 #pragma unroll
             for (int r = 0; r < WR; ++r) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = m0 + 16 * (wr0 + r) + 4 * lg + j;
-                    if (row < M && col < N)
+                    if (row < M && col < N && (!HALF || li < 8))
                         C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[r][c][j]);
                 }
             }
@@ -307,12 +326,12 @@ __global__ void pack_fp8_kernel(int N, int K, const uint8_t* __restrict__ B, int
     *reinterpret_cast<u32x4*>(Bp + u * 16) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF>
+template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool HALF = false>
 hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 {
-    const int n_tiles = ((a.N + 15) / 16 + CB - 1) / CB;
+    const int n_tiles = ((a.N + 15) / 16 + CB - 1) / CB * (HALF ? 2 : 1);
     const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-    gemm_fp8_packed_kernel<WAVES, RB, CB, WR, WC, KB_ST, PF>
+    gemm_fp8_packed_kernel<WAVES, RB, CB, WR, WC, KB_ST, PF, HALF>
         <<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0, stream>>>(
             a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
             (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles);
@@ -325,7 +344,8 @@ hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 // per-element arithmetic).  64 x 64 tiles once they still give each compute
 // unit a workgroup, 64 x 32 above 128 rows, 64 x 16 (eight waves) from 17
 // rows, and for M <= 16 one 16 x 16 block per workgroup with eight waves
-// streaming its weights.
+// streaming its weights -- or, while N/16 blocks would leave compute units
+// without a workgroup, half a block (8 columns, four waves) per workgroup.
 int fp8_packed_geometry(int M, int N)
 {
     const int nb = (N + 15) / 16;
@@ -336,6 +356,8 @@ int fp8_packed_geometry(int M, int N)
         return 2;                                  // 64 x 32
     if (M > 16)
         return 1;                                  // 64 x 16
+    if (nb < 256)
+        return 4;                                  // 16 x 8: N/8 workgroups
     return 0;                                      // 16 x 16
 }
 
@@ -345,6 +367,7 @@ hipError_t launch_fp8_packed(const GemmArgs& a, hipStream_t stream)
     case 3: return launch_geometry<4, 4, 4, 2, 2, 2, 2>(a, stream);
     case 2: return launch_geometry<4, 4, 2, 2, 1, 2, 4>(a, stream);
     case 1: return launch_geometry<8, 4, 1, 1, 1, 4, 4>(a, stream);
+    case 4: return launch_geometry<4, 1, 1, 1, 1, 8, 4, true>(a, stream);
     default: return launch_geometry<8, 1, 1, 1, 1, 8, 4>(a, stream);
     }
 }

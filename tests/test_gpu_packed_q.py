@@ -39,9 +39,11 @@ def fp8_case(M, N, K, seed):
     return qA, sA, qB, sB
 
 
-# M values cover every launch geometry: 16, 32, 48 and 64 rows x 16 columns,
-# then 64 x 32 and 64 x 64 tiles once they still fill the compute units.
-@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (5, 300, 384), (17, 144, 1024), (40, 272, 512),
+# M values cover every launch geometry: 16 rows x 8 columns (N < 4096) or
+# x 16 columns, then 64 x 16, 64 x 32 and 64 x 64 tiles once they still fill
+# the compute units.
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (5, 300, 384), (3, 4112, 256), (16, 4096, 128),
+                                   (17, 144, 1024), (40, 272, 512),
                                    (64, 2048, 896), (200, 2048, 1024), (512, 2048, 512),
                                    (129, 4112, 256)])
 def test_fp8_packed_bitwise_equal_to_unpacked(bg, M, N, K):
