@@ -535,6 +535,32 @@ def attention_probe(torch, bg, L=4096, Hq=64, Hkv=8):
     log("probe: 3 x split B=1 done")
 
 
+def vendor_matmul(torch, packed_us, rounds, K=8192, N=8192):
+    """Context only, not batch-invariant: torch.matmul (hipBLASLt) on the
+    headline shape, weights rotated over HBM copies as in the headline, next
+    to the packed invariant kernel's time at the same M."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20262)
+    nb = max(2, -(-ROT_BYTES // (K * N * 2)))
+    Bs = [(torch.randn((K, N), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+          for _ in range(nb)]
+    res = {}
+    for M in SWEEP_C2:
+        A = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        i = [0]
+
+        def fn():
+            torch.matmul(A, Bs[i[0] % nb], out=C)
+            i[0] += 1
+        med, _ = time_launches(torch, fn, reps=nb * 2, rounds=max(3, rounds // 2))
+        res[str(M)] = {"us": round(med, 2), "tflops": round(flops(M, N, K) / med / 1e6, 2),
+                       "packed_invariant_over_vendor_time": round(packed_us[str(M)] / med, 3)}
+    del Bs
+    torch.cuda.empty_cache()
+    return res
+
+
 def replay(torch, bg, inputs, steps=1000):
     """Dynamic-batching replay on the bf16 projection shape: pool of 4096 rows,
     `steps` batches of 1..256 distinct rows; GPU time of the GEMM launches."""
@@ -686,6 +712,7 @@ def main():
                                round(out["bf16_rowmajor_K8192_N8192"][str(M)]["us"] / med, 3),
                            "packed_invariant_over_splitk_time": round(packed_us[str(M)] / med, 3)}
         out["splitk_gap"] = gap
+        out["vendor_matmul_bf16_K8192_N8192"] = vendor_matmul(torch, packed_us, args.rounds)
         del ws
         del c2
         c2t = C2T(torch, bigemm, inputs)
