@@ -34,7 +34,8 @@
 // probabilities of one head for 8 keys -- exactly an A operand of the P . V
 // product once the key order inside each 32-key block is permuted the same
 // way for P and V (V is read from LDS with the transposing ds_read_b64_tr_b16,
-// whose row addresses follow that permutation).
+// whose row addresses follow that permutation).  K and V are read once per
+// call and loaded non-temporal.
 #include <algorithm>
 
 #include "common.h"
@@ -265,13 +266,13 @@ void attn_decode_kernel(
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                ka[4 * tt + ks] = buf_load16(rk, off0 + tt * 16 * (kD * 2) + 64 * ks);
+                ka[4 * tt + ks] = buf_load16_nt(rk, off0 + tt * 16 * (kD * 2) + 64 * ks);
     };
     auto load_v = [&](int grp) {
         const uint32_t off0 = sub_off(grp) + lane * 16;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            vr[r] = buf_load16(rv, off0 + r * 1024);
+            vr[r] = buf_load16_nt(rv, off0 + r * 1024);
     };
     if (t < t_end) {
         load_k(t);

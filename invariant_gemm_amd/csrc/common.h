@@ -87,6 +87,14 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
+// The same load marked non-temporal (gfx950 cache policy "nt"): for data
+// read exactly once -- streamed weights, a KV cache -- so it does not
+// displace reused lines.  Only the caching changes, never the value.
+__device__ __forceinline__ u32x4 buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 2));
+}
+
 // Byte extent clamp for a buffer resource.
 __device__ __forceinline__ uint32_t clamp_bytes(int64_t b)
 {

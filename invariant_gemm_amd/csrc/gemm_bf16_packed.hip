@@ -25,6 +25,8 @@
 //   large     : 4 waves x 2 column blocks, BM = 64 -- B fragments reused over
 //               four row blocks, A fragments over two column blocks.
 // None changes the K order, the MFMA or the epilogue of any element.
+// Weight loads are marked non-temporal (read once) except in the large
+// geometry, whose four row tiles share each column strip through L2.
 #include "common.h"
 #include "launch.h"
 
@@ -53,7 +55,7 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
 // offsets, and slots past the last tile exit at once.  A row's arithmetic is
 // the same as in the ungrouped kernel, so it does not depend on how many rows
 // the other groups -- or its own group -- hold.
-template <int WAVES, int CB, int RB, int KS_ST, int PF, bool GROUPED>
+template <int WAVES, int CB, int RB, int KS_ST, int PF, bool GROUPED, bool NT>
 __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
     int M, int N, int K,
     const uint16_t* __restrict__ A, int64_t lda,
@@ -143,7 +145,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
                 live && nb < NB ? clamp_bytes((int64_t)(KS - ks0) * 1024) : 0u);
 #pragma unroll
             for (int ks = 0; ks < KS_ST; ++ks)
-                br[ks][c] = buf_load16(rb, (uint32_t)(ks * 1024 + lane * 16));
+                br[ks][c] = NT ? buf_load16_nt(rb, (uint32_t)(ks * 1024 + lane * 16))
+                               : buf_load16(rb, (uint32_t)(ks * 1024 + lane * 16));
         }
     };
 
@@ -236,7 +239,7 @@ __global__ void pack_b_bf16_kernel(int N, int K, const uint16_t* __restrict__ B,
     *reinterpret_cast<u32x4*>(Bp + q * 16) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <int WAVES, int CB, int RB, int KS_ST, int PF>
+template <int WAVES, int CB, int RB, int KS_ST, int PF, bool NT = true>
 hipError_t launch_geometry(const GemmArgs& a, const GroupArgs* grp, hipStream_t stream)
 {
     const int n_tiles = ((a.N + 15) / 16 + WAVES * CB - 1) / (WAVES * CB);
@@ -244,12 +247,12 @@ hipError_t launch_geometry(const GemmArgs& a, const GroupArgs* grp, hipStream_t 
     if (grp) {
         // row slots: every group adds at most one partial tile
         const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB) + grp->n_groups;
-        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, true><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
+        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, true, NT><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
             a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles,
             grp->offsets, grp->n_groups, grp->b_stride);
     } else {
         const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, false><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
+        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, false, NT><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
             a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles,
             nullptr, 0, 0);
     }
@@ -286,7 +289,7 @@ namespace {
 hipError_t launch_packed(const GemmArgs& a, const GroupArgs* grp, int geometry, hipStream_t stream)
 {
     switch (geometry) {
-    case 4: return launch_geometry<4, 2, 4, 4, 4>(a, grp, stream);
+    case 4: return launch_geometry<4, 2, 4, 4, 4, false>(a, grp, stream);   // B strips shared by 4 row tiles
     case 3: return launch_geometry<4, 1, 4, 4, 4>(a, grp, stream);
     case 2: return launch_geometry<2, 1, 4, 4, 4>(a, grp, stream);
     case 1: return launch_geometry<2, 1, 2, 8, 2>(a, grp, stream);

@@ -15,6 +15,9 @@
 // unpacked entry point; rows independent of M, position and companions.
 // Launch geometries: streaming (2 waves x 16 columns, BM 16), medium
 // (4 waves x 16 columns, BM 64), large (4 waves x 32 columns, BM 64).
+//
+// Weight codes and scales are read once and loaded non-temporal, except in
+// the largest-M geometry, whose row tiles share each column strip.
 #include "common.h"
 #include "launch.h"
 
@@ -38,7 +41,7 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t q)
 
 // WAVES waves; wave w owns column blocks nb0 + w*CB .. +CB-1; RB row blocks.
 // Stage = QS 128-K groups (4*QS K steps).
-template <int WAVES, int CB, int RB, int QS, int PF>
+template <int WAVES, int CB, int RB, int QS, int PF, bool NT>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     int M, int N, int K,
     const uint16_t* __restrict__ A, int64_t lda,
@@ -112,8 +115,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                 scales + ((int64_t)nb * KQ + q0) * 64, ok ? clamp_bytes((int64_t)(KQ - q0) * 64) : 0u);
 #pragma unroll
             for (int q = 0; q < QS; ++q) {
-                qr[q][c] = buf_load16(rq, (uint32_t)(q * 1024 + lane * 16));
-                sr[q][c] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(q * 64 + li * 4), 0, 0);
+                qr[q][c] = NT ? buf_load16_nt(rq, (uint32_t)(q * 1024 + lane * 16))
+                              : buf_load16(rq, (uint32_t)(q * 1024 + lane * 16));
+                sr[q][c] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(q * 64 + li * 4), 0, NT ? 2 : 0);
             }
         }
     };
@@ -288,12 +292,12 @@ __global__ void pack_fp4_kernel(int N, int K, const uint8_t* __restrict__ Bq, in
     }
 }
 
-template <int WAVES, int CB, int RB, int QS, int PF>
+template <int WAVES, int CB, int RB, int QS, int PF, bool NT = true>
 hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 {
     const int n_tiles = ((a.N + 15) / 16 + WAVES * CB - 1) / (WAVES * CB);
     const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-    gemm_fp4_packed_kernel<WAVES, CB, RB, QS, PF><<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0,
+    gemm_fp4_packed_kernel<WAVES, CB, RB, QS, PF, NT><<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0,
                                                     stream>>>(
         a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
     return hipGetLastError();
@@ -309,7 +313,7 @@ hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream)
     const int nb = (a.N + 15) / 16;
     const int mt64 = (a.M + 63) / 64;
     if (a.M >= 64 && mt64 * ((nb + 7) / 8) >= 256)
-        return launch_geometry<4, 2, 4, 1, 2>(a, stream);
+        return launch_geometry<4, 2, 4, 1, 2, false>(a, stream);   // weights shared by row tiles
     if (a.M > 16)
         return launch_geometry<4, 1, 4, 1, 4>(a, stream);
     return launch_geometry<2, 1, 1, 2, 4>(a, stream);

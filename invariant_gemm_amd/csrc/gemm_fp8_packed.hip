@@ -27,6 +27,7 @@
 // output columns are independent, so the block's other 8 columns are fed
 // the same bytes again and simply not stored -- each stored column sees
 // exactly the operands, K order and scales of the full-block path.
+// Weight bytes are read once and loaded non-temporal.
 #include "common.h"
 #include "launch.h"
 
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(
                 Bp + ((int64_t)nb * nkb + kb0) * BTILE,
                 live && nb < NB ? clamp_bytes((int64_t)(nkb - kb0) * BTILE) : 0u);
-            br[j] = buf_load16(rb, b_voff[j]);
+            br[j] = buf_load16_nt(rb, b_voff[j]);
         }
 #pragma unroll
         for (int j = 0; j < SA_LD; ++j)

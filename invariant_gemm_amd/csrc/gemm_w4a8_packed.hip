@@ -25,6 +25,9 @@
 // column 16nb + i at k = 128kb + 32g + j, code j in byte j/2 (even j in the
 // low nibble).  Scales: 64-byte tile (nb, kb) at byte NB*KB*1024 +
 // (nb*KB + kb)*64, byte l = sE[4kb + g][16nb + i].  Zero past N.
+//
+// Weight codes and scales are read once and loaded non-temporal, except in
+// the largest-M geometry, whose row tiles share each column strip.
 #include "common.h"
 #include "launch.h"
 
@@ -35,7 +38,7 @@ constexpr int KBK = 128;       // K per MFMA (and per activation scale)
 constexpr int CTILE = 1024;    // code bytes per (column block, K block)
 constexpr int STILE = 64;      // scale bytes per (column block, K block)
 
-template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF>
+template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool NT>
 __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
     int M, int N, int K,
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t ldsa,
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
             const __amdgpu_buffer_rsrc_t rb = make_rsrc(
                 Bp + ((int64_t)nb * nkb + kb0) * CTILE,
                 live && nb < NB ? clamp_bytes((int64_t)(nkb - kb0) * CTILE) : 0u);
-            br[j] = buf_load16(rb, b_voff[j]);
+            br[j] = NT ? buf_load16_nt(rb, b_voff[j]) : buf_load16(rb, b_voff[j]);
         }
 #pragma unroll
         for (int j = 0; j < SA_LD; ++j)
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
         // blocks past K of a live stage read the next column's scales (or
         // nothing, past the region); the K-tail code below clears them
         const uint32_t off = sc_voff + (uint32_t)(kb0 * STILE);
-        scr = __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)off, 0, 0);
+        scr = __builtin_amdgcn_raw_buffer_load_b32(rsc, (int)off, 0, NT ? 2 : 0);
     };
 
 #pragma unroll
@@ -305,12 +308,12 @@ __global__ void pack_mxfp4_kernel(int N, int K, const uint8_t* __restrict__ Bq, 
     Bp[(int64_t)NB * KB * CTILE + t * STILE + l] = n < N ? sE[(int64_t)(4 * kb + g) * ldse + n] : 0u;
 }
 
-template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF>
+template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool NT = true>
 hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 {
     const int n_tiles = ((a.N + 15) / 16 + CB - 1) / CB;
     const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-    gemm_w4a8_packed_kernel<WAVES, RB, CB, WR, WC, KB_ST, PF>
+    gemm_w4a8_packed_kernel<WAVES, RB, CB, WR, WC, KB_ST, PF, NT>
         <<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0, stream>>>(
             a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
             (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
@@ -327,7 +330,7 @@ hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream)
 {
     if (a.M > 128)
-        return launch_geometry<4, 4, 4, 2, 2, 1, 4>(a, stream);
+        return launch_geometry<4, 4, 4, 2, 2, 1, 4, false>(a, stream);   // weights shared by row tiles
     if (a.M > 16)
         return launch_geometry<4, 4, 4, 2, 2, 2, 2>(a, stream);
     return launch_geometry<4, 1, 4, 1, 1, 4, 4>(a, stream);
