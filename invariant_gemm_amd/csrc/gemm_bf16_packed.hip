@@ -15,10 +15,10 @@
 // its batch companions (the invariance definition in section
 // "什么是batch invariance" of the QbitAI article).
 //
-// Three launch geometries share that arithmetic (the dual-program idea of
-// section 4.1 of the lshu.cn article and section 3.3 of the wmrh.cn blog,
-// applied to the GEMM: programs for "GPU not saturated" / "saturated" whose
-// results are bit-identical):
+// Five launch geometries in three families share that arithmetic (the
+// dual-program idea of section 4.1 of the lshu.cn article and section 3.3 of
+// the wmrh.cn blog, applied to the GEMM: programs for "GPU not saturated" /
+// "saturated" whose results are bit-identical):
 //   streaming : 2 waves x 1 column block, BM = 16, 32 or 64 -- N/32
 //               workgroups stream B;
 //   medium    : 4 waves x 1 column block, BM = 64;
