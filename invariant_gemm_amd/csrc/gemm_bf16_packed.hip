@@ -15,18 +15,21 @@
 // its batch companions (the invariance definition in section
 // "什么是batch invariance" of the QbitAI article).
 //
-// Five launch geometries in three families share that arithmetic (the
+// Six launch geometries in three families share that arithmetic (the
 // dual-program idea of section 4.1 of the lshu.cn article and section 3.3 of
 // the wmrh.cn blog, applied to the GEMM: programs for "GPU not saturated" /
 // "saturated" whose results are bit-identical):
 //   streaming : 2 waves x 1 column block, BM = 16, 32 or 64 -- N/32
-//               workgroups stream B;
+//               workgroups stream B (1 wave, N/16 workgroups, for small N
+//               and M <= 16);
 //   medium    : 4 waves x 1 column block, BM = 64;
 //   large     : 4 waves x 2 column blocks, BM = 64 -- B fragments reused over
 //               four row blocks, A fragments over two column blocks.
 // None changes the K order, the MFMA or the epilogue of any element.
 // Weight loads are marked non-temporal (read once) except in the large
 // geometry, whose four row tiles share each column strip through L2.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -267,7 +270,8 @@ hipError_t launch_geometry(const GemmArgs& a, const GroupArgs* grp, hipStream_t 
 // the output tiles are shared among workgroups.  The largest tile that still
 // yields a workgroup per compute unit wins; below that, the streaming
 // geometry (one 16-row block, two 16-column waves) covers N with N/32
-// workgroups.
+// workgroups -- or, for up to 16 rows while N/32 workgroups would leave
+// compute units idle, one wave per 16 columns (N/16 workgroups).
 int packed_geometry(int M, int N)
 {
     const int nb = (N + 15) / 16;
@@ -281,6 +285,8 @@ int packed_geometry(int M, int N)
         return 2;                                           // streaming, BM 64
     if (M > 16)
         return 1;                                           // streaming, BM 32
+    if ((nb + 1) / 2 < 256)
+        return 5;                                           // streaming, BM 16, one wave
     return 0;                                               // streaming, BM 16
 }
 
@@ -293,6 +299,7 @@ hipError_t launch_packed(const GemmArgs& a, const GroupArgs* grp, int geometry, 
     case 3: return launch_geometry<4, 1, 4, 4, 4>(a, grp, stream);
     case 2: return launch_geometry<2, 1, 4, 4, 4>(a, grp, stream);
     case 1: return launch_geometry<2, 1, 2, 8, 2>(a, grp, stream);
+    case 5: return launch_geometry<1, 1, 1, 16, 2>(a, grp, stream);
     default: return launch_geometry<2, 1, 1, 8, 4>(a, grp, stream);
     }
 }
@@ -305,11 +312,17 @@ hipError_t launch_bf16_packed(const GemmArgs& a, hipStream_t stream)
 }
 
 // Grouped launch: the geometry follows the mean rows per group (any choice
-// gives the same bits).
+// gives the same bits).  The one-wave streaming geometry only pays while the
+// groups that can hold rows -- at most min(groups, M) -- leave compute units
+// idle with two-wave workgroups.
 hipError_t launch_bf16_grouped_packed(const GemmArgs& a, const GroupArgs& g, hipStream_t stream)
 {
     const int mean = (a.M + g.n_groups - 1) / g.n_groups;
-    return launch_packed(a, &g, packed_geometry(mean > 0 ? mean : 1, a.N), stream);
+    int geometry = packed_geometry(mean > 0 ? mean : 1, a.N);
+    const int64_t active = std::min<int64_t>(g.n_groups, a.M);
+    if (geometry == 5 && active * ((a.N + 31) / 32) >= 256)
+        geometry = 0;
+    return launch_packed(a, &g, geometry, stream);
 }
 
 hipError_t launch_pack_b_bf16(int N, int K, const uint16_t* B, int64_t ldb, uint8_t* Bp,
