@@ -48,7 +48,7 @@ constexpr int kD = 128;                    // head dimension
 constexpr int kSub = 64;                   // keys per sub-chunk (one wave)
 constexpr int kGroup = 4 * kSub;           // keys per group (one workgroup)
 constexpr int kGmax = 16;                  // query heads per KV head, at most
-constexpr int64_t kSplitTarget = 512;      // split workgroups to aim for (2 per compute unit)
+constexpr int64_t kSplitTarget = 2048;     // split workgroups before runs of groups (measured)
 constexpr int KP = kD * 2 + 16;            // LDS bytes per K / V row (padded)
 constexpr int kWaveLds = kSub * KP;        // one wave's V rows: 17408 B
 constexpr int kPartM = kGmax * kD;         // float offset of m in a sub-partial
@@ -441,9 +441,10 @@ hipError_t launch_attn_decode(const AttnArgs& a, bool split, hipStream_t stream)
         return hipGetLastError();
     }
     if (ngm > 0) {
-        // groups per workgroup: one while the groups alone leave compute
-        // units without two workgroups each, more (walked with prefetch)
-        // once they do
+        // groups per workgroup: one up to 2048 groups (eight workgroups per
+        // compute unit), then runs of consecutive groups walked with the
+        // next group prefetched; measured, one group per workgroup is the
+        // faster choice below that
         const int64_t groups = bh * ngm;
         const int gpw = (int)std::min<int64_t>(std::max<int64_t>(groups / kSplitTarget, 1), ngm);
         const int64_t wps = (ngm + gpw - 1) / gpw;

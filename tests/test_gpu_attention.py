@@ -109,19 +109,19 @@ def test_single_and_split_are_bit_identical():
 
 
 def test_split_runs_of_groups_with_ragged_lengths():
-    # 40 sequences x 8 KV heads x 8 groups = 2560 groups: the split kernel gives
-    # each workgroup a run of 5 consecutive groups (walked with prefetch), so
+    # 16 sequences x 16 KV heads x 16 groups = 4096 groups: the split kernel gives
+    # each workgroup a run of 2 consecutive groups (walked with prefetch), so
     # runs end inside and past ragged lengths; bits must not change
-    Hq, Hkv, Lmax = 32, 8, 2048
-    lens = inputs.seq_lens(40, Lmax, 4500, lo=0)
-    lens[:4] = [0, 1, 1280, 1281]                    # empty, tiny, run boundaries
-    Q, K, V = _case(40, Hq, Hkv, Lmax, 4501, lens)
+    Hq, Hkv, Lmax = 32, 16, 4096
+    lens = inputs.seq_lens(16, Lmax, 4500, lo=0)
+    lens[:4] = [0, 1, 512, 513]                      # empty, tiny, run boundaries
+    Q, K, V = _case(16, Hq, Hkv, Lmax, 4501, lens)
     a = _run(Q, K, V, lens, 0.1, "split")
     assert np.array_equal(a, _run(Q, K, V, lens, 0.1, "single"))
-    for b in (1, 2, 3, 20):
+    for b in (1, 2, 3, 9):
         alone = _run(Q[b:b + 1], K[b:b + 1], V[b:b + 1], lens[b:b + 1], 0.1, "split")
         assert np.array_equal(alone[0], a[b]), f"sequence {b}"
-    _check_parity(a, Q, K, V, lens, 0.1, seqs=[0, 1, 2, 3, 20])
+    _check_parity(a, Q, K, V, lens, 0.1, seqs=[0, 1, 2, 3, 9])
 
 
 def test_batch_invariance_across_batch_size_position_and_kernel():
