@@ -25,7 +25,9 @@
 //   medium    : 4 waves x 1 column block, BM = 64;
 //   large     : 4 waves x 2 column blocks, BM = 64 -- B fragments reused over
 //               four row blocks, A fragments over two column blocks.
-// None changes the K order, the MFMA or the epilogue of any element.
+// None changes the K order, the MFMA or the epilogue of any element.  The
+// two 16-row streaming geometries stage only the first 4 or 8 rows of A when
+// the call has no more rows than that.
 // Weight loads are marked non-temporal (read once) except in the large
 // geometry, whose four row tiles share each column strip through L2.
 #include <algorithm>
@@ -58,7 +60,12 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
 // offsets, and slots past the last tile exit at once.  A row's arithmetic is
 // the same as in the ungrouped kernel, so it does not depend on how many rows
 // the other groups -- or its own group -- hold.
-template <int WAVES, int CB, int RB, int KS_ST, int PF, bool GROUPED, bool NT>
+//
+// Only the first AR rows of each A stage are loaded (AR = BM, or fewer when
+// no tile can hold more than AR rows): LDS rows past them keep stale values,
+// which reach only output rows that are never stored -- an MFMA output row
+// depends on its own A row alone.
+template <int WAVES, int CB, int RB, int KS_ST, int PF, bool GROUPED, bool NT, int AR>
 __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
     int M, int N, int K,
     const uint16_t* __restrict__ A, int64_t lda,
@@ -72,7 +79,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
     constexpr int CPR = BKS * 2 / 16;                 // 16-byte A chunks per row per stage
     constexpr int A_STAGE = BM * BKS * 2;
     constexpr int A_LD = A_STAGE / (NTHR * 16);
+    constexpr int A_LDU = (AR * CPR + NTHR - 1) / NTHR;   // loads that cover rows < AR
     static_assert(A_LD * NTHR * 16 == A_STAGE, "A stage must split evenly over the threads");
+    static_assert(AR >= 1 && AR <= BM, "staged rows must lie in the tile");
     static_assert(PF % 2 == 0, "the LDS double buffer is indexed by stage parity");
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * A_STAGE];
 
@@ -137,7 +146,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
             A + (int64_t)m0 * lda + kst,
             live ? clamp_bytes(((int64_t)(rows_valid - 1) * lda + kpad - kst) * 2) : 0u);
 #pragma unroll
-        for (int j = 0; j < A_LD; ++j)
+        for (int j = 0; j < A_LDU; ++j)
             ar[j] = buf_load16(ra, a_voff[j]);
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
@@ -168,14 +177,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
                 // K tail: A's row pitch past K may hold anything (packed B is
                 // already zero past K)
 #pragma unroll
-                for (int j = 0; j < A_LD; ++j) {
+                for (int j = 0; j < A_LDU; ++j) {
                     const int c = j * NTHR + tid;
                     const int kc = (c % CPR) ^ swz<CPR>(c / CPR);
                     areg[p][j] = keep_first(areg[p][j], K - (kst + 8 * kc));
                 }
             }
 #pragma unroll
-            for (int j = 0; j < A_LD; ++j)
+            for (int j = 0; j < A_LDU; ++j)
                 *reinterpret_cast<u32x4*>(abuf + (j * NTHR + tid) * 16) = areg[p][j];
             __syncthreads();
             // all A fragments of the stage first (their LDS latency overlaps),
@@ -242,7 +251,7 @@ __global__ void pack_b_bf16_kernel(int N, int K, const uint16_t* __restrict__ B,
     *reinterpret_cast<u32x4*>(Bp + q * 16) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <int WAVES, int CB, int RB, int KS_ST, int PF, bool NT = true>
+template <int WAVES, int CB, int RB, int KS_ST, int PF, bool NT = true, int AR = 16 * RB>
 hipError_t launch_geometry(const GemmArgs& a, const GroupArgs* grp, hipStream_t stream)
 {
     const int n_tiles = ((a.N + 15) / 16 + WAVES * CB - 1) / (WAVES * CB);
@@ -250,12 +259,12 @@ hipError_t launch_geometry(const GemmArgs& a, const GroupArgs* grp, hipStream_t 
     if (grp) {
         // row slots: every group adds at most one partial tile
         const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB) + grp->n_groups;
-        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, true, NT><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
+        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, true, NT, AR><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
             a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles,
             grp->offsets, grp->n_groups, grp->b_stride);
     } else {
         const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, false, NT><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
+        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, false, NT, AR><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
             a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles,
             nullptr, 0, 0);
     }
@@ -299,8 +308,15 @@ hipError_t launch_packed(const GemmArgs& a, const GroupArgs* grp, int geometry, 
     case 3: return launch_geometry<4, 1, 4, 4, 4>(a, grp, stream);
     case 2: return launch_geometry<2, 1, 4, 4, 4>(a, grp, stream);
     case 1: return launch_geometry<2, 1, 2, 8, 2>(a, grp, stream);
-    case 5: return launch_geometry<1, 1, 1, 16, 2>(a, grp, stream);
-    default: return launch_geometry<2, 1, 1, 8, 4>(a, grp, stream);
+    case 5:
+        // at most 4 or 8 rows in the call: stage only those rows of A
+        if (a.M <= 4) return launch_geometry<1, 1, 1, 16, 2, true, 4>(a, grp, stream);
+        if (a.M <= 8) return launch_geometry<1, 1, 1, 16, 2, true, 8>(a, grp, stream);
+        return launch_geometry<1, 1, 1, 16, 2>(a, grp, stream);
+    default:
+        if (a.M <= 4) return launch_geometry<2, 1, 1, 8, 4, true, 4>(a, grp, stream);
+        if (a.M <= 8) return launch_geometry<2, 1, 1, 8, 4, true, 8>(a, grp, stream);
+        return launch_geometry<2, 1, 1, 8, 4>(a, grp, stream);
     }
 }
 

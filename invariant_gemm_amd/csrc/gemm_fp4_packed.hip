@@ -41,7 +41,11 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t q)
 
 // WAVES waves; wave w owns column blocks nb0 + w*CB .. +CB-1; RB row blocks.
 // Stage = QS 128-K groups (4*QS K steps).
-template <int WAVES, int CB, int RB, int QS, int PF, bool NT>
+// Only the first AR rows of each A stage are loaded (AR = BM, or fewer when
+// the call has at most AR rows): LDS rows past them keep stale values, which
+// reach only output rows that are never stored -- an MFMA output row depends
+// on its own A row alone.
+template <int WAVES, int CB, int RB, int QS, int PF, bool NT, int AR>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     int M, int N, int K,
     const uint16_t* __restrict__ A, int64_t lda,
@@ -56,7 +60,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     constexpr int A_LD = A_STAGE / (NTHR * 16);
     // K steps per product group of the small-tile path: 4 or 2 steps
     constexpr int SG = RB * CB >= 2 ? 2 : 4;
+    constexpr int A_LDU = (AR * CPR + NTHR - 1) / NTHR;   // loads that cover rows < AR
     static_assert(A_LD * NTHR * 16 == A_STAGE, "A stage must split evenly over the threads");
+    static_assert(AR >= 1 && AR <= BM, "staged rows must lie in the tile");
     static_assert(PF % 2 == 0, "the LDS double buffer is indexed by stage parity");
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * A_STAGE];
 
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
             A + (int64_t)m0 * lda + kst,
             live ? clamp_bytes(((int64_t)(rows_valid - 1) * lda + K - kst) * 2) : 0u);
 #pragma unroll
-        for (int j = 0; j < A_LD; ++j)
+        for (int j = 0; j < A_LDU; ++j)
             ar[j] = buf_load16(ra, a_voff[j]);
 #pragma unroll
         for (int c = 0; c < CB; ++c) {
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                 // K tail (K % 32 == 0): zero A chunks at k >= K -- the row pitch
                 // may hold anything there; packed codes and scales are zero
 #pragma unroll
-                for (int j = 0; j < A_LD; ++j) {
+                for (int j = 0; j < A_LDU; ++j) {
                     const int c = j * NTHR + tid;
                     const int kc = (c % CPR) ^ swz<CPR>(c / CPR);
                     if (kst + 8 * kc >= K)
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                 }
             }
 #pragma unroll
-            for (int j = 0; j < A_LD; ++j)
+            for (int j = 0; j < A_LDU; ++j)
                 *reinterpret_cast<u32x4*>(abuf + (j * NTHR + tid) * 16) = areg[p][j];
             __syncthreads();
             if constexpr (RB * CB <= 2) {
@@ -292,12 +298,12 @@ __global__ void pack_fp4_kernel(int N, int K, const uint8_t* __restrict__ Bq, in
     }
 }
 
-template <int WAVES, int CB, int RB, int QS, int PF, bool NT = true>
+template <int WAVES, int CB, int RB, int QS, int PF, bool NT = true, int AR = 16 * RB>
 hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 {
     const int n_tiles = ((a.N + 15) / 16 + WAVES * CB - 1) / (WAVES * CB);
     const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-    gemm_fp4_packed_kernel<WAVES, CB, RB, QS, PF, NT><<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0,
+    gemm_fp4_packed_kernel<WAVES, CB, RB, QS, PF, NT, AR><<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0,
                                                     stream>>>(
         a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
     return hipGetLastError();
@@ -307,7 +313,8 @@ hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 
 // Launch geometry (tile sharing only: the per-element arithmetic is the same
 // for all): 64 x 128 tiles once they still give each compute unit a
-// workgroup, 64 x 64 from 17 rows, else two waves of 16 x 16 streaming.
+// workgroup, 64 x 64 from 17 rows, else two waves of 16 x 16 streaming that
+// stage only the first 4 or 8 rows of A when the call has no more.
 hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream)
 {
     const int nb = (a.N + 15) / 16;
@@ -316,6 +323,11 @@ hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream)
         return launch_geometry<4, 2, 4, 1, 2, false>(a, stream);   // weights shared by row tiles
     if (a.M > 16)
         return launch_geometry<4, 1, 4, 1, 4>(a, stream);
+    // at most 4 or 8 rows: stage only those rows of A
+    if (a.M <= 4)
+        return launch_geometry<2, 1, 1, 2, 4, true, 4>(a, stream);
+    if (a.M <= 8)
+        return launch_geometry<2, 1, 1, 2, 4, true, 8>(a, stream);
     return launch_geometry<2, 1, 1, 2, 4>(a, stream);
 }
 

@@ -108,7 +108,8 @@ def fp4_run(bg, A, Bq, sB, N):
     return got, ref
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 32, 32), (3, 130, 288), (17, 256, 512), (33, 96, 320),
+@pytest.mark.parametrize("M,N,K", [(1, 32, 32), (3, 130, 288), (6, 4096, 384), (8, 272, 160),
+                                   (17, 256, 512), (33, 96, 320),
                                    (65, 1024, 640), (130, 14336, 256), (512, 2048, 384)])
 def test_fp4_packed_bitwise_equal_to_unpacked(bg, M, N, K):
     A = inputs.normal_bf16((M, K), 1.0, 800 + M)
@@ -197,7 +198,7 @@ def test_fp8_k_tail_ignores_pitch_padding(bg):
 def test_fp4_k_tail_ignores_pitch_padding(bg):
     """K = 288 (not a multiple of either kernel's stage) with A's row pitch
     padded with bf16 NaN."""
-    for M, N, K in ((3, 130, 288), (40, 1024, 160), (513, 256, 96)):
+    for M, N, K in ((3, 130, 288), (7, 130, 288), (40, 1024, 160), (513, 256, 96)):
         Ah = inputs.normal_bf16((M, K), 1.0, 960 + M)
         Ap = np.full((M, K + 64), 0x7FC0, np.uint16)
         Ap[:, :K] = Ah
@@ -211,9 +212,10 @@ def test_fp4_k_tail_ignores_pitch_padding(bg):
         assert np.array_equal(got_p, got)
 
 
-def test_bf16_k_tail_ignores_pitch_padding(bg):
+@pytest.mark.parametrize("M", [19, 3, 6])
+def test_bf16_k_tail_ignores_pitch_padding(bg, M):
     # the same property for the three bf16 layouts (K = 200: a partial 32-step)
-    M, N, K = 19, 272, 200
+    N, K = 272, 200
     Ah = inputs.normal_bf16((M, K), 1.0, 971)
     Bh = inputs.normal_bf16((K, N), 0.02, 972)
     Ap = np.full((M, K + 56), 0x7FC0, np.uint16)
