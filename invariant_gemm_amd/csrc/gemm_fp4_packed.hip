@@ -314,7 +314,7 @@ hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 // Launch geometry (tile sharing only: the per-element arithmetic is the same
 // for all): 64 x 128 tiles once they still give each compute unit a
 // workgroup, 64 x 64 from 17 rows, else two waves of 16 x 16 streaming that
-// stage only the first 4 or 8 rows of A when the call has no more.
+// stage only the first 8 rows of A when the call has no more.
 hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream)
 {
     const int nb = (a.N + 15) / 16;
@@ -323,9 +323,8 @@ hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream)
         return launch_geometry<4, 2, 4, 1, 2, false>(a, stream);   // weights shared by row tiles
     if (a.M > 16)
         return launch_geometry<4, 1, 4, 1, 4>(a, stream);
-    // at most 4 or 8 rows: stage only those rows of A
-    if (a.M <= 4)
-        return launch_geometry<2, 1, 1, 2, 4, true, 4>(a, stream);
+    // at most 8 rows: stage only those rows of A (a 4-row variant measured
+    // no faster)
     if (a.M <= 8)
         return launch_geometry<2, 1, 1, 2, 4, true, 8>(a, stream);
     return launch_geometry<2, 1, 1, 2, 4>(a, stream);
