@@ -31,12 +31,18 @@ __device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w)
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, BYTE));
 }
 
-__device__ __forceinline__ float e4m3_to_f32(uint32_t q)
+// Byte b of w, an e4m3fn code, -> fp32, exact, by the hardware conversion:
+// on gfx950 v_cvt_f32_fp8 decodes the OCP e4m3fn format (bias 7, subnormals
+// m*2^-9, S.1111.111 NaN; checked against that definition for all 256 codes
+// in every byte position).  b is a constant after unrolling.
+__device__ __forceinline__ float e4m3_byte_to_f32(uint32_t w, int b)
 {
-    const uint32_t mag = q & 0x7Fu;
-    float v = __builtin_bit_cast(float, mag << 20) * 0x1p120f;
-    v = mag == 0x7Fu ? __builtin_nanf("") : v;
-    return (q & 0x80u) ? -v : v;
+    switch (b) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+    }
 }
 
 // WAVES waves; wave w owns column blocks nb0 + w*CB .. +CB-1; RB row blocks.
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                                 const uint32_t w = qreg[p][q][c][t];
                                 bfrag[c] = u32x4{e2m1x2_to_bf16x2<0>(w), e2m1x2_to_bf16x2<1>(w),
                                                  e2m1x2_to_bf16x2<2>(w), e2m1x2_to_bf16x2<3>(w)};
-                                sc[tt][c] = e4m3_to_f32((sreg[p][q][c] >> (8 * t)) & 0xFFu);
+                                sc[tt][c] = e4m3_byte_to_f32(sreg[p][q][c], t);
                             }
 #pragma unroll
                             for (int r = 0; r < RB; ++r) {
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                                 const uint32_t w = qreg[p][q][c][t];
                                 bfrag[c] = u32x4{e2m1x2_to_bf16x2<0>(w), e2m1x2_to_bf16x2<1>(w),
                                                  e2m1x2_to_bf16x2<2>(w), e2m1x2_to_bf16x2<3>(w)};
-                                sc[c] = e4m3_to_f32((sreg[p][q][c] >> (8 * t)) & 0xFFu);
+                                sc[c] = e4m3_byte_to_f32(sreg[p][q][c], t);
                             }
 #pragma unroll
                             for (int r = 0; r < RB; ++r) {
