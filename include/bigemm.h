@@ -19,7 +19,9 @@
  *     fp32 accumulator in registers: no split-K, no stream-K, no atomics
  *     (the split-K conflict is the one the same article's section
  *     "牺牲了什么" describes);
- *   - the M tail is handled only by zero-filling rows >= M and masking stores.
+ *   - the M tail only decides which A rows are loaded (rows >= M read as
+ *     zero or are not loaded at all) and which C rows are stored; an output
+ *     row depends on its own A row alone.
  *
  * Conventions common to all entry points
  *   - All matrix pointers are DEVICE pointers (hipMalloc'd or torch tensors).
