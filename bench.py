@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -348,10 +349,103 @@ def cpu_baseline(budget_s=12.0):
         rows += A.shape[0]
         r += 8
     fl = flops(rows, N, K)
-    return {"value": round(fl / t_tot / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"fp64 oracle on {rows} rows of the M=256 bf16 batch (K=N=8192): "
-                      f"{fl / 1e9:.1f} GFLOP in {t_tot:.2f} s"}
+    out = {"value": round(fl / t_tot / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+           "kind": "oracle",
+           "sample": f"fp64 oracle on {rows} rows of the M=256 bf16 batch (K=N=8192): "
+                     f"{fl / 1e9:.1f} GFLOP in {t_tot:.2f} s"}
+    # the same oracle on one host thread, on a smaller sample of the same rows
+    n_threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        A = np.ascontiguousarray(pool[:4])
+        t0 = time.perf_counter()
+        oracle.gemm_bf16(A, Bc)
+        t1 = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(n_threads)
+    out["value_1core"] = round(flops(4, N, K) / t1 / 1e12, 6)
+    out["sample_1core"] = (f"fp64 oracle, one thread, on 4 rows of the same batch: "
+                           f"{flops(4, N, K) / 1e9:.2f} GFLOP in {t1:.2f} s")
+    out["host"] = host_info()
+    return out
+
+
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+# ------------------------------------------------------------------ device and HBM context
+
+def device_info(torch):
+    """Name, architecture and compute units of GPU 0, plus the clock levels
+    rocm-smi reports (read only; clocks are not locked)."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2**30, 1)}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        card = next(iter(json.loads(r.stdout).values()))
+        info["clocks"] = {k: v for k, v in card.items()
+                          if any(c in k for c in ("sclk", "mclk", "fclk")) and "speed" in k}
+    except Exception as e:          # informational only
+        info["clocks"] = f"unavailable ({type(e).__name__})"
+    return info
+
+
+def hbm_probe(torch, nbytes=1 << 30, rounds=5):
+    """Measured streaming rates over 1 GiB with torch's own device copy and
+    sum kernels: the practical HBM roof beside the 8 TB/s nominal one (context,
+    not part of the library)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    copy, read = [], []
+    for _ in range(rounds + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e2 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        src.sum()
+        e2.record()
+        e2.synchronize()
+        copy.append(e0.elapsed_time(e1))
+        read.append(e1.elapsed_time(e2))
+    copy, read = sorted(copy[1:]), sorted(read[1:])
+    del src, dst
+    return {"bytes": nbytes,
+            "copy_GBps": round(2 * nbytes / (copy[len(copy) // 2] * 1e6), 1),
+            "read_GBps": round(nbytes / (read[len(read) // 2] * 1e6), 1),
+            "note": "median of torch's device copy (read + write counted) and fp32 sum "
+                    "(read) over 1 GiB; the nominal HBM peak is 8000 GB/s"}
+
+
+def single_launch_us(torch, fn, n=15):
+    """Median time of one eager launch between HIP events on its stream
+    (launch overhead included), each launch after a full synchronisation."""
+    t = []
+    for _ in range(n):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        t.append(e0.elapsed_time(e1) * 1e3)
+    t.sort()
+    return round(t[len(t) // 2], 2)
 
 
 # ------------------------------------------------------------------ traffic evidence
@@ -452,6 +546,61 @@ def pmc_summary(fetch_dir: str, write_dir: str):
                                                   / len(per_m)),
             "per_m": per_m, "calibration": {k: {kk: vv for kk, vv in v.items() if kk != "bytes_per_launch"}
                                             for k, v in out.items()}}
+
+
+SIMDS, CUS, CLOCK_GHZ = 1024, 256, 2.4     # MI355X: 256 compute units x 4 SIMDs, peak clock
+
+
+def pmc_counters(dirs):
+    """Per-M medians of every counter in `rocprofv3 --pmc` runs of
+    `--pmc-probe` (three launches per M of the headline sweep), with the
+    dispatches' own durations, and the ratios the kernel notes use:
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x duration x 2.4 GHz)
+    (the counter sums over all SIMDs); wave time waiting on anything /
+    unable to issue its next instruction = SQ_WAIT_ANY / SQ_WAVE_CYCLES and
+    SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; LDS bank conflicts per active LDS
+    cycle; L2 hit rate TCC_HIT / (TCC_HIT + TCC_MISS); texture-address stall
+    = TA_ADDR_STALLED_BY_TC_CYCLES / (CUs x duration x 2.4 GHz)."""
+    import csv
+    import glob
+    per_m = {str(M): {} for M in SWEEP_C2}
+    for d in dirs:
+        disp = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                e = disp.setdefault(int(r["Dispatch_Id"]), {
+                    "name": r["Kernel_Name"], "c": {},
+                    "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        gemms = [disp[k] for k in sorted(disp) if "gemm_bf16_packed_kernel" in disp[k]["name"]]
+        if len(gemms) != 3 * len(SWEEP_C2):
+            raise SystemExit(f"{d}: {len(gemms)} GEMM dispatches (expected {3 * len(SWEEP_C2)})")
+        for i, M in enumerate(SWEEP_C2):
+            grp = gemms[3 * i:3 * i + 3]
+            row = per_m[str(M)]
+            for name in grp[0]["c"]:
+                row[name] = sorted(g["c"][name] for g in grp)[1]
+            row.setdefault("duration_ns", sorted(g["ns"] for g in grp)[1])
+
+    def ratio(row, a, b, scale=1.0):
+        return round(row[a] / (row[b] * scale), 4) if a in row and b in row and row[b] else None
+
+    for M, row in per_m.items():
+        cyc = row["duration_ns"] * CLOCK_GHZ
+        d = {}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in row:
+            d["mfma_busy"] = round(row["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cyc), 4)
+        if "TA_ADDR_STALLED_BY_TC_CYCLES" in row:
+            d["ta_stalled_by_cache"] = round(row["TA_ADDR_STALLED_BY_TC_CYCLES"] / (CUS * cyc), 4)
+        d["wave_waiting_any"] = ratio(row, "SQ_WAIT_ANY", "SQ_WAVE_CYCLES")
+        d["wave_cannot_issue"] = ratio(row, "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES")
+        d["lds_bank_conflicts_per_active_cycle"] = ratio(row, "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE")
+        if "TCC_HIT" in row and "TCC_MISS" in row:
+            d["l2_hit_rate"] = round(row["TCC_HIT"] / max(row["TCC_HIT"] + row["TCC_MISS"], 1.0), 4)
+        row["derived"] = d
+    src = [os.path.join(ROOT, "invariant_gemm_amd", "csrc", f) for f in ("gemm_bf16_packed.hip", "common.h")]
+    return {"kernel": "gemm_bf16_packed_kernel (bi_gemm_bf16_packed)",
+            "kernel_sha256": kernel_sha256(src), "per_m": per_m}
 
 
 # ------------------------------------------------------------------ legs
@@ -613,10 +762,15 @@ def main():
                          "pass x3, then B = 1 split x3 (L = 4096, Hq = 64, Hkv = 8)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise the FETCH_SIZE and WRITE_SIZE runs of --pmc-probe (no GPU)")
+    ap.add_argument("--pmc-counters", nargs="+", metavar="DIR",
+                    help="summarise other counter runs of --pmc-probe per M (no GPU)")
     args = ap.parse_args()
 
     if args.pmc_summary:
         print(json.dumps(pmc_summary(*args.pmc_summary), indent=1))
+        return
+    if args.pmc_counters:
+        print(json.dumps(pmc_counters(args.pmc_counters), indent=1))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -695,6 +849,8 @@ def main():
 
     if not args.quick:
         out["per_m"] = sweep(torch, wl, SWEEP_C2, bytes_bf16, MFMA_PEAK_TFLOPS["bf16"], args.rounds)
+        for M in SWEEP_C2:
+            out["per_m"][str(M)]["us_single_launch"] = single_launch_us(torch, lambda: wl.launch(M))
         packed_us = {m: v["us"] for m, v in out["per_m"].items()}
         del wl
         c2 = C2(torch, bigemm, inputs)
@@ -747,6 +903,8 @@ def main():
         del moe
         out["replay_bf16_K8192_N8192"] = replay(torch, bigemm, inputs)
         out["decode_attention_L4096_Hq64_Hkv8_D128"] = decode_attention(torch, bigemm, args.rounds)
+        out["hbm_probe"] = hbm_probe(torch)
+        out["device"] = device_info(torch)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

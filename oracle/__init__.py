@@ -65,6 +65,8 @@ def _load():
     lib.ora_round_bf16.argtypes = [i64, vp, vp]
     lib.ora_num_threads.restype = ctypes.c_int
     lib.ora_num_threads.argtypes = []
+    lib.ora_set_num_threads.restype = None
+    lib.ora_set_num_threads.argtypes = [ctypes.c_int]
     lib.ora_gemm_bf16.restype = None
     lib.ora_gemm_bf16.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, vp, i64]
     lib.ora_gemm_fp8bs.restype = None
@@ -130,6 +132,11 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_load().ora_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Host threads of the parallel loops (timing only; results do not depend on it)."""
+    _load().ora_set_num_threads(int(n))
 
 
 # ------------------------------------------------------------ GEMMs

@@ -123,6 +123,17 @@ int ora_num_threads(void)
 #endif
 }
 
+/* Threads used by the parallel loops below (host timing only: every output
+ * element is computed by one thread in the same order whatever the count). */
+void ora_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------ GEMMs
  * Output C and S are M x N row-major with row stride ldc (elements).
  * Each task owns row m and columns [n0, n1); it sweeps k = 0..K-1 in

@@ -411,3 +411,19 @@ def test_w4a8_scale_block_indexing():
     C, _ = oracle.gemm_w4a8(qA, sA, Bq, sE, N)
     assert np.array_equal(C[:, :3], np.full((M, 3), 256.0))
     assert np.array_equal(C[:, 3], np.full(M, 224.0 + 32 * 1024.0))
+
+
+def test_thread_count_does_not_change_results():
+    # the host thread count is a timing knob only: each element is summed by
+    # one thread in ascending k whatever the count
+    A = inputs.normal_bf16((9, 300), 1.0, 71)
+    B = inputs.normal_bf16((300, 40), 1.0, 72)
+    n = oracle.num_threads()
+    try:
+        C_all, S_all = oracle.gemm_bf16(A, B)
+        oracle.set_num_threads(1)
+        assert oracle.num_threads() == 1
+        C_one, S_one = oracle.gemm_bf16(A, B)
+    finally:
+        oracle.set_num_threads(n)
+    assert np.array_equal(C_all, C_one) and np.array_equal(S_all, S_one)
