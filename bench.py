@@ -548,6 +548,84 @@ def pmc_summary(fetch_dir: str, write_dir: str):
                                             for k, v in out.items()}}
 
 
+def legs_pmc():
+    """(name, kernel, workload class, M sweep, algorithmic bytes) of the
+    quantised legs whose HBM traffic the counters check."""
+    return (("fp8_blockscaled_packed_K7168_N2048", "gemm_fp8_packed_kernel", C3P, SWEEP_C3, bytes_fp8),
+            ("fp4_weight_only_packed_K4096_N14336", "gemm_fp4_packed_kernel", C4P, SWEEP_C4, bytes_fp4),
+            ("w4a8_mxfp4_K4096_N14336", "gemm_w4a8_packed_kernel", W4A8, W4A8.SWEEP, bytes_w4a8))
+
+
+def pmc_probe_legs(torch, bg, inputs):
+    """Launch sequence for the quantised legs' HBM-traffic counters: after the
+    first leg's set-up, a device copy of COPY_BYTES (the calibration
+    reference), then per leg three launches per M of its sweep, each on a
+    different rotated copy of the weights."""
+    for i, (name, _, cls, sweep_ms, _) in enumerate(legs_pmc()):
+        wl = cls(torch, bg, inputs)
+        torch.cuda.synchronize()
+        if i == 0:
+            src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+        for M in sweep_ms:
+            for _ in range(3):
+                wl.launch(M)
+        torch.cuda.synchronize()
+        del wl
+        log("pmc legs probe:", name, "3 launches per M", sweep_ms)
+
+
+def pmc_summary_legs(fetch_dir: str, write_dir: str):
+    """HBM bytes per launch of the quantised legs from the FETCH_SIZE and
+    WRITE_SIZE runs of `--pmc-probe-legs`, calibrated on the probe's copy, beside
+    each launch's algorithmic bytes."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = int(r["Dispatch_Id"])
+                name, v = vals.get(key, (r["Kernel_Name"], 0.0))
+                vals[key] = (name, v + float(r["Counter_Value"]))
+        return [vals[k] for k in sorted(vals)]
+
+    legs = legs_pmc()
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = per_dispatch(d, counter)
+        first = next(i for i, (n, _) in enumerate(rows) if legs[0][1] in n)
+        copies = [v for n, v in rows[:first] if "copy" in n.lower()][-3:]
+        if len(copies) != 3:
+            raise SystemExit(f"{counter}: {len(copies)} calibration copies before the first launch")
+        factor = COPY_BYTES / (sorted(copies)[1] * 1024.0)
+        for name, kern, cls, sweep_ms, nbytes in legs:
+            vals = [v for n, v in rows if kern in n]
+            if len(vals) != 3 * len(sweep_ms):
+                raise SystemExit(f"{counter} {name}: {len(vals)} dispatches (expected {3 * len(sweep_ms)})")
+            leg = out.setdefault(name, {})
+            for i, M in enumerate(sweep_ms):
+                v = sorted(vals[3 * i:3 * i + 3])[1] * 1024.0 * factor
+                leg.setdefault(str(M), {})[counter] = round(v)
+        out.setdefault("calibration", {})[counter] = {"scale_factor": round(factor, 4)}
+    for name, kern, cls, sweep_ms, nbytes in legs:
+        for M in sweep_ms:
+            e = out[name][str(M)]
+            alg = nbytes(M, cls.N, cls.K)
+            e["hbm_bytes"] = e["FETCH_SIZE"] + e["WRITE_SIZE"]
+            e["algorithmic_bytes"] = alg
+            e["ratio"] = round(e["hbm_bytes"] / alg, 3)
+    return out
+
+
 SIMDS, CUS, CLOCK_GHZ = 1024, 256, 2.4     # MI355X: 256 compute units x 4 SIMDs, peak clock
 
 
@@ -764,6 +842,11 @@ def main():
                     help="summarise the FETCH_SIZE and WRITE_SIZE runs of --pmc-probe (no GPU)")
     ap.add_argument("--pmc-counters", nargs="+", metavar="DIR",
                     help="summarise other counter runs of --pmc-probe per M (no GPU)")
+    ap.add_argument("--pmc-probe-legs", action="store_true",
+                    help="a known-size copy plus 3 launches per M of the fp8, fp4 and W4A8 packed "
+                         "legs (for rocprofv3 --pmc)")
+    ap.add_argument("--pmc-summary-legs", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise the FETCH_SIZE and WRITE_SIZE runs of --pmc-probe-legs (no GPU)")
     args = ap.parse_args()
 
     if args.pmc_summary:
@@ -771,6 +854,9 @@ def main():
         return
     if args.pmc_counters:
         print(json.dumps(pmc_counters(args.pmc_counters), indent=1))
+        return
+    if args.pmc_summary_legs:
+        print(json.dumps(pmc_summary_legs(*args.pmc_summary_legs), indent=1))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -790,6 +876,9 @@ def main():
         return
     if args.attention_probe:
         attention_probe(torch, bigemm)
+        return
+    if args.pmc_probe_legs:
+        pmc_probe_legs(torch, bigemm, inputs)
         return
     wl = C2P(torch, bigemm, inputs)
     if args.pmc_probe:
