@@ -641,7 +641,23 @@ def pmc_counters(dirs):
     = TA_ADDR_STALLED_BY_TC_CYCLES / (CUs x duration x 2.4 GHz)."""
     import csv
     import glob
-    per_m = {str(M): {} for M in SWEEP_C2}
+    return _counters_per_m(dirs, [("gemm_bf16_packed_kernel", SWEEP_C2)], csv, glob)[0] | {
+        "kernel": "gemm_bf16_packed_kernel (bi_gemm_bf16_packed)",
+        "kernel_sha256": kernel_sha256([os.path.join(ROOT, "invariant_gemm_amd", "csrc", f)
+                                        for f in ("gemm_bf16_packed.hip", "common.h")])}
+
+
+def pmc_counters_legs(dirs):
+    """The same per-M counter summary for the runs of `--pmc-probe-legs`."""
+    import csv
+    import glob
+    legs = legs_pmc()
+    res = _counters_per_m(dirs, [(kern, sweep_ms) for _, kern, _, sweep_ms, _ in legs], csv, glob)
+    return {name: r for (name, *_), r in zip(legs, res)}
+
+
+def _counters_per_m(dirs, kernels, csv, glob):
+    out = [{"per_m": {str(M): {} for M in sweep_ms}} for _, sweep_ms in kernels]
     for d in dirs:
         disp = {}
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
@@ -650,16 +666,22 @@ def pmc_counters(dirs):
                     "name": r["Kernel_Name"], "c": {},
                     "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
                 e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-        gemms = [disp[k] for k in sorted(disp) if "gemm_bf16_packed_kernel" in disp[k]["name"]]
-        if len(gemms) != 3 * len(SWEEP_C2):
-            raise SystemExit(f"{d}: {len(gemms)} GEMM dispatches (expected {3 * len(SWEEP_C2)})")
-        for i, M in enumerate(SWEEP_C2):
-            grp = gemms[3 * i:3 * i + 3]
-            row = per_m[str(M)]
-            for name in grp[0]["c"]:
-                row[name] = sorted(g["c"][name] for g in grp)[1]
-            row.setdefault("duration_ns", sorted(g["ns"] for g in grp)[1])
+        for (kern, sweep_ms), res in zip(kernels, out):
+            gemms = [disp[k] for k in sorted(disp) if kern in disp[k]["name"]]
+            if len(gemms) != 3 * len(sweep_ms):
+                raise SystemExit(f"{d}: {len(gemms)} {kern} dispatches (expected {3 * len(sweep_ms)})")
+            for i, M in enumerate(sweep_ms):
+                grp = gemms[3 * i:3 * i + 3]
+                row = res["per_m"][str(M)]
+                for name in grp[0]["c"]:
+                    row[name] = sorted(g["c"][name] for g in grp)[1]
+                row.setdefault("duration_ns", sorted(g["ns"] for g in grp)[1])
+    for res in out:
+        _derive(res["per_m"])
+    return out
 
+
+def _derive(per_m):
     def ratio(row, a, b, scale=1.0):
         return round(row[a] / (row[b] * scale), 4) if a in row and b in row and row[b] else None
 
@@ -676,9 +698,6 @@ def pmc_counters(dirs):
         if "TCC_HIT" in row and "TCC_MISS" in row:
             d["l2_hit_rate"] = round(row["TCC_HIT"] / max(row["TCC_HIT"] + row["TCC_MISS"], 1.0), 4)
         row["derived"] = d
-    src = [os.path.join(ROOT, "invariant_gemm_amd", "csrc", f) for f in ("gemm_bf16_packed.hip", "common.h")]
-    return {"kernel": "gemm_bf16_packed_kernel (bi_gemm_bf16_packed)",
-            "kernel_sha256": kernel_sha256(src), "per_m": per_m}
 
 
 # ------------------------------------------------------------------ legs
@@ -847,6 +866,8 @@ def main():
                          "legs (for rocprofv3 --pmc)")
     ap.add_argument("--pmc-summary-legs", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise the FETCH_SIZE and WRITE_SIZE runs of --pmc-probe-legs (no GPU)")
+    ap.add_argument("--pmc-counters-legs", nargs="+", metavar="DIR",
+                    help="summarise other counter runs of --pmc-probe-legs per leg and M (no GPU)")
     args = ap.parse_args()
 
     if args.pmc_summary:
@@ -854,6 +875,9 @@ def main():
         return
     if args.pmc_counters:
         print(json.dumps(pmc_counters(args.pmc_counters), indent=1))
+        return
+    if args.pmc_counters_legs:
+        print(json.dumps(pmc_counters_legs(args.pmc_counters_legs), indent=1))
         return
     if args.pmc_summary_legs:
         print(json.dumps(pmc_summary_legs(*args.pmc_summary_legs), indent=1))
