@@ -90,6 +90,12 @@ typedef struct bi_schedule {
 /* Largest supported extent of any single dimension (M, N or K). */
 #define BI_MAX_DIM ((int64_t)1 << 24)
 
+/* Largest supported row pitch, in bytes, of any matrix or scale array the
+ * GEMM kernels read (A, B, Bt, codes, scales; not C): a kernel addresses up
+ * to 128 rows of an input from one base with 32-bit offsets.  A larger
+ * pitch returns BI_ERR_UNSUPPORTED. */
+#define BI_MAX_PITCH_BYTES ((int64_t)1 << 24)
+
 /*
  * bf16 x bf16 -> bf16.
  *   A : bf16 [M,K], row pitch lda >= K   (elements; lda % 8 == 0)

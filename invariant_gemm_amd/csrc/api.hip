@@ -41,6 +41,11 @@ Schedule schedule_for(bi_dtype dt, int64_t N, int64_t K)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// A kernel addresses up to 128 rows of an input from one buffer resource
+// (a tile's A rows, a stage's B rows) with 32-bit offsets below 2^31; row
+// pitches are capped so that such a span always fits.
+bool pitch_ok(int64_t ld, int64_t elem_bytes) { return ld * elem_bytes <= BI_MAX_PITCH_BYTES; }
+
 bi_status check_dims(int64_t M, int64_t N, int64_t K)
 {
     if (M < 0 || N < 0 || K < 0)
@@ -75,6 +80,8 @@ bi_status validate_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int6
         return BI_ERR_NULL;
     if ((K > 0 && (lda < K || ldb < b_row)) || ldc < N)
         return BI_ERR_STRIDE;
+    if (K > 0 && (!pitch_ok(lda, 2) || !pitch_ok(ldb, 2)))
+        return BI_ERR_UNSUPPORTED;
     if (((uintptr_t)C & 1u) != 0)
         return BI_ERR_ALIGN;
     if (K > 0 && (!aligned16(A) || !aligned16(B) || lda % 8 || ldb % 8))
@@ -103,6 +110,8 @@ bi_status validate_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_
         return BI_ERR_NULL;
     if ((K > 0 && (lda < K || ldb < N || ldsa < kb || ldsb < nb)) || ldc < N)
         return BI_ERR_STRIDE;
+    if (K > 0 && (!pitch_ok(lda, 1) || !pitch_ok(ldb, 1) || !pitch_ok(ldsa, 4) || !pitch_ok(ldsb, 4)))
+        return BI_ERR_UNSUPPORTED;
     if (((uintptr_t)C & 1u) != 0)
         return BI_ERR_ALIGN;
     if (K > 0 && (!aligned16(A) || !aligned16(B) || lda % 16 || ldb % 16 || !aligned4(sA) ||
@@ -129,6 +138,8 @@ bi_status validate_fp4(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64
         return BI_ERR_NULL;
     if ((K > 0 && (lda < K || ldbq < N / 2 || ldsb < N)) || ldc < N)
         return BI_ERR_STRIDE;
+    if (K > 0 && (!pitch_ok(lda, 2) || !pitch_ok(ldbq, 1) || !pitch_ok(ldsb, 1)))
+        return BI_ERR_UNSUPPORTED;
     if (((uintptr_t)C & 1u) != 0)
         return BI_ERR_ALIGN;
     if (K > 0 && (!aligned16(A) || !aligned16(Bq) || !aligned16(sB) || lda % 8 || ldbq % 16 ||
@@ -345,6 +356,8 @@ bi_status bi_gemm_bf16_packed(int64_t M, int64_t N, int64_t K, const uint16_t* A
         return BI_ERR_NULL;
     if ((K > 0 && lda < K) || ldc < N)
         return BI_ERR_STRIDE;
+    if (K > 0 && !pitch_ok(lda, 2))
+        return BI_ERR_UNSUPPORTED;
     if (((uintptr_t)C & 1u) || (K > 0 && (!aligned16(A) || lda % 8 || !aligned16(Bp))))
         return BI_ERR_ALIGN;
     if (bp_bytes < bi_packed_b_bytes(BI_BF16, N, K))
@@ -374,6 +387,8 @@ bi_status bi_gemm_bf16_grouped_packed(int64_t G, const int32_t* offsets, int64_t
         return BI_ERR_NULL;
     if ((K > 0 && lda < K) || ldc < N)
         return BI_ERR_STRIDE;
+    if (K > 0 && !pitch_ok(lda, 2))
+        return BI_ERR_UNSUPPORTED;
     if (((uintptr_t)C & 1u) || ((uintptr_t)offsets & 3u) ||
         (K > 0 && (!aligned16(A) || lda % 8 || !aligned16(Bp))))
         return BI_ERR_ALIGN;
@@ -457,6 +472,8 @@ bi_status bi_gemm_fp8_blockscaled_packed(int64_t M, int64_t N, int64_t K, const 
         return BI_ERR_NULL;
     if ((K > 0 && (lda < K || ldsa < kb || ldsb < nb)) || ldc < N)
         return BI_ERR_STRIDE;
+    if (K > 0 && (!pitch_ok(lda, 1) || !pitch_ok(ldsa, 4) || !pitch_ok(ldsb, 4)))
+        return BI_ERR_UNSUPPORTED;
     if (((uintptr_t)C & 1u) ||
         (K > 0 && (!aligned16(A) || lda % 16 || !aligned16(Bp) || !aligned4(sA) || !aligned4(sB))))
         return BI_ERR_ALIGN;
@@ -506,6 +523,8 @@ bi_status bi_gemm_fp4_w_packed(int64_t M, int64_t N, int64_t K, const uint16_t* 
         return BI_ERR_NULL;
     if ((K > 0 && lda < K) || ldc < N)
         return BI_ERR_STRIDE;
+    if (K > 0 && !pitch_ok(lda, 2))
+        return BI_ERR_UNSUPPORTED;
     if (((uintptr_t)C & 1u) || (K > 0 && (!aligned16(A) || lda % 8 || !aligned16(Bp))))
         return BI_ERR_ALIGN;
     if (bp_bytes < bi_packed_b_bytes(BI_FP4_W, N, K))
@@ -556,6 +575,8 @@ bi_status bi_gemm_w4a8_packed(int64_t M, int64_t N, int64_t K, const uint8_t* A,
         return BI_ERR_NULL;
     if ((K > 0 && (lda < K || ldsa < K / 128)) || ldc < N)
         return BI_ERR_STRIDE;
+    if (K > 0 && (!pitch_ok(lda, 1) || !pitch_ok(ldsa, 4)))
+        return BI_ERR_UNSUPPORTED;
     if (((uintptr_t)C & 1u) ||
         (K > 0 && (!aligned16(A) || lda % 16 || !aligned16(Bp) || !aligned4(sA))))
         return BI_ERR_ALIGN;

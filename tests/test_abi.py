@@ -262,3 +262,22 @@ def test_decode_attention_validation():
     assert bigemm.decode_attention_choice(1, 64, 8, 4096) == "split"
     assert bigemm.decode_attention_choice(32, 64, 8, 4096) == "single"
     assert bigemm.decode_attention_choice(1, 64, 8, 256) == "single"    # one group: nothing to split
+
+
+def test_row_pitch_cap():
+    # a kernel reads up to 128 rows of an input from one base with 32-bit
+    # offsets; pitches past BI_MAX_PITCH_BYTES (16 MiB) are refused up front
+    # (every call here must be refused: a call that passed would launch on
+    # the fake pointer)
+    cap = 1 << 24
+    assert bf16(8, 8, 8, lda=cap // 2 + 8) == UNSUP
+    assert bf16(8, 8, 8, ldb=cap // 2 + 8) == UNSUP
+    assert fp4(8, 8, 32, ldbq=cap + 16) == UNSUP
+    assert fp4(8, 8, 32, lda=cap // 2 + 8) == UNSUP
+    assert lib.bi_gemm_fp8_blockscaled(8, 8, 128, P, cap + 16, P, 1, P, 16, P, 1, P, 8, None) == UNSUP
+    assert lib.bi_gemm_fp8_blockscaled(8, 8, 128, P, 128, P, cap // 4 + 4, P, 16, P, 1, P, 8,
+                                       None) == UNSUP
+    need = bigemm.packed_b_bytes(bigemm.BI_BF16, 64, 64)
+    assert lib.bi_gemm_bf16_packed(8, 64, 64, P, cap // 2 + 8, P, need, P, 64, None) == UNSUP
+    need = bigemm.packed_b_bytes(bigemm.BI_W4A8, 64, 128)
+    assert lib.bi_gemm_w4a8_packed(8, 64, 128, P, cap + 16, P, 1, P, need, P, 64, None) == UNSUP
