@@ -27,7 +27,8 @@
 //               four row blocks, A fragments over two column blocks.
 // None changes the K order, the MFMA or the epilogue of any element.  The
 // two 16-row streaming geometries stage only the first 4 or 8 rows of A when
-// the call has no more rows than that.
+// the call has no more rows than that, and the one-wave geometry can run on
+// half blocks (8 columns per workgroup) when N/16 blocks are too few.
 // Weight loads are marked non-temporal (read once) except in the large
 // geometry, whose four row tiles share each column strip through L2.
 #include <algorithm>
@@ -65,13 +66,20 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
 // no tile can hold more than AR rows): LDS rows past them keep stale values,
 // which reach only output rows that are never stored -- an MFMA output row
 // depends on its own A row alone.
-template <int WAVES, int CB, int RB, int KS_ST, int PF, bool GROUPED, bool NT, int AR>
+//
+// HALF (one wave, one column block): a workgroup owns 8 of a block's 16
+// columns, so twice as many workgroups share the weights.  Its lanes load
+// only those 8 columns' bytes (lanes of the other 8 columns load the same
+// bytes again, which costs no extra memory traffic) and store only those
+// columns; MFMA output columns are independent, so each stored column sees
+// exactly the operands and K order of the full-block path.
+template <int WAVES, int CB, int RB, int KS_ST, int PF, bool GROUPED, bool NT, int AR, bool HALF>
 __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
     int M, int N, int K,
     const uint16_t* __restrict__ A, int64_t lda,
     const uint8_t* __restrict__ Bp,
     uint16_t* __restrict__ C, int64_t ldc, int m_tiles,
-    const int32_t* __restrict__ offsets, int n_groups, int64_t b_stride)
+    const int32_t* __restrict__ offsets, int n_groups, int64_t b_stride, int slot_first)
 {
     constexpr int NTHR = 64 * WAVES;
     constexpr int BM = 16 * RB;
@@ -82,15 +90,36 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
     constexpr int A_LDU = (AR * CPR + NTHR - 1) / NTHR;   // loads that cover rows < AR
     static_assert(A_LD * NTHR * 16 == A_STAGE, "A stage must split evenly over the threads");
     static_assert(AR >= 1 && AR <= BM, "staged rows must lie in the tile");
+    static_assert(!HALF || (WAVES == 1 && CB == 1), "half blocks: one wave, one column block");
     static_assert(PF % 2 == 0, "the LDS double buffer is indexed by stage parity");
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * A_STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tile = xcd_remap(blockIdx.x, gridDim.x);
-    const int nt = tile / m_tiles;
-    const int mt = tile - nt * m_tiles;
+    // Plain calls: the row tiles of a column strip are consecutive and meet in
+    // one XCD's L2.  Grouped calls with slot_first give each XCD (dispatch
+    // id % 8) a contiguous range of column tiles and walk it row slot first,
+    // so every occupied slot is dispatched before the empty ones (which exit
+    // at once) and the occupied slots spread evenly over the XCDs.
+    int nt, mt;
+    if (GROUPED && slot_first) {
+        const int n_tiles = gridDim.x / m_tiles;
+        const int b = blockIdx.x;
+        if (n_tiles % kXcds == 0) {
+            const int per = n_tiles / kXcds;
+            const int i = b / kXcds;
+            mt = i / per;
+            nt = (b % kXcds) * per + (i - mt * per);
+        } else {
+            mt = b / n_tiles;
+            nt = b - mt * n_tiles;
+        }
+    } else {
+        const int tile = xcd_remap(blockIdx.x, gridDim.x);
+        nt = tile / m_tiles;
+        mt = tile - nt * m_tiles;
+    }
     int m0 = mt * BM;
     int row_end = M;                                  // rows [m0, row_end) are this tile's
     if constexpr (GROUPED) {
@@ -114,7 +143,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
     }
     const int NB = (N + 15) >> 4;
     const int KS = (K + KSTEP - 1) / KSTEP;
-    const int nb0 = nt * (WAVES * CB) + wave * CB;    // first column block of this wave
+    const int ntb = HALF ? nt >> 1 : nt;              // column tile in blocks
+    const int ch = HALF ? nt & 1 : 0;                 // which 8 columns of the block
+    const int nb0 = ntb * (WAVES * CB) + wave * CB;   // first column block of this wave
+    // the lane whose 16 packed bytes this lane loads (its own unless HALF)
+    const int blane = HALF ? (lane & 48) | (8 * ch + (lane & 7)) : lane;
 
     const int nst = (K + BKS - 1) / BKS;
     const int kpad = (K + 7) & ~7;
@@ -157,8 +190,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
                 live && nb < NB ? clamp_bytes((int64_t)(KS - ks0) * 1024) : 0u);
 #pragma unroll
             for (int ks = 0; ks < KS_ST; ++ks)
-                br[ks][c] = NT ? buf_load16_nt(rb, (uint32_t)(ks * 1024 + lane * 16))
-                               : buf_load16(rb, (uint32_t)(ks * 1024 + lane * 16));
+                br[ks][c] = NT ? buf_load16_nt(rb, (uint32_t)(ks * 1024 + blane * 16))
+                               : buf_load16(rb, (uint32_t)(ks * 1024 + blane * 16));
         }
     };
 
@@ -213,13 +246,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
 
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
-        const int col = 16 * (nb0 + c) + li;
+        const int col = 16 * (nb0 + c) + (HALF ? 8 * ch + li : li);
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int row = m0 + 16 * r + 4 * lg + j;
-                if (row < row_end && col < N)
+                if (row < row_end && col < N && (!HALF || li < 8))
                     C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[r][c][j]);
             }
         }
@@ -251,22 +284,27 @@ __global__ void pack_b_bf16_kernel(int N, int K, const uint16_t* __restrict__ B,
     *reinterpret_cast<u32x4*>(Bp + q * 16) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <int WAVES, int CB, int RB, int KS_ST, int PF, bool NT = true, int AR = 16 * RB>
+template <int WAVES, int CB, int RB, int KS_ST, int PF, bool NT = true, int AR = 16 * RB,
+          bool HALF = false>
 hipError_t launch_geometry(const GemmArgs& a, const GroupArgs* grp, hipStream_t stream)
 {
-    const int n_tiles = ((a.N + 15) / 16 + WAVES * CB - 1) / (WAVES * CB);
+    const int n_tiles = ((a.N + 15) / 16 + WAVES * CB - 1) / (WAVES * CB) * (HALF ? 2 : 1);
     const dim3 block(64 * WAVES);
     if (grp) {
-        // row slots: every group adds at most one partial tile
-        const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB) + grp->n_groups;
-        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, true, NT, AR><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
+        // row slots: the rows (at most M once the kernel clamps the offsets)
+        // fall in at most k = min(groups, M) non-empty groups of r_g rows, and
+        // sum ceil(r_g / BM) <= floor((M + k (BM - 1)) / BM) -- one slot at M = 1
+        constexpr int BM = 16 * RB;
+        const int64_t k = std::min<int64_t>(grp->n_groups, a.M);
+        const int m_tiles = (int)(((int64_t)a.M + k * (BM - 1)) / BM);
+        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, true, NT, AR, HALF><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
             a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles,
-            grp->offsets, grp->n_groups, grp->b_stride);
+            grp->offsets, grp->n_groups, grp->b_stride, grp->slot_first);
     } else {
         const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, false, NT, AR><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
+        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, false, NT, AR, HALF><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
             a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles,
-            nullptr, 0, 0);
+            nullptr, 0, 0, 0);
     }
     return hipGetLastError();
 }
@@ -313,6 +351,10 @@ hipError_t launch_packed(const GemmArgs& a, const GroupArgs* grp, int geometry, 
         if (a.M <= 4) return launch_geometry<1, 1, 1, 16, 2, true, 4>(a, grp, stream);
         if (a.M <= 8) return launch_geometry<1, 1, 1, 16, 2, true, 8>(a, grp, stream);
         return launch_geometry<1, 1, 1, 16, 2>(a, grp, stream);
+    case 6:                                          // geometry 5 on half blocks
+        if (a.M <= 4) return launch_geometry<1, 1, 1, 16, 2, true, 4, true>(a, grp, stream);
+        if (a.M <= 8) return launch_geometry<1, 1, 1, 16, 2, true, 8, true>(a, grp, stream);
+        return launch_geometry<1, 1, 1, 16, 2, true, 16, true>(a, grp, stream);
     default:
         if (a.M <= 4) return launch_geometry<2, 1, 1, 8, 4, true, 4>(a, grp, stream);
         if (a.M <= 8) return launch_geometry<2, 1, 1, 8, 4, true, 8>(a, grp, stream);
@@ -322,9 +364,16 @@ hipError_t launch_packed(const GemmArgs& a, const GroupArgs* grp, int geometry, 
 
 }  // namespace
 
+// The one-wave geometry runs on half blocks (8 columns per workgroup) while
+// the column blocks are fewer than the compute units (N = 2048: M = 8
+// 10.0 -> 9.4 us, M = 16 11.2 -> 10.5 us, the same at M <= 4).  Grouped
+// calls keep whole blocks: there the doubled slot count measured slower.
 hipError_t launch_bf16_packed(const GemmArgs& a, hipStream_t stream)
 {
-    return launch_packed(a, nullptr, packed_geometry(a.M, a.N), stream);
+    int geometry = packed_geometry(a.M, a.N);
+    if (geometry == 5 && (a.N + 15) / 16 < 256)
+        geometry = 6;
+    return launch_packed(a, nullptr, geometry, stream);
 }
 
 // Grouped launch: the geometry follows the mean rows per group (any choice
@@ -338,7 +387,12 @@ hipError_t launch_bf16_grouped_packed(const GemmArgs& a, const GroupArgs& g, hip
     const int64_t active = std::min<int64_t>(g.n_groups, a.M);
     if (geometry == 5 && active * ((a.N + 31) / 32) >= 256)
         geometry = 0;
-    return launch_packed(a, &g, geometry, stream);
+    // slot order: row slot first from four rows per group on (E = 8, N = 2048:
+    // 64 tokens 45.7 -> 38.9 us, 512 tokens 91.1 -> 89.5 us); below that the
+    // XCD-contiguous column order measured faster (8 tokens 27.5 vs 30.2 us)
+    GroupArgs gs = g;
+    gs.slot_first = mean >= 4 ? 1 : 0;
+    return launch_packed(a, &gs, geometry, stream);
 }
 
 hipError_t launch_pack_b_bf16(int N, int K, const uint16_t* B, int64_t ldb, uint8_t* Bp,

@@ -30,6 +30,7 @@ struct GroupArgs {
     const int32_t* offsets;  // device, n_groups + 1 row offsets
     int n_groups;
     int64_t b_stride;        // bytes between consecutive groups' packed weights
+    int slot_first = 0;      // launch order of the workgroup slots (set by the launcher)
 };
 
 hipError_t launch_bf16(const GemmArgs& a, const Schedule& s, hipStream_t stream);

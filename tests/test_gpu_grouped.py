@@ -116,6 +116,27 @@ def test_every_geometry(bg):
                 assert np.array_equal(C[lo:hi], ref), f"M={M} expert {e}"
 
 
+def test_narrow_n_few_rows(bg):
+    # few rows over a narrow, ragged N (the one-wave geometry with its tight
+    # slot count): every expert's rows must equal the row-major kernel's
+    # result for that expert, bit for bit
+    E, K, N = 3, 256, 1000
+    Bh = [inputs.normal_bf16((K, N), 0.02, 1460 + e) for e in range(E)]
+    Bd = [dev_bf16(b) for b in Bh]
+    Bp = bg.pack_b_bf16_grouped(Bd)
+    for M in (1, 3, 9):
+        Ah = inputs.normal_bf16((M, K), 1.0, 1470 + M)
+        expert = inputs.route_tokens(M, E, 1480 + M, 1.0)
+        order, offsets = inputs.group_by_expert(expert, E)
+        A = dev_bf16(Ah[order])
+        C = host_codes(run(bg, A, offsets, Bp))
+        for e in range(E):
+            lo, hi = offsets[e], offsets[e + 1]
+            if hi > lo:
+                ref = host_codes(bg.gemm_bf16(A[lo:hi], Bd[e]))
+                assert np.array_equal(C[lo:hi], ref), f"M={M} expert {e}"
+
+
 def test_malformed_offsets_stay_in_bounds(bg):
     # a decreasing entry is clamped (no access outside A, B or C); the rows of
     # the well-formed groups before it still come out right
