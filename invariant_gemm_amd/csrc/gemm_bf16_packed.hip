@@ -15,14 +15,14 @@
 // its batch companions (the invariance definition in section
 // "什么是batch invariance" of the QbitAI article).
 //
-// Six launch geometries in three families share that arithmetic (the
+// Seven launch geometries in three families share that arithmetic (the
 // dual-program idea of section 4.1 of the lshu.cn article and section 3.3 of
 // the wmrh.cn blog, applied to the GEMM: programs for "GPU not saturated" /
 // "saturated" whose results are bit-identical):
 //   streaming : 2 waves x 1 column block, BM = 16, 32 or 64 -- N/32
 //               workgroups stream B (1 wave, N/16 workgroups, for small N
 //               and M <= 16);
-//   medium    : 4 waves x 1 column block, BM = 64;
+//   medium    : 4 waves x 1 column block, BM = 32 (33..64 rows) or 64;
 //   large     : 4 waves x 2 column blocks, BM = 64 -- B fragments reused over
 //               four row blocks, A fragments over two column blocks.
 // None changes the K order, the MFMA or the epilogue of any element.  The
@@ -346,6 +346,7 @@ hipError_t launch_packed(const GemmArgs& a, const GroupArgs* grp, int geometry, 
     case 3: return launch_geometry<4, 1, 4, 4, 4>(a, grp, stream);
     case 2: return launch_geometry<2, 1, 4, 4, 4>(a, grp, stream);
     case 1: return launch_geometry<2, 1, 2, 8, 2>(a, grp, stream);
+    case 7: return launch_geometry<4, 1, 2, 8, 2>(a, grp, stream);   // 32 x 64, four waves
     case 5:
         // at most 4 or 8 rows in the call: stage only those rows of A
         if (a.M <= 4) return launch_geometry<1, 1, 1, 16, 2, true, 4>(a, grp, stream);
@@ -373,6 +374,12 @@ hipError_t launch_bf16_packed(const GemmArgs& a, hipStream_t stream)
     int geometry = packed_geometry(a.M, a.N);
     if (geometry == 5 && (a.N + 15) / 16 < 256)
         geometry = 6;
+    // 33..64 rows: 32 x 64 tiles on four waves keep all four SIMDs of a
+    // compute unit busy where the two-wave 64 x 32 streaming tiles leave two
+    // idle (K = N = 8192, M = 64: 34.0 -> 31.7 us) -- while they still give
+    // every compute unit a workgroup
+    if (geometry == 2 && a.M <= 64 && ((a.M + 31) / 32) * (((a.N + 15) / 16 + 3) / 4) >= 256)
+        geometry = 7;
     return launch_packed(a, nullptr, geometry, stream);
 }
 
