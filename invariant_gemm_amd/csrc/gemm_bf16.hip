@@ -16,10 +16,11 @@
 //     return zero) or skipped as whole 16-row MFMA blocks, which cannot change
 //     another row's result: an MFMA output row depends only on its own A row.
 //
-// Workgroup: 256 threads = 4 waves, output tile BM x 32 (BM = 32 * RB).
-//   wave w: 16-column block cb = w & 1, row group rg = w >> 1 with RB
-//   16-row blocks each.  Small M is served by N-tiling alone: N/32 workgroups
-//   stream disjoint column strips of B.
+// Workgroup: 256 threads = 4 waves, output tile BM x BN (BM = 32 * RB,
+//   BN = 32 * CBW).  wave w: column group cb = w & 1 of CBW 16-column blocks,
+//   row group rg = w >> 1 with RB 16-row blocks each.  Small M is served by
+//   N-tiling alone: N/32 workgroups stream disjoint column strips of B;
+//   larger M takes wider strips (CBW = 2 or 4), which A rows then share.
 //
 // Data path per pipeline stage of 128 K rows (PF stages in flight):
 //   A [M,K] --buffer_load_dwordx4--> VGPR --ds_write_b128--> LDS [m][k]
@@ -34,12 +35,9 @@
 namespace bigemm {
 namespace {
 
-constexpr int BN = 32;                   // columns per workgroup
 constexpr int BKS = 128;                 // K rows per stage
 constexpr int KSTEP = 32;                // K per MFMA
 constexpr int KS_PER_ST = BKS / KSTEP;   // 4
-constexpr int B_PITCH = BN * 2 + 16;     // LDS bytes per B row (padded against bank conflicts)
-constexpr int B_STAGE = BKS * B_PITCH;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -66,7 +64,7 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
 // SPLIT = false: the batch-invariant kernel (full K per workgroup).
 // SPLIT = true : the split-K comparator; blockIdx.y picks a K range and the
 //                partial tile is added into an fp32 workspace with atomics.
-template <int RB, int PF, bool SPLIT>
+template <int RB, int PF, bool SPLIT, int CBW>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     int M, int N, int K,
     const uint16_t* __restrict__ A, int64_t lda,
@@ -75,6 +73,11 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
     float* __restrict__ ws, int m_tiles, int splits)
 {
     static_assert(PF % 2 == 0, "the LDS double buffer is indexed by stage parity");
+    constexpr int BN = 32 * CBW;                 // columns per workgroup
+    constexpr int B_PITCH = BN * 2 + 16;         // LDS bytes per B row (padded against bank conflicts)
+    constexpr int B_STAGE = BKS * B_PITCH;
+    constexpr int B_CPR = BN / 8;                // 16-byte B chunks per row
+    constexpr int B_LD = BKS * B_CPR / 256;      // 16-byte B chunks per lane per stage
     constexpr int BM = 32 * RB;
     constexpr int A_STAGE = BM * BKS * 2;        // bytes
     constexpr int A_LD = BM / 16;                // 16-byte A chunks per lane per stage
@@ -111,12 +114,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
         const int kc = (c & 15) ^ (row & 7);
         a_voff[j] = (uint32_t)(row * lda + kc * 8) * 2u;
     }
-    // ---- B staging map: rows 2q, 2q+1 of the stage, 16-byte column chunk lc.
-    const int q = tid >> 2;
-    const int lc = tid & 3;
-    const uint32_t b_voff = (uint32_t)(2 * q * ldb + 8 * lc) * 2u;
-    const uint32_t b_ldb2 = (uint32_t)ldb * 2u;
-    const int b_lds = 2 * q * B_PITCH + lc * 16;
+    // ---- B staging map: chunk c = j*256 + tid -> row c / B_CPR of the stage,
+    //      16-byte column chunk c % B_CPR; LDS rows padded to B_PITCH.
+    uint32_t b_voff[B_LD];
+    int b_lds[B_LD];
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j) {
+        const int c = j * 256 + tid;
+        const int row = c / B_CPR;
+        const int ch = c % B_CPR;
+        b_voff[j] = (uint32_t)(row * ldb + 8 * ch) * 2u;
+        b_lds[j] = row * B_PITCH + ch * 16;
+    }
 
     // ---- MFMA role.
     const int cb = wave & 1;
@@ -136,17 +145,20 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
             a_rd[r][ks] = (row * 16 + ((ks * 4 + lg) ^ (row & 7))) * 16;
     }
     // transposed B reads: within 16-lane group lg, lane li points at row
-    // 8*lg + 4*half + li/4 of the k-step, columns cb*16 + 4*(li%4) .. +3
-    const int b_rd = (8 * lg + (li >> 2)) * B_PITCH + cb * 32 + (li & 3) * 8;
+    // 8*lg + 4*half + li/4 of the k-step, columns 16*(CBW*cb + c) + 4*(li%4)
+    // .. +3 of this wave's block c
+    const int b_rd = (8 * lg + (li >> 2)) * B_PITCH + CBW * cb * 32 + (li & 3) * 8;
 
     u32x4 areg[PF][A_LD];
-    u32x4 breg[PF][2];
-    f32x4 acc[RB];
+    u32x4 breg[PF][B_LD];
+    f32x4 acc[RB][CBW];
 #pragma unroll
     for (int r = 0; r < RB; ++r)
-        acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < CBW; ++c)
+            acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto issue = [&](int s, u32x4 (&ar)[A_LD], u32x4 (&br)[2]) {
+    auto issue = [&](int s, u32x4 (&ar)[A_LD], u32x4 (&br)[B_LD]) {
         // stages past this workgroup's range get an empty extent: no traffic
         const bool live = s < nst;
         const int kst = (st_lo + s) * BKS;
@@ -159,8 +171,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < A_LD; ++j)
             ar[j] = buf_load16(ra, a_voff[j]);
-        br[0] = buf_load16(rb, b_voff);
-        br[1] = buf_load16(rb, b_voff + b_ldb2);
+#pragma unroll
+        for (int j = 0; j < B_LD; ++j)
+            br[j] = buf_load16(rb, b_voff[j]);
     };
 
     // prologue: PF stages in flight
@@ -195,38 +208,48 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 #pragma unroll
             for (int j = 0; j < A_LD; ++j)
                 *reinterpret_cast<u32x4*>(abuf + (j * 256 + tid) * 16) = areg[p][j];
-            *reinterpret_cast<u32x4*>(bbuf + b_lds) = breg[p][0];
-            *reinterpret_cast<u32x4*>(bbuf + b_lds + B_PITCH) = breg[p][1];
+#pragma unroll
+            for (int j = 0; j < B_LD; ++j)
+                *reinterpret_cast<u32x4*>(bbuf + b_lds[j]) = breg[p][j];
             issue(s + PF, areg[p], breg[p]);
             __syncthreads();
 #pragma unroll
             for (int ks = 0; ks < KS_PER_ST; ++ks) {
-                const uint8_t* bp = bbuf + b_rd + ks * KSTEP * B_PITCH;
-                const u32x2 b0 = ds_read_tr16(bp);
-                const u32x2 b1 = ds_read_tr16(bp + 4 * B_PITCH);
-                const u32x4 bfrag = {b0[0], b0[1], b1[0], b1[1]};
+                u32x4 bfrag[CBW];
+#pragma unroll
+                for (int c = 0; c < CBW; ++c) {
+                    const uint8_t* bp = bbuf + b_rd + c * 32 + ks * KSTEP * B_PITCH;
+                    const u32x2 b0 = ds_read_tr16(bp);
+                    const u32x2 b1 = ds_read_tr16(bp + 4 * B_PITCH);
+                    bfrag[c] = u32x4{b0[0], b0[1], b1[0], b1[1]};
+                }
 #pragma unroll
                 for (int r = 0; r < RB; ++r) {
                     const u32x4 afrag = *reinterpret_cast<const u32x4*>(abuf + a_rd[r][ks]);
-                    acc[r] = mfma_bf16(afrag, bfrag, acc[r]);
+#pragma unroll
+                    for (int c = 0; c < CBW; ++c)
+                        acc[r][c] = mfma_bf16(afrag, bfrag[c], acc[r][c]);
                 }
             }
         }
     }
 
     // epilogue: lane (li, lg) holds rows 4*lg + j of each row block, column li
-    const int col = n0 + cb * 16 + li;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        if (r < nrb) {
+    for (int c = 0; c < CBW; ++c) {
+        const int col = n0 + (CBW * cb + c) * 16 + li;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = m0 + rbase + 16 * r + 4 * lg + j;
-                if (row < M && col < N) {
-                    if constexpr (SPLIT)
-                        atomicAdd(ws + (int64_t)row * N + col, acc[r][j]);
-                    else
-                        C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[r][j]);
+        for (int r = 0; r < RB; ++r) {
+            if (r < nrb) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = m0 + rbase + 16 * r + 4 * lg + j;
+                    if (row < M && col < N) {
+                        if constexpr (SPLIT)
+                            atomicAdd(ws + (int64_t)row * N + col, acc[r][c][j]);
+                        else
+                            C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[r][c][j]);
+                    }
                 }
             }
         }
@@ -250,12 +273,12 @@ __global__ void round_ws_to_bf16(const float* __restrict__ ws, int M, int N,
     }
 }
 
-template <int RB, int PF>
+template <int RB, int PF, int CBW = 1>
 hipError_t launch_rb(const GemmArgs& a, hipStream_t stream)
 {
-    const int n_tiles = (a.N + BN - 1) / BN;
+    const int n_tiles = (a.N + 32 * CBW - 1) / (32 * CBW);
     const int m_tiles = (a.M + 32 * RB - 1) / (32 * RB);
-    gemm_bf16_kernel<RB, PF, false><<<dim3(n_tiles * m_tiles), dim3(256), 0, stream>>>(
+    gemm_bf16_kernel<RB, PF, false, CBW><<<dim3(n_tiles * m_tiles), dim3(256), 0, stream>>>(
         a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint16_t*)a.B, a.ldb, a.C, a.ldc,
         nullptr, m_tiles, 1);
     return hipGetLastError();
@@ -264,11 +287,11 @@ hipError_t launch_rb(const GemmArgs& a, hipStream_t stream)
 template <int RB, int PF>
 hipError_t launch_rb_split(const GemmArgs& a, float* ws, int splits, hipStream_t stream)
 {
-    const int n_tiles = (a.N + BN - 1) / BN;
+    const int n_tiles = (a.N + 31) / 32;
     const int m_tiles = (a.M + 32 * RB - 1) / (32 * RB);
     const int64_t n = (int64_t)a.M * a.N;
     fill_zero_f32<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(ws, n);
-    gemm_bf16_kernel<RB, PF, true><<<dim3(n_tiles * m_tiles, splits), dim3(256), 0, stream>>>(
+    gemm_bf16_kernel<RB, PF, true, 1><<<dim3(n_tiles * m_tiles, splits), dim3(256), 0, stream>>>(
         a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint16_t*)a.B, a.ldb, a.C, a.ldc,
         ws, m_tiles, splits);
     round_ws_to_bf16<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(ws, a.M, a.N, a.C,
@@ -278,11 +301,19 @@ hipError_t launch_rb_split(const GemmArgs& a, float* ws, int splits, hipStream_t
 
 }  // namespace
 
+// Launch geometry (tile sharing only; every choice runs the same arithmetic
+// per element): 64 x 64 tiles, two stages in flight, once they still give
+// every compute unit a workgroup -- A rows then serve twice the columns
+// (K = N = 8192: M = 128 73.2 -> 52.6 us, M = 256 123.4 -> 81.0 us) --
+// else 64 x 32 tiles streaming N/32 column strips.
 hipError_t launch_bf16(const GemmArgs& a, const Schedule& s, hipStream_t stream)
 {
     switch (s.rb) {
     case 1: return launch_rb<1, 8>(a, stream);
-    case 2: return launch_rb<2, 6>(a, stream);
+    case 2:
+        if ((int64_t)((a.M + 63) / 64) * ((a.N + 63) / 64) >= 256)
+            return launch_rb<2, 2, 2>(a, stream);
+        return launch_rb<2, 6>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

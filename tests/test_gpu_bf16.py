@@ -245,7 +245,7 @@ def test_splitk_comparator_is_flagged(bg, c2):
 @pytest.mark.parametrize("M,N,K", [(17, 256, 512), (37, 100, 203), (1, 8, 1), (65, 40, 129),
                                    (3, 2048, 7168), (16, 1000, 777), (9, 8200, 300),
                                    (4, 8192, 320), (7, 8192, 200), (6, 1000, 777), (8, 2048, 96),
-                                   (40, 8200, 200), (64, 8192, 96),
+                                   (40, 8200, 200), (64, 8192, 96), (200, 8200, 300), (130, 8192, 96),
                                    (130, 264, 1000), (1, 8192, 8192), (200, 96, 4096)])
 def test_bt_bitwise_equal_to_rowmajor(bg, M, N, K):
     """Storing the weights transposed changes only the data movement: the same
@@ -280,7 +280,7 @@ def test_bt_c2_invariance_all_m(bg, c2):
 @pytest.mark.parametrize("M,N,K", [(17, 256, 512), (37, 100, 203), (1, 8, 1), (65, 40, 129),
                                    (3, 2048, 7168), (16, 1000, 777), (9, 8200, 300),
                                    (4, 8192, 320), (7, 8192, 200), (6, 1000, 777), (8, 2048, 96),
-                                   (40, 8200, 200), (64, 8192, 96),
+                                   (40, 8200, 200), (64, 8192, 96), (200, 8200, 300), (130, 8192, 96),
                                    (130, 264, 1000), (200, 96, 4096), (256, 2048, 512),
                                    (300, 4096, 256)])
 def test_packed_bitwise_equal_to_rowmajor(bg, M, N, K):
