@@ -11,9 +11,10 @@
 // lane per K step, no LDS, no transpose), PF stages ahead, so the weight
 // stream is a set of long contiguous runs.
 //
-// Workgroup: 128 threads = 2 waves, output tile 16*RB x 32; wave w owns
-// columns n0 + 16w .. +15 and all RB row blocks of the tile.  The A tile is
-// shared through LDS (double-buffered, 16-byte chunks XOR-swizzled by row).
+// Workgroup: 128 threads = 2 waves, output tile 16*RB x 32 (RB = 1, 2 or 4
+// by M); wave w owns columns n0 + 16w .. +15 and all RB row blocks of the
+// tile.  The A tile is shared through LDS (double-buffered, 16-byte chunks
+// XOR-swizzled by row).
 #include "common.h"
 #include "launch.h"
 
@@ -157,18 +158,36 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_bt_kernel(
     }
 }
 
-}  // namespace
-
-hipError_t launch_bf16_bt(const GemmArgs& a, const Schedule& s, hipStream_t stream)
+template <int RB, int PF>
+hipError_t launch_rb(const GemmArgs& a, hipStream_t stream)
 {
-    (void)s;
-    constexpr int RB = 1;
     const int n_tiles = (a.N + BN - 1) / BN;
     const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-    gemm_bf16_bt_kernel<RB, 4><<<dim3(n_tiles * m_tiles), dim3(NTHR), 0, stream>>>(
+    gemm_bf16_bt_kernel<RB, PF><<<dim3(n_tiles * m_tiles), dim3(NTHR), 0, stream>>>(
         a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint16_t*)a.B, a.ldb, a.C, a.ldc,
         m_tiles);
     return hipGetLastError();
+}
+
+}  // namespace
+
+// Launch geometry (tile sharing only; every choice runs the same arithmetic
+// per element): one 16-row block per workgroup up to 16 rows, two up to 32,
+// four beyond (weight rows then serve 64 rows of A instead of 16; K = N =
+// 8192, M = 64: 72.5 -> 41.5 us, M = 256: 266.5 -> 121.7 us), fewer while
+// the tiles would leave compute units without a workgroup.
+hipError_t launch_bf16_bt(const GemmArgs& a, const Schedule& s, hipStream_t stream)
+{
+    (void)s;
+    const int64_t n_tiles = (a.N + BN - 1) / BN;
+    int rb = a.M > 32 ? 4 : (a.M > 16 ? 2 : 1);
+    while (rb > 1 && ((a.M + 16 * rb - 1) / (16 * rb)) * n_tiles < 256)
+        rb /= 2;
+    switch (rb) {
+    case 4: return launch_rb<4, 2>(a, stream);
+    case 2: return launch_rb<2, 2>(a, stream);
+    default: return launch_rb<1, 4>(a, stream);
+    }
 }
 
 }  // namespace bigemm

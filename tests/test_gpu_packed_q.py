@@ -212,10 +212,11 @@ def test_fp4_k_tail_ignores_pitch_padding(bg):
         assert np.array_equal(got_p, got)
 
 
-@pytest.mark.parametrize("M", [19, 3, 6])
-def test_bf16_k_tail_ignores_pitch_padding(bg, M):
-    # the same property for the three bf16 layouts (K = 200: a partial 32-step)
-    N, K = 272, 200
+@pytest.mark.parametrize("M,N", [(19, 272), (3, 272), (6, 272), (130, 8192)])
+def test_bf16_k_tail_ignores_pitch_padding(bg, M, N):
+    # the same property for the three bf16 layouts (K = 200: a partial 32-step),
+    # on small tiles and on the large-M tiles of each layout
+    K = 200
     Ah = inputs.normal_bf16((M, K), 1.0, 971)
     Bh = inputs.normal_bf16((K, N), 0.02, 972)
     Ap = np.full((M, K + 56), 0x7FC0, np.uint16)
