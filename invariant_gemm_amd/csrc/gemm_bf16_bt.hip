@@ -11,21 +11,19 @@
 // lane per K step, no LDS, no transpose), PF stages ahead, so the weight
 // stream is a set of long contiguous runs.
 //
-// Workgroup: 128 threads = 2 waves, output tile 16*RB x 32 (RB = 1, 2 or 4
-// by M); wave w owns columns n0 + 16w .. +15 and all RB row blocks of the
-// tile.  The A tile is shared through LDS (double-buffered, 16-byte chunks
-// XOR-swizzled by row).
+// Workgroup: WAVES = 2 or 4 waves, output tile 16*RB x 16*WAVES (RB = 1, 2
+// or 4, both by M); wave w owns columns n0 + 16w .. +15 and all RB row
+// blocks of the tile.  The A tile is shared through LDS (double-buffered,
+// 16-byte chunks XOR-swizzled by row).
 #include "common.h"
 #include "launch.h"
 
 namespace bigemm {
 namespace {
 
-constexpr int BN = 32;
 constexpr int BKS = 256;                  // K per stage
 constexpr int KSTEP = 32;
 constexpr int KS_PER_ST = BKS / KSTEP;    // 8
-constexpr int NTHR = 128;
 
 __device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
 {
@@ -38,16 +36,19 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int valid)
     return v;
 }
 
-template <int RB, int PF>
-__global__ __launch_bounds__(NTHR) void gemm_bf16_bt_kernel(
+template <int RB, int PF, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_bf16_bt_kernel(
     int M, int N, int K,
     const uint16_t* __restrict__ A, int64_t lda,
     const uint16_t* __restrict__ Bt, int64_t ldbt,
     uint16_t* __restrict__ C, int64_t ldc, int m_tiles)
 {
+    constexpr int NTHR = 64 * WAVES;
+    constexpr int BN = 16 * WAVES;
     constexpr int BM = 16 * RB;
     constexpr int A_STAGE = BM * BKS * 2;             // bytes
     constexpr int A_LD = A_STAGE / (NTHR * 16);       // chunks per thread per stage
+    static_assert(A_LD * NTHR * 16 == A_STAGE, "A stage must split evenly over the threads");
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * A_STAGE];
 
     const int tid = threadIdx.x;
@@ -158,12 +159,12 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_bt_kernel(
     }
 }
 
-template <int RB, int PF>
+template <int RB, int PF, int WAVES = 2>
 hipError_t launch_rb(const GemmArgs& a, hipStream_t stream)
 {
-    const int n_tiles = (a.N + BN - 1) / BN;
+    const int n_tiles = (a.N + 16 * WAVES - 1) / (16 * WAVES);
     const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-    gemm_bf16_bt_kernel<RB, PF><<<dim3(n_tiles * m_tiles), dim3(NTHR), 0, stream>>>(
+    gemm_bf16_bt_kernel<RB, PF, WAVES><<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0, stream>>>(
         a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint16_t*)a.B, a.ldb, a.C, a.ldc,
         m_tiles);
     return hipGetLastError();
@@ -172,22 +173,27 @@ hipError_t launch_rb(const GemmArgs& a, hipStream_t stream)
 }  // namespace
 
 // Launch geometry (tile sharing only; every choice runs the same arithmetic
-// per element): one 16-row block per workgroup up to 16 rows, two up to 32,
-// four beyond (weight rows then serve 64 rows of A instead of 16; K = N =
-// 8192, M = 64: 72.5 -> 41.5 us, M = 256: 266.5 -> 121.7 us), fewer while
-// the tiles would leave compute units without a workgroup.
+// per element): taller and wider tiles as M grows, each only while its tiles
+// still give every compute unit a workgroup -- 64 x 64 (four waves) beyond
+// 64 rows, 32 x 64 beyond 32, 32 x 32 beyond 16, else 16 x 32 streaming.
+// K = N = 8192: M = 64 72.5 -> 41.0 us, M = 128 136.2 -> 53.9 us, M = 256
+// 266.5 -> 89.6 us against one 16-row block per workgroup.
 hipError_t launch_bf16_bt(const GemmArgs& a, const Schedule& s, hipStream_t stream)
 {
     (void)s;
-    const int64_t n_tiles = (a.N + BN - 1) / BN;
-    int rb = a.M > 32 ? 4 : (a.M > 16 ? 2 : 1);
-    while (rb > 1 && ((a.M + 16 * rb - 1) / (16 * rb)) * n_tiles < 256)
-        rb /= 2;
-    switch (rb) {
-    case 4: return launch_rb<4, 2>(a, stream);
-    case 2: return launch_rb<2, 2>(a, stream);
-    default: return launch_rb<1, 4>(a, stream);
-    }
+    const int64_t M = a.M, N = a.N;
+    auto tiles = [&](int rb, int waves) {
+        return ((M + 16 * rb - 1) / (16 * rb)) * ((N + 16 * waves - 1) / (16 * waves));
+    };
+    if (M > 64 && tiles(4, 4) >= 256)
+        return launch_rb<4, 2, 4>(a, stream);
+    if (M > 32 && tiles(2, 4) >= 256)
+        return launch_rb<2, 2, 4>(a, stream);
+    if (M > 32 && tiles(4, 2) >= 256)
+        return launch_rb<4, 2, 2>(a, stream);
+    if (M > 16 && tiles(2, 2) >= 256)
+        return launch_rb<2, 2, 2>(a, stream);
+    return launch_rb<1, 4, 2>(a, stream);
 }
 
 }  // namespace bigemm
