@@ -38,7 +38,7 @@ constexpr int KBK = 128;       // K per MFMA (and per activation scale)
 constexpr int CTILE = 1024;    // code bytes per (column block, K block)
 constexpr int STILE = 64;      // scale bytes per (column block, K block)
 
-template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool NT>
+template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool NT, int AR>
 __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
     int M, int N, int K,
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t ldsa,
@@ -51,6 +51,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
     constexpr int B_BYTES = CB * KB_ST * CTILE;
     constexpr int S_DW = CB * KB_ST * STILE / 4;      // scale dwords per stage
     constexpr int A_LD = A_BYTES / (NTHR * 16);
+    constexpr int A_LDU = (AR * CPR + NTHR - 1) / NTHR;   // loads that cover rows < AR
     constexpr int B_LD = B_BYTES / (NTHR * 16);
     constexpr int SA_N = BM * KB_ST;
     constexpr int SA_LD = (SA_N + NTHR - 1) / NTHR;
@@ -59,6 +60,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
     constexpr int WGR = RB / WR;
     constexpr int WGC = CB / WC;
     static_assert(A_LD * NTHR * 16 == A_BYTES, "A stage must split evenly over the threads");
+    static_assert(AR >= 1 && AR <= BM, "staged rows must lie in the tile");
     static_assert(B_LD * NTHR * 16 == B_BYTES, "B stage must split evenly over the threads");
     static_assert(S_DW <= NTHR, "one scale dword per thread and stage");
     static_assert(WGR * WR == RB && WGC * WC == CB && WGR * WGC <= WAVES, "wave tiling");
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
             live ? clamp_bytes(((int64_t)(rows_valid - 1) * ldsa + nkb - kb0) * 4) : 0u);
         const __amdgpu_buffer_rsrc_t rsc = make_rsrc(scales, live ? sc_bytes : 0u);
 #pragma unroll
-        for (int j = 0; j < A_LD; ++j)
+        for (int j = 0; j < A_LDU; ++j)
             ar[j] = buf_load16(ra, a_voff[j]);
 #pragma unroll
         for (int j = 0; j < B_LD; ++j) {
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
                 // weight scales may not, so all three are cleared.
                 const int qv = nkb - s * KB_ST;
 #pragma unroll
-                for (int j = 0; j < A_LD; ++j) {
+                for (int j = 0; j < A_LDU; ++j) {
                     const int u = j * NTHR + tid;
                     if (((u % CPR) ^ swz<CPR>(u / CPR)) >= 8 * qv)
                         areg[p][j] = u32x4{0u, 0u, 0u, 0u};
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
                     screg[p] = 0u;
             }
 #pragma unroll
-            for (int j = 0; j < A_LD; ++j)
+            for (int j = 0; j < A_LDU; ++j)
                 *reinterpret_cast<u32x4*>(buf + (j * NTHR + tid) * 16) = areg[p][j];
 #pragma unroll
             for (int j = 0; j < B_LD; ++j)
@@ -308,12 +310,13 @@ __global__ void pack_mxfp4_kernel(int N, int K, const uint8_t* __restrict__ Bq, 
     Bp[(int64_t)NB * KB * CTILE + t * STILE + l] = n < N ? sE[(int64_t)(4 * kb + g) * ldse + n] : 0u;
 }
 
-template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool NT = true>
+template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool NT = true,
+          int AR = 16 * RB>
 hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 {
     const int n_tiles = ((a.N + 15) / 16 + CB - 1) / CB;
     const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-    gemm_w4a8_packed_kernel<WAVES, RB, CB, WR, WC, KB_ST, PF, NT>
+    gemm_w4a8_packed_kernel<WAVES, RB, CB, WR, WC, KB_ST, PF, NT, AR>
         <<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0, stream>>>(
             a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
             (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
@@ -325,7 +328,10 @@ hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 // Launch geometry (tile sharing only; the per-element arithmetic is the same
 // for all), from a sweep on the K = 4096, N = 14336 weight shape: for
 // M <= 16 four waves each stream their own 16-column block and share one
-// staged activation tile; 64 x 64 tiles above that, with one K block per
+// staged activation tile (of which only the first 8 rows are loaded when the
+// call has no more: LDS rows past them keep stale bytes, which reach only
+// output rows that are never stored, an MFMA output row depending on its own
+// A row alone); 64 x 64 tiles above that, with one K block per
 // stage once M > 128.
 hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream)
 {
@@ -333,6 +339,8 @@ hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream)
         return launch_geometry<4, 4, 4, 2, 2, 1, 4, false>(a, stream);   // weights shared by row tiles
     if (a.M > 16)
         return launch_geometry<4, 4, 4, 2, 2, 2, 2>(a, stream);
+    if (a.M <= 8)
+        return launch_geometry<4, 1, 4, 1, 1, 4, 4, true, 8>(a, stream);   // 8 rows of A staged
     return launch_geometry<4, 1, 4, 1, 1, 4, 4>(a, stream);
 }
 

@@ -43,6 +43,7 @@ def fp8_case(M, N, K, seed):
 # x 16 columns, then 64 x 16, 64 x 32 and 64 x 64 tiles once they still fill
 # the compute units.
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (5, 300, 384), (3, 4112, 256), (16, 4096, 128),
+                                   (8, 2048, 1152), (7, 144, 896), (9, 272, 1152),
                                    (17, 144, 1024), (40, 272, 512),
                                    (64, 2048, 896), (200, 2048, 1024), (512, 2048, 512),
                                    (129, 4112, 256)])
@@ -179,7 +180,7 @@ def test_fp8_k_tail_ignores_pitch_padding(bg):
     """K = 384 leaves the last pipeline stage partly past K at every geometry.
     The row pitches of A and sA are padded with NaN codes / NaN scales, which
     must never reach the result (blocks past K contribute exact zeros)."""
-    for M, N, K in ((5, 272, 384), (70, 144, 640), (300, 2048, 384)):
+    for M, N, K in ((5, 272, 384), (8, 144, 1152), (70, 144, 640), (300, 2048, 384)):
         qA, sA, qB, sB = fp8_case(M, N, K, 950 + M)
         Ap = np.full((M, K + 128), 0x7F, np.uint8)          # e4m3fn NaN past K
         Ap[:, :K] = qA
