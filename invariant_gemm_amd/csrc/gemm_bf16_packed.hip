@@ -15,7 +15,7 @@
 // its batch companions (the invariance definition in section
 // "什么是batch invariance" of the QbitAI article).
 //
-// Seven launch geometries in three families share that arithmetic (the
+// Eight launch geometries in three families share that arithmetic (the
 // dual-program idea of section 4.1 of the lshu.cn article and section 3.3 of
 // the wmrh.cn blog, applied to the GEMM: programs for "GPU not saturated" /
 // "saturated" whose results are bit-identical):
@@ -30,7 +30,8 @@
 // the call has no more rows than that, and the one-wave geometry can run on
 // half blocks (8 columns per workgroup) when N/16 blocks are too few.
 // Weight loads are marked non-temporal (read once) except in the large
-// geometry, whose four row tiles share each column strip through L2.
+// geometry, whose four row tiles share each column strip through L2, and in a
+// medium variant for grouped calls whose many row tiles share the strips.
 #include <algorithm>
 
 #include "common.h"
@@ -350,6 +351,7 @@ hipError_t launch_packed(const GemmArgs& a, const GroupArgs* grp, int geometry, 
     case 2: return launch_geometry<2, 1, 4, 4, 4>(a, grp, stream);
     case 1: return launch_geometry<2, 1, 2, 8, 2>(a, grp, stream);
     case 7: return launch_geometry<4, 1, 2, 8, 2>(a, grp, stream);   // 32 x 64, four waves
+    case 8: return launch_geometry<4, 1, 4, 4, 4, false>(a, grp, stream);   // 64 x 64, B via L2
     case 5:
         // at most 4 or 8 rows in the call: stage only those rows of A
         if (a.M <= 4) return launch_geometry<1, 1, 1, 16, 2, true, 4>(a, grp, stream);
@@ -390,6 +392,27 @@ hipError_t launch_bf16_packed(const GemmArgs& a, hipStream_t stream)
 // gives the same bits).  The one-wave streaming geometry only pays while the
 // groups that can hold rows -- at most min(groups, M) -- leave compute units
 // idle with two-wave workgroups.
+//
+// From 25 rows per group on, the 64-row tiles are chosen from the workgroups
+// the call is expected to occupy: T rows over k groups fill about T/64 + k/2
+// row slots (a group wastes half a tile on average).  64 x 64 tiles while
+// they need at most one workgroup per compute unit; else 64 x 128 while those
+// fill at least three quarters of the compute units, or fill their last
+// round that well; else 64 x 64 with the weights kept in L2 for the row
+// tiles that share them.  E = 8, K = 7168, N = 2048: 256 tokens 68.7 -> 42.9
+// us, 512 tokens 88.4 -> 59.8 us, 1024 tokens 128.9 -> 88.6 us.
+int grouped_wide_geometry(int64_t M, int N, int64_t k)
+{
+    const int64_t slots = (M + 32 * k + 63) / 64;
+    const int64_t nb = (N + 15) / 16;
+    const int64_t medium = slots * ((nb + 3) / 4), large = slots * ((nb + 7) / 8);
+    if (medium <= 256)
+        return 3;
+    if (large <= 256)
+        return large >= 192 ? 4 : 3;
+    return large % 256 == 0 || large % 256 >= 192 ? 4 : 8;
+}
+
 hipError_t launch_bf16_grouped_packed(const GemmArgs& a, const GroupArgs& g, hipStream_t stream)
 {
     const int mean = (a.M + g.n_groups - 1) / g.n_groups;
@@ -397,6 +420,8 @@ hipError_t launch_bf16_grouped_packed(const GemmArgs& a, const GroupArgs& g, hip
     const int64_t active = std::min<int64_t>(g.n_groups, a.M);
     if (geometry == 5 && active * ((a.N + 31) / 32) >= 256)
         geometry = 0;
+    if (mean > 24)
+        geometry = grouped_wide_geometry(a.M, a.N, active);
     // slot order: row slot first from four rows per group on (E = 8, N = 2048:
     // 64 tokens 45.7 -> 38.9 us, 512 tokens 91.1 -> 89.5 us); below that the
     // XCD-contiguous column order measured faster (8 tokens 27.5 vs 30.2 us)

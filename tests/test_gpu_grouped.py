@@ -103,7 +103,7 @@ def test_every_geometry(bg):
     Bd = [dev_bf16(b) for b in Bh]
     Bp = bg.pack_b_bf16_grouped(Bd)
     single = [bg.pack_b_bf16(b) for b in Bd]
-    for M in (1, 2, 4, 7, 70, 130, 250, 600, 2000):
+    for M in (1, 2, 4, 7, 70, 100, 130, 250, 600, 900, 2000):
         Ah = inputs.normal_bf16((M, K), 1.0, 1410 + M)
         expert = inputs.route_tokens(M, E, 1420 + M, 1.0)
         order, offsets = inputs.group_by_expert(expert, E)
