@@ -641,7 +641,16 @@ def pmc_counters(dirs):
     = TA_ADDR_STALLED_BY_TC_CYCLES / (CUs x duration x 2.4 GHz)."""
     import csv
     import glob
-    return _counters_per_m(dirs, [("gemm_bf16_packed_kernel", SWEEP_C2)], csv, glob)[0] | {
+    res = _counters_per_m(dirs, [("gemm_bf16_packed_kernel", SWEEP_C2)], csv, glob)[0]
+    # MFMA work actually issued (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts 512 flops)
+    # against 2MNK: every 16 x 16 block of a tile runs its whole K chain once,
+    # so the ratio is the tile's rows over M (16-row blocks at M < 16)
+    for M, row in res["per_m"].items():
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in row:
+            fl = row["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+            row["derived"]["mfma_flops"] = fl
+            row["derived"]["mfma_flops_over_2mnk"] = round(fl / flops(int(M), C2.N, C2.K), 4)
+    return res | {
         "kernel": "gemm_bf16_packed_kernel (bi_gemm_bf16_packed)",
         "kernel_sha256": kernel_sha256([os.path.join(ROOT, "invariant_gemm_amd", "csrc", f)
                                         for f in ("gemm_bf16_packed.hip", "common.h")])}
