@@ -894,7 +894,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the batch-invariant GEMM is timed on a single "
-              "MI355X; how the path would shard over GPUs is described in DESIGN.md.",
+              "MI355X (sharding the rows or the output columns over GPUs needs no exchange "
+              "between them; only the one-GPU path is implemented).",
               file=sys.stderr)
         sys.exit(2)
 
