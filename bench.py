@@ -367,7 +367,36 @@ def cpu_baseline(budget_s=12.0):
     out["sample_1core"] = (f"fp64 oracle, one thread, on 4 rows of the same batch: "
                            f"{flops(4, N, K) / 1e9:.2f} GFLOP in {t1:.2f} s")
     out["host"] = host_info()
+    out["formats"] = cpu_baseline_formats()
     return out
+
+
+def cpu_baseline_formats(budget_s=3.0):
+    """The same oracle on the quantised configurations, on a few rows each
+    (the fp64 work per row is fixed by N and K): fp8 block-scaled K = 7168,
+    N = 2048 and fp4 weight-only K = 4096, N = 14336, seeded as the GPU legs."""
+    import oracle
+    from invariant_gemm_amd import inputs
+    res = {}
+    qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((16, 7168), 1.0, 301))
+    qB, sB = inputs.quant_fp8_tiles(inputs.normal_f32((7168, 2048), 1.0, 302))
+    A4 = inputs.normal_bf16((16, 4096), 1.0, 401)
+    Bq, s4 = inputs.quant_fp4_weights(inputs.normal_f32((4096, 14336), 0.02, 402))
+    for name, N, K, run in (
+            ("fp8_blockscaled_K7168_N2048", 2048, 7168,
+             lambda a, b: oracle.gemm_fp8bs(np.ascontiguousarray(qA[a:b]), np.ascontiguousarray(sA[a:b]), qB, sB)),
+            ("fp4_weight_only_K4096_N14336", 14336, 4096,
+             lambda a, b: oracle.gemm_fp4w(np.ascontiguousarray(A4[a:b]), Bq, s4, 14336))):
+        rows, t_tot = 0, 0.0
+        while t_tot < budget_s and rows < 16:
+            t0 = time.perf_counter()
+            run(rows, rows + 2)
+            t_tot += time.perf_counter() - t0
+            rows += 2
+        res[name] = {"value": round(flops(rows, N, K) / t_tot / 1e12, 5), "unit": "TFLOP/s",
+                     "sample": f"fp64 oracle on {rows} rows: {flops(rows, N, K) / 1e9:.2f} GFLOP "
+                               f"in {t_tot:.2f} s"}
+    return res
 
 
 def host_info():
