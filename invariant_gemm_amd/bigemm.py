@@ -135,7 +135,30 @@ def schedule(dtype: int, N: int, K: int) -> dict:
 def _out(M, N, device, out):
     if out is None:
         return torch.empty((M, N), dtype=torch.bfloat16, device=device)
-    return _mat(out, _BF16, "out")
+    out = _mat(out, _BF16, "out")
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out: expected shape {(M, N)}, got {tuple(out.shape)}")
+    _same_device(device, out=out)
+    return out
+
+
+def _same_device(device, **tensors):
+    for name, t in tensors.items():
+        if t.device != device:
+            raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _shape(t: torch.Tensor, shape, name: str):
+    """The C ABI sees pointers and pitches only, so every operand's extent is
+    checked here: a short tensor would otherwise be read or written past its end."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _blocks(K: int, blk: int, what: str) -> int:
+    if K % blk:
+        raise ValueError(f"{what}: K = {K} is not a multiple of {blk}")
+    return K // blk
 
 
 def gemm_bf16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -146,6 +169,7 @@ def gemm_bf16(A: torch.Tensor, B: torch.Tensor, out: torch.Tensor | None = None)
     if B.shape[0] != K:
         raise ValueError("A and B inner dimensions differ")
     N = B.shape[1]
+    _same_device(A.device, B=B)
     C = _out(M, N, A.device, out)
     _check(lib.bi_gemm_bf16(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
                             C.data_ptr(), _ld(C), _stream()), "bi_gemm_bf16")
@@ -160,6 +184,7 @@ def gemm_bf16_bt(A: torch.Tensor, Bt: torch.Tensor, out: torch.Tensor | None = N
     if Bt.shape[1] != K:
         raise ValueError("A and Bt inner dimensions differ")
     N = Bt.shape[0]
+    _same_device(A.device, Bt=Bt)
     C = _out(M, N, A.device, out)
     _check(lib.bi_gemm_bf16_bt(M, N, K, A.data_ptr(), _ld(A), Bt.data_ptr(), _ld(Bt),
                                C.data_ptr(), _ld(C), _stream()), "bi_gemm_bf16_bt")
@@ -194,6 +219,7 @@ def gemm_bf16_packed(A: torch.Tensor, Bp: PackedWeights, out: torch.Tensor | Non
     M, K = A.shape
     if Bp.dtype != BI_BF16 or Bp.K != K:
         raise ValueError("packed weights do not match A")
+    _same_device(A.device, Bp=Bp.data)
     C = _out(M, Bp.N, A.device, out)
     _check(lib.bi_gemm_bf16_packed(M, Bp.N, K, A.data_ptr(), _ld(A), Bp.data.data_ptr(),
                                    Bp.data.numel(), C.data_ptr(), _ld(C), _stream()),
@@ -227,6 +253,7 @@ def gemm_bf16_grouped_packed(A: torch.Tensor, offsets: torch.Tensor, Bp: PackedW
     if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1 \
             or offsets.numel() != Bp.groups + 1 or (offsets.numel() > 1 and offsets.stride(0) != 1):
         raise ValueError("offsets: a contiguous int32 device tensor of G + 1 entries")
+    _same_device(A.device, Bp=Bp.data, offsets=offsets)
     C = _out(M, Bp.N, A.device, out)
     _check(lib.bi_gemm_bf16_grouped_packed(Bp.groups, offsets.data_ptr(), M, Bp.N, K, A.data_ptr(),
                                            _ld(A), Bp.data.data_ptr(), Bp.data.numel(),
@@ -246,6 +273,10 @@ def gemm_fp8_blockscaled(A: torch.Tensor, sA: torch.Tensor, B: torch.Tensor, sB:
     if B.shape[0] != K:
         raise ValueError("A and B inner dimensions differ")
     N = B.shape[1]
+    kb = _blocks(K, 128, "gemm_fp8_blockscaled")
+    _shape(sA, (M, kb), "sA")
+    _shape(sB, (kb, (N + 127) // 128), "sB")
+    _same_device(A.device, sA=sA, B=B, sB=sB)
     C = _out(M, N, A.device, out)
     _check(lib.bi_gemm_fp8_blockscaled(M, N, K, A.data_ptr(), _ld(A), sA.data_ptr(), _ld(sA),
                                        B.data_ptr(), _ld(B), sB.data_ptr(), _ld(sB),
@@ -262,6 +293,11 @@ def gemm_fp4_w(A: torch.Tensor, Bq: torch.Tensor, sB: torch.Tensor, N: int,
     M, K = A.shape
     if Bq.shape[0] != K:
         raise ValueError("A and Bq inner dimensions differ")
+    if N % 2:
+        raise ValueError(f"gemm_fp4_w: N = {N} must be even")
+    _shape(Bq, (K, N // 2), "Bq")
+    _shape(sB, (_blocks(K, 32, "gemm_fp4_w"), N), "sB")
+    _same_device(A.device, Bq=Bq, sB=sB)
     C = _out(M, N, A.device, out)
     _check(lib.bi_gemm_fp4_w(M, N, K, A.data_ptr(), _ld(A), Bq.data_ptr(), _ld(Bq),
                              sB.data_ptr(), _ld(sB), C.data_ptr(), _ld(C), _stream()),
@@ -289,6 +325,10 @@ def gemm_fp8_blockscaled_packed(A: torch.Tensor, sA: torch.Tensor, Bp: PackedWei
     M, K = A.shape
     if Bp.dtype != BI_FP8_BS or Bp.K != K:
         raise ValueError("packed weights do not match A")
+    kb = _blocks(K, 128, "gemm_fp8_blockscaled_packed")
+    _shape(sA, (M, kb), "sA")
+    _shape(sB, (kb, (Bp.N + 127) // 128), "sB")
+    _same_device(A.device, sA=sA, Bp=Bp.data, sB=sB)
     C = _out(M, Bp.N, A.device, out)
     _check(lib.bi_gemm_fp8_blockscaled_packed(M, Bp.N, K, A.data_ptr(), _ld(A), sA.data_ptr(),
                                               _ld(sA), Bp.data.data_ptr(), Bp.data.numel(),
@@ -302,6 +342,11 @@ def pack_b_fp4(Bq: torch.Tensor, sB: torch.Tensor, N: int) -> PackedWeights:
     Bq = _mat(Bq, _U8, "Bq")
     sB = _mat(sB, _U8, "sB")
     K = Bq.shape[0]
+    if N % 2:
+        raise ValueError(f"pack_b_fp4: N = {N} must be even")
+    _shape(Bq, (K, N // 2), "Bq")
+    _shape(sB, (_blocks(K, 32, "pack_b_fp4"), N), "sB")
+    _same_device(Bq.device, sB=sB)
     nbytes = packed_b_bytes(BI_FP4_W, N, K)
     buf = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=Bq.device)
     _check(lib.bi_pack_b_fp4(N, K, Bq.data_ptr(), _ld(Bq), sB.data_ptr(), _ld(sB),
@@ -315,6 +360,7 @@ def gemm_fp4_w_packed(A: torch.Tensor, Bp: PackedWeights, out: torch.Tensor | No
     M, K = A.shape
     if Bp.dtype != BI_FP4_W or Bp.K != K:
         raise ValueError("packed weights do not match A")
+    _same_device(A.device, Bp=Bp.data)
     C = _out(M, Bp.N, A.device, out)
     _check(lib.bi_gemm_fp4_w_packed(M, Bp.N, K, A.data_ptr(), _ld(A), Bp.data.data_ptr(),
                                     Bp.data.numel(), C.data_ptr(), _ld(C), _stream()),
@@ -327,6 +373,11 @@ def pack_b_mxfp4(Bq: torch.Tensor, sE: torch.Tensor, N: int) -> PackedWeights:
     Bq = _mat(Bq, _U8, "Bq")
     sE = _mat(sE, _U8 + (getattr(torch, "float8_e8m0fnu", torch.uint8),), "sE")
     K = Bq.shape[0]
+    if N % 2:
+        raise ValueError(f"pack_b_mxfp4: N = {N} must be even")
+    _shape(Bq, (K, N // 2), "Bq")
+    _shape(sE, (_blocks(K, 32, "pack_b_mxfp4"), N), "sE")
+    _same_device(Bq.device, sE=sE)
     nbytes = packed_b_bytes(BI_W4A8, N, K)
     buf = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=Bq.device)
     _check(lib.bi_pack_b_mxfp4(N, K, Bq.data_ptr(), _ld(Bq), sE.data_ptr(), _ld(sE),
@@ -342,6 +393,8 @@ def gemm_w4a8_packed(A: torch.Tensor, sA: torch.Tensor, Bp: PackedWeights,
     M, K = A.shape
     if Bp.dtype != BI_W4A8 or Bp.K != K:
         raise ValueError("packed weights do not match A")
+    _shape(sA, (M, _blocks(K, 128, "gemm_w4a8_packed")), "sA")
+    _same_device(A.device, sA=sA, Bp=Bp.data)
     C = _out(M, Bp.N, A.device, out)
     _check(lib.bi_gemm_w4a8_packed(M, Bp.N, K, A.data_ptr(), _ld(A), sA.data_ptr(), _ld(sA),
                                    Bp.data.data_ptr(), Bp.data.numel(), C.data_ptr(), _ld(C),
@@ -359,10 +412,13 @@ def gemm_bf16_splitk(A: torch.Tensor, B: torch.Tensor, workspace: torch.Tensor, 
     A = _mat(A, _BF16, "A")
     B = _mat(B, _BF16, "B")
     M, K = A.shape
+    if B.shape[0] != K:
+        raise ValueError("A and B inner dimensions differ")
     N = B.shape[1]
-    C = _out(M, N, A.device, out)
     if workspace.dtype != torch.float32 or not workspace.is_cuda:
         raise TypeError("workspace must be a float32 device tensor")
+    _same_device(A.device, B=B, workspace=workspace)
+    C = _out(M, N, A.device, out)
     _check(lib.bi_gemm_bf16_splitk(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
                                    C.data_ptr(), _ld(C), workspace.data_ptr(),
                                    workspace.numel() * 4, splits, _stream()), "bi_gemm_bf16_splitk")
@@ -401,12 +457,24 @@ def decode_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens
         raise TypeError("seq_lens: int32 device vector")
     B, Hq, D = Q.shape
     Hkv, Lmax = K.shape[1], K.shape[2]
+    if K.shape[0] != B or K.shape[3] != D:
+        raise ValueError(f"K, V: expected [{B}, Hkv, Lmax, {D}], got {tuple(K.shape)}")
+    _shape(seq_lens, (B,), "seq_lens")
+    _same_device(Q.device, K=K, V=V, seq_lens=seq_lens)
     k = _ATTN_KERNELS[kernel]
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=Q.device)
+    elif out.dtype not in _BF16 or not out.is_contiguous() or tuple(out.shape) != (B, Hq, D):
+        raise ValueError(f"out: expected a contiguous bf16 tensor of shape {(B, Hq, D)}")
+    else:
+        _same_device(Q.device, out=out)
     need = decode_attention_workspace_bytes(B, Hq, Hkv, Lmax)
     if workspace is None and k != ATTN_SINGLE and need:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=Q.device)
+    if workspace is not None:
+        if not workspace.is_contiguous():
+            raise ValueError("workspace: must be contiguous")
+        _same_device(Q.device, workspace=workspace)
     wp, wb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) \
         if workspace is not None else (None, 0)
     _check(lib.bi_decode_attention_bf16(B, Hq, Hkv, D, Lmax, Q.data_ptr(), K.data_ptr(),

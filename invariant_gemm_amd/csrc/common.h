@@ -36,6 +36,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return u >> 16;
 }
 
+// GEMM epilogue: fp32 accumulator -> bf16 output, RNE, subnormals kept, and
+// a zero result always written as +0.  The sign of an fp32 zero accumulator
+// depends on how many all-zero K steps (zero-padded stages) follow the last
+// nonzero one -- an underflowed negative sum is -0 until a +0 product is
+// added -- and that count follows the launch geometry, hence M.  No nonzero
+// value depends on the sign of a zero, so writing every zero as +0 keeps the
+// output bits the same in every geometry.
+__device__ __forceinline__ uint32_t gemm_out_bf16(float acc)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, acc);
+    return (u & 0x7FFFFFFFu) == 0 ? 0u : f32_to_bf16_rne(acc);
+}
+
 // Workgroups are dispatched round-robin over the XCDs (id % 8).  Remap the
 // dispatch id so that each XCD receives a contiguous range of tile ids: the
 // tiles sharing B columns (and the M tiles of one N strip) then meet in the

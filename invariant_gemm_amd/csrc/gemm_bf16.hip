@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
                         if constexpr (SPLIT)
                             atomicAdd(ws + (int64_t)row * N + col, acc[r][c][j]);
                         else
-                            C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[r][c][j]);
+                            C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc[r][c][j]);
                     }
                 }
             }
@@ -269,7 +269,7 @@ __global__ void round_ws_to_bf16(const float* __restrict__ ws, int M, int N,
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < (int64_t)M * N) {
         const int64_t row = i / N, col = i - row * N;
-        C[row * ldc + col] = (uint16_t)f32_to_bf16_rne(ws[i]);
+        C[row * ldc + col] = (uint16_t)gemm_out_bf16(ws[i]);
     }
 }
 

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_bt_kernel(
         for (int j = 0; j < 4; ++j) {
             const int row = m0 + 16 * r + 4 * lg + j;
             if (row < M && col < N)
-                C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[r][j]);
+                C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc[r][j]);
         }
     }
 }

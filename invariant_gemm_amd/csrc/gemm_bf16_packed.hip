@@ -254,7 +254,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
             for (int j = 0; j < 4; ++j) {
                 const int row = m0 + 16 * r + 4 * lg + j;
                 if (row < row_end && col < N && (!HALF || li < 8))
-                    C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[r][c][j]);
+                    C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc[r][c][j]);
             }
         }
     }

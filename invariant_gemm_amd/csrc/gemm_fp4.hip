@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(
         for (int j = 0; j < 4; ++j) {
             const int row = m0 + 16 * rg + 4 * lg + j;
             if (row < M && col < N)
-                C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[j]);
+                C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc[j]);
         }
     }
 }

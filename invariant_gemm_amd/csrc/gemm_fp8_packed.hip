@@ -235,8 +235,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
                 // and MFMAs of different blocks overlap; (2) the ordered
                 // accumulation acc = fma(P, sA*sB, acc), blocks ascending.
                 // No per-block guard: blocks past K are all-zero (tail
-                // clearing above) and fma(+0, +0, acc) == acc bit for bit, as
-                // acc can never be -0.
+                // clearing above) and fma(+0, +0, acc) == acc for every
+                // nonzero acc; a -0 acc turns +0, which the epilogue writes
+                // as +0 anyway (gemm_out_bf16), so the bits are the same.
                 f32x4 P[KB_ST][WR][WC];
 #pragma unroll
                 for (int q = 0; q < KB_ST; ++q) {
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
                 for (int j = 0; j < 4; ++j) {
                     const int row = m0 + 16 * (wr0 + r) + 4 * lg + j;
                     if (row < M && col < N && (!HALF || li < 8))
-                        C[(int64_t)row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[r][c][j]);
+                        C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc[r][c][j]);
                 }
             }
         }

@@ -190,12 +190,15 @@ void ora_gemm_fp8bs(int64_t M, int64_t N, int64_t K,
             c[n] = 0.0;
             s[n] = 0.0;
         }
+        double e4m3[256];                      /* ora_dec_e4m3fn of every code */
+        for (int q = 0; q < 256; ++q)
+            e4m3[q] = ora_dec_e4m3fn((uint8_t)q);
         for (int64_t k = 0; k < K; ++k) {
-            double a = ora_dec_e4m3fn(A[m * lda + k]) * (double)sA[m * ldsa + k / 128];
+            double a = e4m3[A[m * lda + k]] * (double)sA[m * ldsa + k / 128];
             const uint8_t* brow = B + k * ldb;
             const float* srow = sB + (k / 128) * ldsb;
             for (int64_t n = n0; n < n1; ++n) {
-                double b = ora_dec_e4m3fn(brow[n]) * (double)srow[n / 128];
+                double b = e4m3[brow[n]] * (double)srow[n / 128];
                 double p = a * b;
                 c[n] += p;
                 s[n] += fabs(p);
@@ -232,13 +235,20 @@ void ora_gemm_w4a8(int64_t M, int64_t N, int64_t K,
             c[n] = 0.0;
             s[n] = 0.0;
         }
+        double e4m3[256], e8m0[256], e2m1[16]; /* the decoders' values of every code */
+        for (int q = 0; q < 256; ++q) {
+            e4m3[q] = ora_dec_e4m3fn((uint8_t)q);
+            e8m0[q] = ora_dec_e8m0((uint8_t)q);
+        }
+        for (int q = 0; q < 16; ++q)
+            e2m1[q] = ora_dec_e2m1((uint8_t)q);
         for (int64_t k = 0; k < K; ++k) {
-            double a = ora_dec_e4m3fn(qA[m * lda + k]) * (double)sA[m * ldsa + k / 128];
+            double a = e4m3[qA[m * lda + k]] * (double)sA[m * ldsa + k / 128];
             const uint8_t* brow = Bq + k * ldbq;
             const uint8_t* srow = sE + (k / 32) * ldse;
             for (int64_t n = n0; n < n1; ++n) {
                 uint8_t code = (uint8_t)((brow[n / 2] >> (4 * (n & 1))) & 15);
-                double b = ora_dec_e2m1(code) * ora_dec_e8m0(srow[n]);
+                double b = e2m1[code] * e8m0[srow[n]];
                 double p = a * b;
                 c[n] += p;
                 s[n] += fabs(p);
@@ -267,13 +277,18 @@ void ora_gemm_fp4w(int64_t M, int64_t N, int64_t K,
             c[n] = 0.0;
             s[n] = 0.0;
         }
+        double e4m3[256], e2m1[16];            /* the decoders' values of every code */
+        for (int q = 0; q < 256; ++q)
+            e4m3[q] = ora_dec_e4m3fn((uint8_t)q);
+        for (int q = 0; q < 16; ++q)
+            e2m1[q] = ora_dec_e2m1((uint8_t)q);
         for (int64_t k = 0; k < K; ++k) {
             double a = ora_dec_bf16(A[m * lda + k]);
             const uint8_t* brow = Bq + k * ldbq;
             const uint8_t* srow = sB + (k / 32) * ldsb;
             for (int64_t n = n0; n < n1; ++n) {
                 uint8_t code = (uint8_t)((brow[n / 2] >> (4 * (n & 1))) & 15);
-                double b = ora_dec_e2m1(code) * ora_dec_e4m3fn(srow[n]);
+                double b = e2m1[code] * e4m3[srow[n]];
                 double p = a * b;
                 c[n] += p;
                 s[n] += fabs(p);

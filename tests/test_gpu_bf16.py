@@ -15,6 +15,7 @@ import torch
 
 import oracle
 from invariant_gemm_amd import inputs
+from tests import full_size
 from tests.gpu_util import (bf16_vals, check_parity, dev_bf16, host_codes, require_gpu,
                             rows_equal)
 
@@ -181,9 +182,7 @@ def test_c1_invariance_and_parity(bg):
 
 @pytest.fixture(scope="module")
 def c2(bg):
-    K = N = 8192
-    pool = inputs.normal_bf16((256, K), 1.0, 201)
-    Bc = inputs.normal_bf16((K, N), 0.02, 202)
+    pool, Bc, _, _ = full_size.c2()
     return pool, Bc, dev_bf16(pool), dev_bf16(Bc)
 
 
@@ -208,12 +207,11 @@ def test_c2_invariance_all_m(bg, c2):
         assert bool(rows_equal(bg.gemm_bf16(A[:m], B), ref[:m]).all()), f"M={m}"
 
 
-def test_c2_parity_sampled_rows(bg, c2):
+def test_c2_parity_every_row(bg, c2):
     pool, Bc, A, B = c2
-    C = host_codes(bg.gemm_bf16(A, B))       # the M = 256 batch
-    rows = np.sort(inputs.rng(204).choice(256, size=6, replace=False))
-    C64, S = oracle.gemm_bf16(np.ascontiguousarray(pool[rows]), Bc)
-    check_parity(C[rows], C64, S, 8192, "C2 M=256 sampled rows")
+    _, _, C64, S = full_size.c2()
+    C = host_codes(bg.gemm_bf16(A, B))       # the M = 256 batch, every row
+    check_parity(full_size.all_rows(C, C64), C64, S, 8192, "C2 M=256 every row")
 
 
 # ------------------------------------------------------------------ negative control
@@ -308,5 +306,6 @@ def test_packed_c2_all_geometries_bitwise(bg, c2):
         p = torch.as_tensor(inputs.permutation(256, 208 + s), device="cuda")
         assert bool(rows_equal(bg.gemm_bf16_packed(A.index_select(0, p), Bp),
                                ref.index_select(0, p)).all()), f"shuffle {s}"
-    C64, S = oracle.gemm_bf16(np.ascontiguousarray(pool[[0, 77, 255]]), Bc)
-    check_parity(host_codes(ref[[0, 77, 255]]), C64, S, 8192, "packed C2")
+    # every row computed alone (M = 1), which all the comparisons above use
+    _, _, C64, S = full_size.c2()
+    check_parity(full_size.all_rows(host_codes(ref), C64), C64, S, 8192, "packed C2 rows at M=1")

@@ -9,6 +9,7 @@ import torch
 
 import oracle
 from invariant_gemm_amd import inputs
+from tests import full_size
 from tests.gpu_util import (check_parity, dev_bf16, dev_u8, host_codes, require_gpu, rows_equal)
 
 pytestmark = pytest.mark.gpu
@@ -91,8 +92,7 @@ def test_parity_random(bg, M, N, K):
 @pytest.fixture(scope="module")
 def c4(bg):
     # fp4 e2m1 weight-only K=4096, N=14336; weights N(0,0.02) before quantisation
-    A = inputs.normal_bf16((512, 4096), 1.0, 401)
-    Bq, sB = inputs.quant_fp4_weights(inputs.normal_f32((4096, 14336), 0.02, 402))
+    A, Bq, sB, _, _ = full_size.c4()
     return A, Bq, sB, dev_bf16(A), dev_u8(Bq), dev_u8(sB)
 
 
@@ -109,9 +109,8 @@ def test_c4_invariance(bg, c4):
         assert bool(ok.all()), f"shuffle {s}"
 
 
-def test_c4_parity_sampled_rows(bg, c4):
+def test_c4_parity_every_row(bg, c4):
     A, Bq, sB, Ad, Bd, sBd = c4
-    C = host_codes(bg.gemm_fp4_w(Ad, Bd, sBd, 14336))
-    rows = np.sort(inputs.rng(404).choice(512, size=4, replace=False))
-    C64, S = oracle.gemm_fp4w(np.ascontiguousarray(A[rows]), Bq, sB, 14336)
-    check_parity(C[rows], C64, S, 4096, "C4 M=512 sampled rows")
+    *_, C64, S = full_size.c4()
+    C = host_codes(bg.gemm_fp4_w(Ad, Bd, sBd, 14336))          # M = 512, every row
+    check_parity(full_size.all_rows(C, C64), C64, S, 4096, "C4 M=512 every row")

@@ -10,6 +10,7 @@ import torch
 
 import oracle
 from invariant_gemm_amd import inputs
+from tests import full_size
 from tests.gpu_util import check_parity, dev_f32, dev_u8, host_codes, require_gpu, rows_equal
 
 pytestmark = pytest.mark.gpu
@@ -107,8 +108,7 @@ def test_strided_scales_and_operands(bg):
 @pytest.fixture(scope="module")
 def c3(bg):
     # fp8 e4m3 K=7168, N=2048; activations 1x128 fp32 scales, weights 128x128
-    qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((512, 7168), 1.0, 301))
-    qB, sB = inputs.quant_fp8_tiles(inputs.normal_f32((7168, 2048), 1.0, 302))
+    qA, sA, qB, sB, _, _ = full_size.c3()
     return qA, sA, qB, sB, dev_u8(qA), dev_f32(sA), dev_u8(qB), dev_f32(sB)
 
 
@@ -126,9 +126,8 @@ def test_c3_invariance_every_m(bg, c3):
         assert bool(ok.all()), f"shuffle M={m}"
 
 
-def test_c3_parity_sampled_rows(bg, c3):
+def test_c3_parity_every_row(bg, c3):
     qA, sA, qB, sB, A, sAd, B, sBd = c3
-    C = host_codes(bg.gemm_fp8_blockscaled(A, sAd, B, sBd))
-    rows = np.sort(inputs.rng(306).choice(512, size=8, replace=False))
-    C64, S = oracle.gemm_fp8bs(np.ascontiguousarray(qA[rows]), np.ascontiguousarray(sA[rows]), qB, sB)
-    check_parity(C[rows], C64, S, 7168, "C3 M=512 sampled rows")
+    *_, C64, S = full_size.c3()
+    C = host_codes(bg.gemm_fp8_blockscaled(A, sAd, B, sBd))     # M = 512, every row
+    check_parity(full_size.all_rows(C, C64), C64, S, 7168, "C3 M=512 every row")

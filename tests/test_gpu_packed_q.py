@@ -10,6 +10,7 @@ import torch
 
 import oracle
 from invariant_gemm_amd import inputs
+from tests import full_size
 from tests.gpu_util import check_parity, dev_bf16, dev_f32, dev_u8, host_codes, require_gpu, rows_equal
 
 pytestmark = pytest.mark.gpu
@@ -74,7 +75,7 @@ def test_fp8_packed_empty_and_k0(bg):
 @pytest.fixture(scope="module")
 def c3p(bg):
     # fp8 e4m3 K=7168, N=2048 (the same seeded workload as the unpacked tests)
-    qA, sA, qB, sB = fp8_case(512, 2048, 7168, 301)
+    qA, sA, qB, sB, _, _ = full_size.c3()
     A, sAd, B, sBd = dev_u8(qA), dev_f32(sA), dev_u8(qB), dev_f32(sB)
     return qA, sA, qB, sB, A, sAd, bg.pack_b_fp8(B), sBd, B
 
@@ -93,9 +94,9 @@ def test_fp8_packed_c3_invariance_every_m(bg, c3p):
         ok = rows_equal(bg.gemm_fp8_blockscaled_packed(A.index_select(0, p), sAd.index_select(0, p),
                                                        Bp, sBd), ref.index_select(0, p))
         assert bool(ok.all()), f"shuffle M={m}"
-    rows = np.array([0, 255, 511])
-    C64, S = oracle.gemm_fp8bs(np.ascontiguousarray(qA[rows]), np.ascontiguousarray(sA[rows]), qB, sB)
-    check_parity(host_codes(ref[rows]), C64, S, 7168, "C3 packed sampled rows")
+    # every row computed alone (M = 1), which all the comparisons above use
+    *_, C64, S = full_size.c3()
+    check_parity(full_size.all_rows(host_codes(ref), C64), C64, S, 7168, "C3 packed rows at M=1")
 
 
 # ------------------------------------------------------------------ fp4
@@ -150,8 +151,7 @@ def test_fp4_packed_nan_scale_propagates(bg):
 @pytest.fixture(scope="module")
 def c4p(bg):
     # fp4 e2m1 weight-only K=4096, N=14336 (same seeded workload as the unpacked tests)
-    A = inputs.normal_bf16((512, 4096), 1.0, 401)
-    Bq, sB = inputs.quant_fp4_weights(inputs.normal_f32((4096, 14336), 0.02, 402))
+    A, Bq, sB, _, _ = full_size.c4()
     Bd, sBd = dev_u8(Bq), dev_u8(sB)
     return A, Bq, sB, dev_bf16(A), Bd, sBd, bg.pack_b_fp4(Bd, sBd, 14336)
 
@@ -168,9 +168,8 @@ def test_fp4_packed_c4_invariance(bg, c4p):
         p = torch.as_tensor(inputs.permutation(512, 403 + s), device="cuda")
         ok = rows_equal(bg.gemm_fp4_w_packed(Ad.index_select(0, p), Bp), ref.index_select(0, p))
         assert bool(ok.all()), f"shuffle {s}"
-    rows = np.array([1, 300])
-    C64, S = oracle.gemm_fp4w(np.ascontiguousarray(A[rows]), Bq, sB, N)
-    check_parity(host_codes(ref[rows]), C64, S, 4096, "C4 packed sampled rows")
+    *_, C64, S = full_size.c4()
+    check_parity(full_size.all_rows(host_codes(ref), C64), C64, S, 4096, "C4 packed rows at M=1")
 
 
 # ------------------------------------------------------------------ K tails with poisoned pitch padding

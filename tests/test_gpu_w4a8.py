@@ -10,6 +10,7 @@ import torch
 
 import oracle
 from invariant_gemm_amd import inputs
+from tests import full_size
 from tests.gpu_util import check_parity, dev_f32, dev_u8, host_codes, require_gpu, rows_equal
 
 pytestmark = pytest.mark.gpu
@@ -120,8 +121,7 @@ def test_k_tail_ignores_pitch_padding(bg):
 def test_invariance_c4_shape(bg):
     # the fp4 weight shape (K=4096, N=14336) with fp8 activations
     K, N = 4096, 14336
-    qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((512, K), 1.0, 1801))
-    Bq, sE = inputs.quant_mxfp4_weights(inputs.normal_f32((K, N), 0.02, 1802))
+    qA, sA, Bq, sE, C64, S = full_size.w4a8()
     A, sAd = dev_u8(qA), dev_f32(sA)
     Bp = bg.pack_b_mxfp4(dev_u8(Bq), dev_u8(sE), N)
     ref = torch.cat([bg.gemm_w4a8_packed(A[i:i + 1], sAd[i:i + 1], Bp) for i in range(512)])
@@ -133,6 +133,7 @@ def test_invariance_c4_shape(bg):
         ok = rows_equal(bg.gemm_w4a8_packed(A.index_select(0, p), sAd.index_select(0, p), Bp),
                         ref.index_select(0, p))
         assert bool(ok.all()), f"shuffle {s}"
-    rows = np.array([0, 333])
-    C64, S = oracle.gemm_w4a8(np.ascontiguousarray(qA[rows]), np.ascontiguousarray(sA[rows]), Bq, sE, N)
-    check_parity(host_codes(ref[rows]), C64, S, K, "w4a8 C4-shape sampled rows")
+    # every row, computed alone (M = 1) and in the M = 512 batch
+    check_parity(full_size.all_rows(host_codes(ref), C64), C64, S, K, "w4a8 C4 shape rows at M=1")
+    full = host_codes(bg.gemm_w4a8_packed(A, sAd, Bp))
+    check_parity(full_size.all_rows(full, C64), C64, S, K, "w4a8 C4 shape M=512 every row")
