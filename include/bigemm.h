@@ -13,8 +13,11 @@
  * the same K, N, every output row C[i,:] is bit-identical whatever M is, where
  * row i sits in the batch and which other rows share the batch.  The library
  * guarantees this because, for the three invariant entry points:
- *   - the kernel schedule (MFMA instruction, tile sizes, K step and K order)
- *     is a function of (dtype, N, K) only -- M is not an input to it;
+ *   - the arithmetic (MFMA instruction, K step, K order and the order in
+ *     which block results are combined) is a function of the format only --
+ *     M is not an input to it (bi_schedule_query); the launch geometry
+ *     (tile shape, waves, grid) follows M but never changes a result
+ *     (bi_geometry_query);
  *   - one workgroup owns the whole K loop of each output element, with the
  *     fp32 accumulator in registers: no split-K, no stream-K, no atomics
  *     (the split-K conflict is the one the same article's section
@@ -76,16 +79,57 @@ typedef enum bi_dtype {
                                (e2m1 with an E8M0 scale per 32 along K)          */
 } bi_dtype;
 
-/* Introspection only: the schedule a (dtype, N, K) triple runs with. */
+/* How the K blocks of one output element are combined (bi_schedule.order). */
+typedef enum bi_order {
+    /* one fp32 accumulator from +0; one MFMA per k_block-long K step, steps
+       ascending (bf16) */
+    BI_ORDER_SEQUENTIAL = 0,
+    /* per k_block-long K block, one MFMA forms the block product P into a
+       fresh zero accumulator; then acc = fma(P, scale, acc) in fp32, blocks
+       ascending (fp8 block-scaled, fp4 weight-only, W4A8) */
+    BI_ORDER_BLOCK_FMA = 1
+} bi_order;
+
+/* The arithmetic of a format: what decides the bits of an output element.
+ * It is a function of the format alone -- the same for every M, N and K --
+ * so it takes no M (the batch-invariance rule). */
 typedef struct bi_schedule {
     int32_t mfma_m, mfma_n, mfma_k; /* shape of the one MFMA instruction used      */
-    int32_t bm, bn;                 /* output tile of one workgroup                 */
-    int32_t bk;                     /* K consumed per pipeline stage                */
     int32_t k_block;                /* K per accumulation block (scale granularity) */
-    int32_t waves;                  /* wavefronts per workgroup                     */
-    int32_t stages;                 /* global->LDS pipeline depth (stages)          */
+    int32_t order;                  /* bi_order                                    */
     int32_t id;                     /* schedule identifier                          */
 } bi_schedule;
+
+/* Entry points whose launch geometry can be queried. */
+typedef enum bi_entry {
+    BI_ENTRY_BF16 = 0,                /* bi_gemm_bf16                    */
+    BI_ENTRY_BF16_BT = 1,             /* bi_gemm_bf16_bt                 */
+    BI_ENTRY_BF16_PACKED = 2,         /* bi_gemm_bf16_packed             */
+    BI_ENTRY_BF16_GROUPED_PACKED = 3, /* bi_gemm_bf16_grouped_packed     */
+    BI_ENTRY_FP8 = 4,                 /* bi_gemm_fp8_blockscaled         */
+    BI_ENTRY_FP8_PACKED = 5,          /* bi_gemm_fp8_blockscaled_packed  */
+    BI_ENTRY_FP4 = 6,                 /* bi_gemm_fp4_w                   */
+    BI_ENTRY_FP4_PACKED = 7,          /* bi_gemm_fp4_w_packed            */
+    BI_ENTRY_W4A8_PACKED = 8          /* bi_gemm_w4a8_packed             */
+} bi_entry;
+
+/* The launch geometry an entry point uses for one call: how the output
+ * tiles are shared among workgroups.  It follows M (the "dual program" of
+ * section 4.1 of the lshu.cn article: programs for an unsaturated and a
+ * saturated GPU with bit-identical results) but does NOT affect any result:
+ * every geometry of an entry point runs the arithmetic of bi_schedule_query
+ * on every output element.  The entry point launches exactly this geometry
+ * (both read one table). */
+typedef struct bi_geometry {
+    int32_t id;          /* index into the entry point's geometry table       */
+    int32_t bm, bn;      /* output tile of one workgroup (rows x columns)     */
+    int32_t waves;       /* wavefronts per workgroup                          */
+    int32_t a_rows;      /* rows of A each stage loads (<= bm)                */
+    int32_t k_stage;     /* K consumed per pipeline stage                     */
+    int32_t stages;      /* pipeline stages kept in flight                    */
+    int32_t reserved;    /* 0                                                 */
+    int64_t workgroups;  /* workgroups the call launches                      */
+} bi_geometry;
 
 /* Largest supported extent of any single dimension (M, N or K). */
 #define BI_MAX_DIM ((int64_t)1 << 24)
@@ -376,10 +420,21 @@ bi_status bi_decode_attention_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t D
                                    const int32_t* seq_lens, float scale, uint16_t* O,
                                    void* workspace, size_t ws_bytes, int kernel, void* stream);
 
-/* The schedule (dtype, N, K) selects.  There is no M argument by design.
- * Returns BI_ERR_NULL for out == NULL, BI_ERR_UNSUPPORTED for an unknown
- * dtype, BI_ERR_SHAPE for invalid N or K. */
+/* The arithmetic of a format (bi_schedule).  There is no M argument by
+ * design, and the result does not depend on N or K either: N and K are
+ * validated as the format requires (fp8 and W4A8 K % 128 == 0, fp4 K % 32
+ * == 0 and N even).  Returns BI_ERR_NULL for out == NULL,
+ * BI_ERR_UNSUPPORTED for an unknown dtype, BI_ERR_SHAPE for invalid N or K. */
 bi_status bi_schedule_query(bi_dtype dtype, int64_t N, int64_t K, bi_schedule* out);
+
+/* The launch geometry `entry` uses for a call of M x N x K (and `groups`
+ * groups for BI_ENTRY_BF16_GROUPED_PACKED; ignored otherwise).  Informational:
+ * no geometry changes any output bit.  Returns BI_ERR_NULL for out == NULL,
+ * BI_ERR_UNSUPPORTED for an unknown entry or sizes beyond the limits,
+ * BI_ERR_SHAPE for sizes the entry point rejects or M == 0 or N == 0 (no
+ * launch at all), or groups < 1 for a grouped call. */
+bi_status bi_geometry_query(bi_entry entry, int64_t M, int64_t N, int64_t K, int64_t groups,
+                            bi_geometry* out);
 
 /* Static string naming a status code ("BI_OK", ...); never NULL. */
 const char* bi_status_str(bi_status s);

@@ -32,8 +32,18 @@ BI_BF16, BI_FP8_BS, BI_FP4_W, BI_W4A8 = 0, 1, 2, 3
 
 
 class BiSchedule(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("mfma_m", "mfma_n", "mfma_k", "k_block", "order", "id")]
+
+
+class BiGeometry(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("mfma_m", "mfma_n", "mfma_k", "bm", "bn", "bk", "k_block", "waves", "stages", "id")]
+                ("id", "bm", "bn", "waves", "a_rows", "k_stage", "stages", "reserved")] + \
+               [("workgroups", ctypes.c_int64)]
+
+
+ORDER_SEQUENTIAL, ORDER_BLOCK_FMA = 0, 1
+ENTRIES = {"bf16": 0, "bf16_bt": 1, "bf16_packed": 2, "bf16_grouped_packed": 3, "fp8": 4,
+           "fp8_packed": 5, "fp4": 6, "fp4_packed": 7, "w4a8_packed": 8}
 
 
 lib.bi_gemm_bf16.restype = _i32
@@ -74,6 +84,8 @@ lib.bi_splitk_choose.restype = _i32
 lib.bi_splitk_choose.argtypes = [_i64, _i64, _i64]
 lib.bi_schedule_query.restype = _i32
 lib.bi_schedule_query.argtypes = [_i32, _i64, _i64, ctypes.POINTER(BiSchedule)]
+lib.bi_geometry_query.restype = _i32
+lib.bi_geometry_query.argtypes = [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(BiGeometry)]
 lib.bi_status_str.restype = ctypes.c_char_p
 lib.bi_status_str.argtypes = [_i32]
 lib.bi_version.restype = ctypes.c_char_p
@@ -130,6 +142,15 @@ def schedule(dtype: int, N: int, K: int) -> dict:
     s = BiSchedule()
     _check(lib.bi_schedule_query(dtype, N, K, ctypes.byref(s)), "bi_schedule_query")
     return {n: getattr(s, n) for n, _ in BiSchedule._fields_}
+
+
+def geometry(entry: str, M: int, N: int, K: int, groups: int = 0) -> dict:
+    """The launch geometry `entry` uses at M x N x K (informational: no
+    geometry changes a result)."""
+    g = BiGeometry()
+    _check(lib.bi_geometry_query(ENTRIES[entry], M, N, K, groups, ctypes.byref(g)),
+           "bi_geometry_query")
+    return {n: getattr(g, n) for n, _ in BiGeometry._fields_ if n != "reserved"}
 
 
 def _out(M, N, device, out):

@@ -12,31 +12,22 @@ namespace {
 
 // ------------------------------------------------------------------ schedules
 //
-// The schedule of a call is a function of (dtype, N, K) only.  M never
-// reaches this table, so the MFMA instruction, the K step and the order in
-// which an output element's K blocks are accumulated cannot depend on the
-// batch: the "all paths fixed at compile time, no runtime heuristic" rule of
-// section 3.1 of the lshu.cn article, applied per shape class.
-Schedule schedule_for(bi_dtype dt, int64_t N, int64_t K)
+// The arithmetic of a format -- the one MFMA instruction, the K it consumes,
+// the K per scale block and the order in which block results are combined --
+// is fixed per format at compile time, the same for every M, N and K: the
+// "all paths fixed at compile time, no runtime heuristic" rule of section 3.1
+// of the lshu.cn article.  M never reaches it.  What follows M is only the
+// launch geometry (geometry_* in the kernel files), which no result depends
+// on.
+Schedule schedule_for(bi_dtype dt)
 {
-    (void)N;
-    (void)K;
-    Schedule s{};
     switch (dt) {
-    case BI_BF16:
-        s = Schedule{/*id*/ 1, /*rb*/ 2, /*pf*/ 8, /*bm*/ 64, /*bn*/ 32, /*bk*/ 128, /*kblock*/ 32};
-        break;
-    case BI_FP8_BS:
-        s = Schedule{/*id*/ 2, /*rb*/ 2, /*pf*/ 8, /*bm*/ 64, /*bn*/ 16, /*bk*/ 128, /*kblock*/ 128};
-        break;
-    case BI_FP4_W:
-        s = Schedule{/*id*/ 3, /*rb*/ 2, /*pf*/ 8, /*bm*/ 64, /*bn*/ 32, /*bk*/ 128, /*kblock*/ 32};
-        break;
-    case BI_W4A8:
-        s = Schedule{/*id*/ 4, /*rb*/ 1, /*pf*/ 4, /*bm*/ 64, /*bn*/ 16, /*bk*/ 128, /*kblock*/ 128};
-        break;
+    case BI_BF16: return Schedule{1, 16, 16, 32, 32, BI_ORDER_SEQUENTIAL};
+    case BI_FP8_BS: return Schedule{2, 16, 16, 128, 128, BI_ORDER_BLOCK_FMA};
+    case BI_FP4_W: return Schedule{3, 16, 16, 32, 32, BI_ORDER_BLOCK_FMA};
+    case BI_W4A8: return Schedule{4, 16, 16, 128, 128, BI_ORDER_BLOCK_FMA};
     }
-    return s;
+    return Schedule{0, 0, 0, 0, 0, 0};
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -53,12 +44,6 @@ bi_status check_dims(int64_t M, int64_t N, int64_t K)
     if (M > BI_MAX_DIM || N > BI_MAX_DIM || K > BI_MAX_DIM)
         return BI_ERR_UNSUPPORTED;
     return BI_OK;
-}
-
-bi_status check_grid(int64_t M, int64_t N, const Schedule& s)
-{
-    const int64_t tiles = ((N + s.bn - 1) / s.bn) * ((M + s.bm - 1) / s.bm);
-    return tiles <= 0x7FFFFFFF ? BI_OK : BI_ERR_UNSUPPORTED;
 }
 
 bi_status launched(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_LAUNCH; }
@@ -266,18 +251,69 @@ bi_status bi_schedule_query(bi_dtype dtype, int64_t N, int64_t K, bi_schedule* o
     if ((dtype == BI_FP8_BS && K % 128) || (dtype == BI_FP4_W && (K % 32 || N % 2)) ||
         (dtype == BI_W4A8 && (K % 128 || N % 2)))
         return BI_ERR_SHAPE;
-    const Schedule s = schedule_for(dtype, N, K);
+    const Schedule s = schedule_for(dtype);
     memset(out, 0, sizeof *out);
-    out->mfma_m = 16;
-    out->mfma_n = 16;
-    out->mfma_k = (dtype == BI_FP8_BS || dtype == BI_W4A8) ? 128 : 32;
-    out->bm = s.bm;
-    out->bn = s.bn;
-    out->bk = s.bk;
-    out->k_block = s.kblock;
-    out->waves = 4;
-    out->stages = s.pf;
+    out->mfma_m = s.mfma_m;
+    out->mfma_n = s.mfma_n;
+    out->mfma_k = s.mfma_k;
+    out->k_block = s.k_block;
+    out->order = s.order;
     out->id = s.id;
+    return BI_OK;
+}
+
+bi_status bi_geometry_query(bi_entry entry, int64_t M, int64_t N, int64_t K, int64_t groups,
+                            bi_geometry* out)
+{
+    if (!out)
+        return BI_ERR_NULL;
+    bi_status st = check_dims(M, N, K);
+    if (st != BI_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return BI_ERR_SHAPE;
+    Geometry g;
+    switch (entry) {
+    case BI_ENTRY_BF16: g = geometry_bf16(M, N, K); break;
+    case BI_ENTRY_BF16_BT: g = geometry_bf16_bt(M, N, K); break;
+    case BI_ENTRY_BF16_PACKED: g = geometry_bf16_packed(M, N, K); break;
+    case BI_ENTRY_BF16_GROUPED_PACKED:
+        if (groups < 1)
+            return BI_ERR_SHAPE;
+        if (groups > 65536)
+            return BI_ERR_UNSUPPORTED;
+        g = geometry_bf16_grouped(M, N, K, groups);
+        break;
+    case BI_ENTRY_FP8:
+    case BI_ENTRY_FP8_PACKED:
+        if (K % 128)
+            return BI_ERR_SHAPE;
+        g = entry == BI_ENTRY_FP8 ? geometry_fp8(M, N, K) : geometry_fp8_packed(M, N, K);
+        break;
+    case BI_ENTRY_FP4:
+    case BI_ENTRY_FP4_PACKED:
+        if (K % 32 || N % 2)
+            return BI_ERR_SHAPE;
+        g = entry == BI_ENTRY_FP4 ? geometry_fp4(M, N, K) : geometry_fp4_packed(M, N, K);
+        break;
+    case BI_ENTRY_W4A8_PACKED:
+        if (K % 128 || N % 2)
+            return BI_ERR_SHAPE;
+        g = geometry_w4a8_packed(M, N, K);
+        break;
+    default: return BI_ERR_UNSUPPORTED;
+    }
+    if (g.workgroups > 0x7FFFFFFF)
+        return BI_ERR_UNSUPPORTED;
+    memset(out, 0, sizeof *out);
+    out->id = g.id;
+    out->bm = g.bm;
+    out->bn = g.bn;
+    out->waves = g.waves;
+    out->a_rows = g.a_rows;
+    out->k_stage = g.k_stage;
+    out->stages = g.stages;
+    out->workgroups = g.workgroups;
     return BI_OK;
 }
 
@@ -288,11 +324,8 @@ bi_status bi_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64
     bi_status st = validate_bf16(M, N, K, A, lda, B, ldb, N, C, ldc, &noop);
     if (st != BI_OK || noop)
         return st;
-    const Schedule s = schedule_for(BI_BF16, N, K);
-    if ((st = check_grid(M, N, s)) != BI_OK)
-        return st;
     GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, B, ldb, nullptr, 0, C, ldc};
-    return launched(launch_bf16(a, s, (hipStream_t)stream));
+    return launched(launch_bf16(a, (hipStream_t)stream));
 }
 
 bi_status bi_gemm_bf16_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
@@ -302,11 +335,8 @@ bi_status bi_gemm_bf16_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, in
     bi_status st = validate_bf16(M, N, K, A, lda, Bt, ldbt, K, C, ldc, &noop);
     if (st != BI_OK || noop)
         return st;
-    const Schedule s = schedule_for(BI_BF16, N, K);
-    if ((st = check_grid(M, N, s)) != BI_OK)
-        return st;
     GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, Bt, ldbt, nullptr, 0, C, ldc};
-    return launched(launch_bf16_bt(a, s, (hipStream_t)stream));
+    return launched(launch_bf16_bt(a, (hipStream_t)stream));
 }
 
 size_t bi_packed_b_bytes(bi_dtype dtype, int64_t N, int64_t K)
@@ -411,11 +441,8 @@ bi_status bi_gemm_fp8_blockscaled(int64_t M, int64_t N, int64_t K, const uint8_t
     bi_status st = validate_fp8(M, N, K, A, lda, sA, ldsa, B, ldb, sB, ldsb, C, ldc, &noop);
     if (st != BI_OK || noop)
         return st;
-    const Schedule s = schedule_for(BI_FP8_BS, N, K);
-    if ((st = check_grid(M, N, s)) != BI_OK)
-        return st;
     GemmArgs a{(int)M, (int)N, (int)K, A, lda, sA, ldsa, B, ldb, sB, ldsb, C, ldc};
-    return launched(launch_fp8bs(a, s, (hipStream_t)stream));
+    return launched(launch_fp8bs(a, (hipStream_t)stream));
 }
 
 bi_status bi_gemm_fp4_w(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
@@ -426,11 +453,8 @@ bi_status bi_gemm_fp4_w(int64_t M, int64_t N, int64_t K, const uint16_t* A, int6
     bi_status st = validate_fp4(M, N, K, A, lda, Bq, ldbq, sB, ldsb, C, ldc, &noop);
     if (st != BI_OK || noop)
         return st;
-    const Schedule s = schedule_for(BI_FP4_W, N, K);
-    if ((st = check_grid(M, N, s)) != BI_OK)
-        return st;
     GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, Bq, ldbq, sB, ldsb, C, ldc};
-    return launched(launch_fp4w(a, s, (hipStream_t)stream));
+    return launched(launch_fp4w(a, (hipStream_t)stream));
 }
 
 bi_status bi_pack_b_fp8(int64_t N, int64_t K, const uint8_t* B, int64_t ldb, void* Bp,
@@ -633,11 +657,10 @@ bi_status bi_gemm_bf16_splitk(int64_t M, int64_t N, int64_t K, const uint16_t* A
         S = (int)nst;
     if (S > 65535 || M * N > ((int64_t)1 << 31))
         return BI_ERR_UNSUPPORTED;
-    const Schedule s = schedule_for(BI_BF16, N, K);
-    if ((st = check_grid(M, N, s)) != BI_OK)
-        return st;
+    if (ceil_div(M, 64) * ceil_div(N, 32) > 0x7FFFFFFF)
+        return BI_ERR_UNSUPPORTED;
     GemmArgs a{(int)M, (int)N, (int)K, A, lda, nullptr, 0, B, ldb, nullptr, 0, C, ldc};
-    return launched(launch_bf16_splitk(a, s, workspace, S, (hipStream_t)stream));
+    return launched(launch_bf16_splitk(a, workspace, S, (hipStream_t)stream));
 }
 
 }  // extern "C"

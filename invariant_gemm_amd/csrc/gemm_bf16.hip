@@ -305,27 +305,39 @@ hipError_t launch_rb_split(const GemmArgs& a, float* ws, int splits, hipStream_t
 // per element): 64 x 64 tiles, two stages in flight, once they still give
 // every compute unit a workgroup -- A rows then serve twice the columns
 // (K = N = 8192: M = 128 73.2 -> 52.6 us, M = 256 123.4 -> 81.0 us) --
-// else 64 x 32 tiles streaming N/32 column strips.
-hipError_t launch_bf16(const GemmArgs& a, const Schedule& s, hipStream_t stream)
+// else 64 x 32 tiles streaming N/32 column strips (six stages in flight).
+Geometry geometry_bf16(int64_t M, int64_t N, int64_t K)
 {
-    switch (s.rb) {
-    case 1: return launch_rb<1, 8>(a, stream);
-    case 2:
-        if ((int64_t)((a.M + 63) / 64) * ((a.N + 63) / 64) >= 256)
-            return launch_rb<2, 2, 2>(a, stream);
-        return launch_rb<2, 6>(a, stream);
+    (void)K;
+    Geometry g;
+    const bool wide = ceil_div(M, 64) * ceil_div(N, 64) >= 256;
+    g.id = wide ? 1 : 0;
+    g.bm = 64;
+    g.bn = wide ? 64 : 32;
+    g.waves = 4;
+    g.a_rows = 64;
+    g.k_stage = BKS;
+    g.stages = wide ? 2 : 6;
+    g.workgroups = ceil_div(M, g.bm) * ceil_div(N, g.bn);
+    return g;
+}
+
+hipError_t launch_bf16(const GemmArgs& a, hipStream_t stream)
+{
+    const Geometry g = geometry_bf16(a.M, a.N, a.K);
+    if (g.workgroups > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    switch (g.id) {
+    case 0: return launch_rb<2, 6>(a, stream);
+    case 1: return launch_rb<2, 2, 2>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_bf16_splitk(const GemmArgs& a, const Schedule& s, float* ws, int splits,
-                              hipStream_t stream)
+// The comparator: 64 x 32 tiles, six stages, split over K.
+hipError_t launch_bf16_splitk(const GemmArgs& a, float* ws, int splits, hipStream_t stream)
 {
-    switch (s.rb) {
-    case 1: return launch_rb_split<1, 8>(a, ws, splits, stream);
-    case 2: return launch_rb_split<2, 6>(a, ws, splits, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_rb_split<2, 6>(a, ws, splits, stream);
 }
 
 }  // namespace bigemm

@@ -175,25 +175,68 @@ hipError_t launch_rb(const GemmArgs& a, hipStream_t stream)
 // Launch geometry (tile sharing only; every choice runs the same arithmetic
 // per element): taller and wider tiles as M grows, each only while its tiles
 // still give every compute unit a workgroup -- 64 x 64 (four waves) beyond
-// 64 rows, 32 x 64 beyond 32, 32 x 32 beyond 16, else 16 x 32 streaming.
-// K = N = 8192: M = 64 72.5 -> 41.0 us, M = 128 136.2 -> 53.9 us, M = 256
-// 266.5 -> 89.6 us against one 16-row block per workgroup.
-hipError_t launch_bf16_bt(const GemmArgs& a, const Schedule& s, hipStream_t stream)
+// 64 rows, 32 x 64 beyond 32, 64 x 32 beyond 32, 32 x 32 beyond 16, else
+// 16 x 32 streaming.  K = N = 8192: M = 64 72.5 -> 41.0 us, M = 128 136.2 ->
+// 53.9 us, M = 256 266.5 -> 89.6 us against one 16-row block per workgroup.
+namespace {
+struct Cfg {
+    int rb, pf, waves;
+};
+constexpr Cfg kCfg[] = {
+    /* 0 */ {1, 4, 2},   // 16 x 32
+    /* 1 */ {2, 2, 2},   // 32 x 32
+    /* 2 */ {4, 2, 2},   // 64 x 32
+    /* 3 */ {2, 2, 4},   // 32 x 64
+    /* 4 */ {4, 2, 4},   // 64 x 64
+};
+
+template <int I>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream)
 {
-    (void)s;
-    const int64_t M = a.M, N = a.N;
-    auto tiles = [&](int rb, int waves) {
-        return ((M + 16 * rb - 1) / (16 * rb)) * ((N + 16 * waves - 1) / (16 * waves));
-    };
-    if (M > 64 && tiles(4, 4) >= 256)
-        return launch_rb<4, 2, 4>(a, stream);
-    if (M > 32 && tiles(2, 4) >= 256)
-        return launch_rb<2, 2, 4>(a, stream);
-    if (M > 32 && tiles(4, 2) >= 256)
-        return launch_rb<4, 2, 2>(a, stream);
-    if (M > 16 && tiles(2, 2) >= 256)
-        return launch_rb<2, 2, 2>(a, stream);
-    return launch_rb<1, 4, 2>(a, stream);
+    constexpr Cfg c = kCfg[I];
+    return launch_rb<c.rb, c.pf, c.waves>(a, stream);
+}
+}  // namespace
+
+Geometry geometry_bf16_bt(int64_t M, int64_t N, int64_t K)
+{
+    (void)K;
+    auto tiles = [&](const Cfg& c) { return ceil_div(M, 16 * c.rb) * ceil_div(N, 16 * c.waves); };
+    int id = 0;
+    if (M > 64 && tiles(kCfg[4]) >= 256)
+        id = 4;
+    else if (M > 32 && tiles(kCfg[3]) >= 256)
+        id = 3;
+    else if (M > 32 && tiles(kCfg[2]) >= 256)
+        id = 2;
+    else if (M > 16 && tiles(kCfg[1]) >= 256)
+        id = 1;
+    const Cfg& c = kCfg[id];
+    Geometry g;
+    g.id = id;
+    g.bm = 16 * c.rb;
+    g.bn = 16 * c.waves;
+    g.waves = c.waves;
+    g.a_rows = g.bm;
+    g.k_stage = BKS;
+    g.stages = c.pf;
+    g.workgroups = tiles(c);
+    return g;
+}
+
+hipError_t launch_bf16_bt(const GemmArgs& a, hipStream_t stream)
+{
+    const Geometry g = geometry_bf16_bt(a.M, a.N, a.K);
+    if (g.workgroups > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    switch (g.id) {
+    case 0: return launch_cfg<0>(a, stream);
+    case 1: return launch_cfg<1>(a, stream);
+    case 2: return launch_cfg<2>(a, stream);
+    case 3: return launch_cfg<3>(a, stream);
+    case 4: return launch_cfg<4>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace bigemm

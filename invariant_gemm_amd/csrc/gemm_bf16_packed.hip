@@ -285,149 +285,230 @@ __global__ void pack_b_bf16_kernel(int N, int K, const uint16_t* __restrict__ B,
     *reinterpret_cast<u32x4*>(Bp + q * 16) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <int WAVES, int CB, int RB, int KS_ST, int PF, bool NT = true, int AR = 16 * RB,
-          bool HALF = false>
-hipError_t launch_geometry(const GemmArgs& a, const GroupArgs* grp, hipStream_t stream)
+// One launch geometry: WAVES waves of CB column blocks each, RB row blocks,
+// KS_ST K steps per stage, PF stages in flight, non-temporal weight loads,
+// AR staged A rows, half blocks.
+struct Cfg {
+    int waves, cb, rb, ks_st, pf;
+    bool nt;
+    int ar;
+    bool half;
+};
+
+// The geometry table.  Every entry runs the same per-element arithmetic.
+constexpr Cfg kCfg[] = {
+    /*  0 */ {2, 1, 1, 8, 4, true, 16, false},   // streaming 16 x 32
+    /*  1 */ {2, 1, 1, 8, 4, true, 4, false},    //   the same, 4 rows of A staged
+    /*  2 */ {2, 1, 1, 8, 4, true, 8, false},    //   the same, 8 rows of A staged
+    /*  3 */ {2, 1, 2, 8, 2, true, 32, false},   // streaming 32 x 32
+    /*  4 */ {2, 1, 4, 4, 4, true, 64, false},   // streaming 64 x 32
+    /*  5 */ {4, 1, 2, 8, 2, true, 32, false},   // 32 x 64, four waves
+    /*  6 */ {4, 1, 4, 4, 4, true, 64, false},   // 64 x 64
+    /*  7 */ {4, 2, 4, 4, 4, false, 64, false},  // 64 x 128, B strips shared by 4 row tiles
+    /*  8 */ {4, 1, 4, 4, 4, false, 64, false},  // 64 x 64, B kept in L2 (grouped calls)
+    /*  9 */ {1, 1, 1, 16, 2, true, 16, false},  // one wave, 16 x 16
+    /* 10 */ {1, 1, 1, 16, 2, true, 4, false},   //   4 rows of A staged
+    /* 11 */ {1, 1, 1, 16, 2, true, 8, false},   //   8 rows of A staged
+    /* 12 */ {1, 1, 1, 16, 2, true, 16, true},   // one wave, half blocks (16 x 8)
+    /* 13 */ {1, 1, 1, 16, 2, true, 4, true},
+    /* 14 */ {1, 1, 1, 16, 2, true, 8, true},
+};
+constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
+
+int64_t n_tiles_of(const Cfg& c, int64_t N)
 {
-    const int n_tiles = ((a.N + 15) / 16 + WAVES * CB - 1) / (WAVES * CB) * (HALF ? 2 : 1);
-    const dim3 block(64 * WAVES);
+    return ceil_div(ceil_div(N, 16), c.waves * c.cb) * (c.half ? 2 : 1);
+}
+
+// Row slots of a grouped call: the rows (at most M once the kernel clamps
+// the offsets) fall in at most k = min(groups, M) non-empty groups of r_g
+// rows, and sum ceil(r_g / BM) <= floor((M + k (BM - 1)) / BM) -- one slot
+// at M = 1.
+int64_t m_tiles_of(const Cfg& c, int64_t M, int64_t groups)
+{
+    const int64_t bm = 16 * c.rb;
+    if (groups <= 0)
+        return ceil_div(M, bm);
+    const int64_t k = std::min<int64_t>(groups, M);
+    return (M + k * (bm - 1)) / bm;
+}
+
+Geometry describe(int id, int64_t M, int64_t N, int64_t groups)
+{
+    const Cfg& c = kCfg[id];
+    Geometry g;
+    g.id = id;
+    g.bm = 16 * c.rb;
+    g.bn = c.half ? 8 : 16 * c.waves * c.cb;
+    g.waves = c.waves;
+    g.a_rows = c.ar;
+    g.k_stage = c.ks_st * KSTEP;
+    g.stages = c.pf;
+    g.workgroups = n_tiles_of(c, N) * m_tiles_of(c, M, groups);
+    return g;
+}
+
+template <int I>
+hipError_t launch_cfg(const GemmArgs& a, const GroupArgs* grp, const Geometry& g, hipStream_t stream)
+{
+    constexpr Cfg c = kCfg[I];
+    const dim3 block(64 * c.waves);
+    if (g.workgroups <= 0 || g.workgroups > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)g.workgroups);
+    const int m_tiles = (int)m_tiles_of(c, a.M, grp ? grp->n_groups : 0);
     if (grp) {
-        // row slots: the rows (at most M once the kernel clamps the offsets)
-        // fall in at most k = min(groups, M) non-empty groups of r_g rows, and
-        // sum ceil(r_g / BM) <= floor((M + k (BM - 1)) / BM) -- one slot at M = 1
-        constexpr int BM = 16 * RB;
-        const int64_t k = std::min<int64_t>(grp->n_groups, a.M);
-        const int m_tiles = (int)(((int64_t)a.M + k * (BM - 1)) / BM);
-        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, true, NT, AR, HALF><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
-            a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles,
-            grp->offsets, grp->n_groups, grp->b_stride, grp->slot_first);
+        gemm_bf16_packed_kernel<c.waves, c.cb, c.rb, c.ks_st, c.pf, true, c.nt, c.ar, c.half>
+            <<<grid, block, 0, stream>>>(a.M, a.N, a.K, (const uint16_t*)a.A, a.lda,
+                                         (const uint8_t*)a.B, a.C, a.ldc, m_tiles, grp->offsets,
+                                         grp->n_groups, grp->b_stride, grp->slot_first);
     } else {
-        const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-        gemm_bf16_packed_kernel<WAVES, CB, RB, KS_ST, PF, false, NT, AR, HALF><<<dim3(n_tiles * m_tiles), block, 0, stream>>>(
-            a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles,
-            nullptr, 0, 0, 0);
+        gemm_bf16_packed_kernel<c.waves, c.cb, c.rb, c.ks_st, c.pf, false, c.nt, c.ar, c.half>
+            <<<grid, block, 0, stream>>>(a.M, a.N, a.K, (const uint16_t*)a.A, a.lda,
+                                         (const uint8_t*)a.B, a.C, a.ldc, m_tiles, nullptr, 0, 0, 0);
     }
     return hipGetLastError();
 }
 
-}  // namespace
-
-// Launch geometry for a call.  Every geometry runs the same per-element
-// arithmetic (same MFMA, same K steps in the same order, same epilogue), so
-// this choice -- unlike the arithmetic -- may follow M: it only decides how
-// the output tiles are shared among workgroups.  The largest tile that still
-// yields a workgroup per compute unit wins; below that, the streaming
-// geometry (one 16-row block, two 16-column waves) covers N with N/32
-// workgroups -- or, for up to 16 rows while N/32 workgroups would leave
-// compute units idle, one wave per 16 columns (N/16 workgroups).
-int packed_geometry(int M, int N)
+hipError_t launch_id(const GemmArgs& a, const GroupArgs* grp, const Geometry& g, hipStream_t stream)
 {
-    const int nb = (N + 15) / 16;
-    const int large = ((M + 63) / 64) * ((nb + 7) / 8);     // 4 waves x 2 blocks, BM 64
-    const int medium = ((M + 63) / 64) * ((nb + 3) / 4);    // 4 waves x 1 block,  BM 64
+    switch (g.id) {
+    case 0: return launch_cfg<0>(a, grp, g, stream);
+    case 1: return launch_cfg<1>(a, grp, g, stream);
+    case 2: return launch_cfg<2>(a, grp, g, stream);
+    case 3: return launch_cfg<3>(a, grp, g, stream);
+    case 4: return launch_cfg<4>(a, grp, g, stream);
+    case 5: return launch_cfg<5>(a, grp, g, stream);
+    case 6: return launch_cfg<6>(a, grp, g, stream);
+    case 7: return launch_cfg<7>(a, grp, g, stream);
+    case 8: return launch_cfg<8>(a, grp, g, stream);
+    case 9: return launch_cfg<9>(a, grp, g, stream);
+    case 10: return launch_cfg<10>(a, grp, g, stream);
+    case 11: return launch_cfg<11>(a, grp, g, stream);
+    case 12: return launch_cfg<12>(a, grp, g, stream);
+    case 13: return launch_cfg<13>(a, grp, g, stream);
+    case 14: return launch_cfg<14>(a, grp, g, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+static_assert(kNumCfg == 15, "every table entry needs its case in launch_id");
+
+// The 16-row streaming geometries stage only as many rows of A as the call
+// can hold: 4 or 8 when M is at most that.
+int staged_variant(int base, int64_t M)
+{
+    if (M <= 4)
+        return base + 1;
+    if (M <= 8)
+        return base + 2;
+    return base;
+}
+
+// The family chosen from M and N (before the staged-row variant).  The
+// largest tile that still yields a workgroup per compute unit wins; below
+// that, the streaming geometry (one 16-row block, two 16-column waves)
+// covers N with N/32 workgroups -- or, for up to 16 rows while N/32
+// workgroups would leave compute units idle, one wave per 16 columns (N/16
+// workgroups).
+int family(int64_t M, int64_t N)
+{
+    const int64_t nb = ceil_div(N, 16);
+    const int64_t large = ceil_div(M, 64) * ceil_div(nb, 8);    // 4 waves x 2 blocks, BM 64
+    const int64_t medium = ceil_div(M, 64) * ceil_div(nb, 4);   // 4 waves x 1 block,  BM 64
     // the large tiles also win where the medium ones would put two workgroups
     // on some compute units: a large-tile workgroup takes about as long
     // whether 64 or 256 of them run (K = N = 8192, M = 160: 71.6 -> 55.1 us)
     if (M >= 64 && (large >= 256 || medium > 256))
-        return 4;
+        return 7;
     if (M >= 64 && medium >= 256)
-        return 3;
+        return 6;
     if (M > 32)
-        return 2;                                           // streaming, BM 64
+        return 4;                                               // streaming, BM 64
     if (M > 16)
-        return 1;                                           // streaming, BM 32
-    if ((nb + 1) / 2 < 256)
-        return 5;                                           // streaming, BM 16, one wave
-    return 0;                                               // streaming, BM 16
+        return 3;                                               // streaming, BM 32
+    if (ceil_div(nb, 2) < 256)
+        return 9;                                               // streaming, BM 16, one wave
+    return 0;                                                   // streaming, BM 16
 }
 
-namespace {
-
-hipError_t launch_packed(const GemmArgs& a, const GroupArgs* grp, int geometry, hipStream_t stream)
+// Grouped launch geometry from 25 rows per group on: the 64-row tiles are
+// chosen from the workgroups the call is expected to occupy: T rows over k
+// groups fill about T/64 + k/2 row slots (a group wastes half a tile on
+// average).  64 x 64 tiles while they need at most one workgroup per compute
+// unit; else 64 x 128 while those fill at least three quarters of the compute
+// units, or fill their last round that well; else 64 x 64 with the weights
+// kept in L2 for the row tiles that share them.  E = 8, K = 7168, N = 2048:
+// 256 tokens 68.7 -> 42.9 us, 512 tokens 88.4 -> 59.8 us, 1024 tokens 128.9
+// -> 88.6 us.
+int grouped_wide(int64_t M, int64_t N, int64_t k)
 {
-    switch (geometry) {
-    case 4: return launch_geometry<4, 2, 4, 4, 4, false>(a, grp, stream);   // B strips shared by 4 row tiles
-    case 3: return launch_geometry<4, 1, 4, 4, 4>(a, grp, stream);
-    case 2: return launch_geometry<2, 1, 4, 4, 4>(a, grp, stream);
-    case 1: return launch_geometry<2, 1, 2, 8, 2>(a, grp, stream);
-    case 7: return launch_geometry<4, 1, 2, 8, 2>(a, grp, stream);   // 32 x 64, four waves
-    case 8: return launch_geometry<4, 1, 4, 4, 4, false>(a, grp, stream);   // 64 x 64, B via L2
-    case 5:
-        // at most 4 or 8 rows in the call: stage only those rows of A
-        if (a.M <= 4) return launch_geometry<1, 1, 1, 16, 2, true, 4>(a, grp, stream);
-        if (a.M <= 8) return launch_geometry<1, 1, 1, 16, 2, true, 8>(a, grp, stream);
-        return launch_geometry<1, 1, 1, 16, 2>(a, grp, stream);
-    case 6:                                          // geometry 5 on half blocks
-        if (a.M <= 4) return launch_geometry<1, 1, 1, 16, 2, true, 4, true>(a, grp, stream);
-        if (a.M <= 8) return launch_geometry<1, 1, 1, 16, 2, true, 8, true>(a, grp, stream);
-        return launch_geometry<1, 1, 1, 16, 2, true, 16, true>(a, grp, stream);
-    default:
-        if (a.M <= 4) return launch_geometry<2, 1, 1, 8, 4, true, 4>(a, grp, stream);
-        if (a.M <= 8) return launch_geometry<2, 1, 1, 8, 4, true, 8>(a, grp, stream);
-        return launch_geometry<2, 1, 1, 8, 4>(a, grp, stream);
-    }
+    const int64_t slots = (M + 32 * k + 63) / 64;
+    const int64_t nb = ceil_div(N, 16);
+    const int64_t medium = slots * ceil_div(nb, 4), large = slots * ceil_div(nb, 8);
+    if (medium <= 256)
+        return 6;
+    if (large <= 256)
+        return large >= 192 ? 7 : 6;
+    return large % 256 == 0 || large % 256 >= 192 ? 7 : 8;
 }
 
 }  // namespace
 
-// The one-wave geometry runs on half blocks (8 columns per workgroup) while
-// the column blocks are fewer than the compute units (N = 2048: M = 8
-// 10.0 -> 9.4 us, M = 16 11.2 -> 10.5 us, the same at M <= 4).  Grouped
-// calls keep whole blocks: there the doubled slot count measured slower.
-hipError_t launch_bf16_packed(const GemmArgs& a, hipStream_t stream)
+// Plain calls.  The one-wave geometry runs on half blocks (8 columns per
+// workgroup) while the column blocks are fewer than the compute units
+// (N = 2048: M = 8 10.0 -> 9.4 us, M = 16 11.2 -> 10.5 us, the same at
+// M <= 4).  33..64 rows: 32 x 64 tiles on four waves keep all four SIMDs of
+// a compute unit busy where the two-wave 64 x 32 streaming tiles leave two
+// idle (K = N = 8192, M = 64: 34.0 -> 31.7 us) -- while they still give
+// every compute unit a workgroup.
+Geometry geometry_bf16_packed(int64_t M, int64_t N, int64_t K)
 {
-    int geometry = packed_geometry(a.M, a.N);
-    if (geometry == 5 && (a.N + 15) / 16 < 256)
-        geometry = 6;
-    // 33..64 rows: 32 x 64 tiles on four waves keep all four SIMDs of a
-    // compute unit busy where the two-wave 64 x 32 streaming tiles leave two
-    // idle (K = N = 8192, M = 64: 34.0 -> 31.7 us) -- while they still give
-    // every compute unit a workgroup
-    if (geometry == 2 && a.M <= 64 && ((a.M + 31) / 32) * (((a.N + 15) / 16 + 3) / 4) >= 256)
-        geometry = 7;
-    return launch_packed(a, nullptr, geometry, stream);
+    (void)K;
+    int id = family(M, N);
+    if (id == 9 && ceil_div(N, 16) < 256)
+        id = 12;
+    if (id == 4 && M <= 64 && ceil_div(M, 32) * ceil_div(ceil_div(N, 16), 4) >= 256)
+        id = 5;
+    if (id == 0 || id == 9 || id == 12)
+        id = staged_variant(id, M);
+    return describe(id, M, N, 0);
 }
 
-// Grouped launch: the geometry follows the mean rows per group (any choice
+// Grouped calls: the geometry follows the mean rows per group (any choice
 // gives the same bits).  The one-wave streaming geometry only pays while the
 // groups that can hold rows -- at most min(groups, M) -- leave compute units
-// idle with two-wave workgroups.
-//
-// From 25 rows per group on, the 64-row tiles are chosen from the workgroups
-// the call is expected to occupy: T rows over k groups fill about T/64 + k/2
-// row slots (a group wastes half a tile on average).  64 x 64 tiles while
-// they need at most one workgroup per compute unit; else 64 x 128 while those
-// fill at least three quarters of the compute units, or fill their last
-// round that well; else 64 x 64 with the weights kept in L2 for the row
-// tiles that share them.  E = 8, K = 7168, N = 2048: 256 tokens 68.7 -> 42.9
-// us, 512 tokens 88.4 -> 59.8 us, 1024 tokens 128.9 -> 88.6 us.
-int grouped_wide_geometry(int64_t M, int N, int64_t k)
+// idle with two-wave workgroups; grouped calls keep whole blocks (there the
+// doubled slot count of half blocks measured slower).
+Geometry geometry_bf16_grouped(int64_t M, int64_t N, int64_t K, int64_t groups)
 {
-    const int64_t slots = (M + 32 * k + 63) / 64;
-    const int64_t nb = (N + 15) / 16;
-    const int64_t medium = slots * ((nb + 3) / 4), large = slots * ((nb + 7) / 8);
-    if (medium <= 256)
-        return 3;
-    if (large <= 256)
-        return large >= 192 ? 4 : 3;
-    return large % 256 == 0 || large % 256 >= 192 ? 4 : 8;
+    (void)K;
+    const int64_t mean = ceil_div(M, groups);
+    int id = family(mean > 0 ? mean : 1, N);
+    const int64_t active = std::min<int64_t>(groups, M);
+    if (id == 9 && active * ceil_div(N, 32) >= 256)
+        id = 0;
+    if (mean > 24)
+        id = grouped_wide(M, N, active);
+    // the staged-row variants follow the call's own M (all rows of a
+    // grouped call can fall into one group)
+    if (id == 0 || id == 9)
+        id = staged_variant(id, M);
+    return describe(id, M, N, groups);
 }
 
+hipError_t launch_bf16_packed(const GemmArgs& a, hipStream_t stream)
+{
+    return launch_id(a, nullptr, geometry_bf16_packed(a.M, a.N, a.K), stream);
+}
+
+// Slot order: row slot first from four rows per group on (E = 8, N = 2048:
+// 64 tokens 45.7 -> 38.9 us, 512 tokens 91.1 -> 89.5 us); below that the
+// XCD-contiguous column order measured faster (8 tokens 27.5 vs 30.2 us).
 hipError_t launch_bf16_grouped_packed(const GemmArgs& a, const GroupArgs& g, hipStream_t stream)
 {
-    const int mean = (a.M + g.n_groups - 1) / g.n_groups;
-    int geometry = packed_geometry(mean > 0 ? mean : 1, a.N);
-    const int64_t active = std::min<int64_t>(g.n_groups, a.M);
-    if (geometry == 5 && active * ((a.N + 31) / 32) >= 256)
-        geometry = 0;
-    if (mean > 24)
-        geometry = grouped_wide_geometry(a.M, a.N, active);
-    // slot order: row slot first from four rows per group on (E = 8, N = 2048:
-    // 64 tokens 45.7 -> 38.9 us, 512 tokens 91.1 -> 89.5 us); below that the
-    // XCD-contiguous column order measured faster (8 tokens 27.5 vs 30.2 us)
     GroupArgs gs = g;
-    gs.slot_first = mean >= 4 ? 1 : 0;
-    return launch_packed(a, &gs, geometry, stream);
+    gs.slot_first = ceil_div(a.M, g.n_groups) >= 4 ? 1 : 0;
+    return launch_id(a, &gs, geometry_bf16_grouped(a.M, a.N, a.K, g.n_groups), stream);
 }
 
 hipError_t launch_pack_b_bf16(int N, int K, const uint16_t* B, int64_t ldb, uint8_t* Bp,

@@ -202,12 +202,29 @@ __global__ __launch_bounds__(256) void gemm_fp4_kernel(
 
 }  // namespace
 
-hipError_t launch_fp4w(const GemmArgs& a, const Schedule& s, hipStream_t stream)
+// One geometry: BM x BN tiles, 4 stages in flight.
+Geometry geometry_fp4(int64_t M, int64_t N, int64_t K)
 {
-    (void)s;
-    const int n_tiles = (a.N + BN - 1) / BN;
-    const int m_tiles = (a.M + BM - 1) / BM;
-    gemm_fp4_kernel<4><<<dim3(n_tiles * m_tiles), dim3(256), 0, stream>>>(
+    (void)K;
+    Geometry g;
+    g.id = 0;
+    g.bm = BM;
+    g.bn = BN;
+    g.waves = 4;
+    g.a_rows = BM;
+    g.k_stage = BKS;
+    g.stages = 4;
+    g.workgroups = ceil_div(M, BM) * ceil_div(N, BN);
+    return g;
+}
+
+hipError_t launch_fp4w(const GemmArgs& a, hipStream_t stream)
+{
+    const Geometry g = geometry_fp4(a.M, a.N, a.K);
+    if (g.workgroups > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    const int m_tiles = (int)ceil_div(a.M, BM);
+    gemm_fp4_kernel<4><<<dim3((unsigned)g.workgroups), dim3(256), 0, stream>>>(
         a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.ldb,
         (const uint8_t*)a.sB, a.ldsb, a.C, a.ldc, m_tiles);
     return hipGetLastError();

@@ -304,14 +304,48 @@ __global__ void pack_fp4_kernel(int N, int K, const uint8_t* __restrict__ Bq, in
     }
 }
 
-template <int WAVES, int CB, int RB, int QS, int PF, bool NT = true, int AR = 16 * RB>
-hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
+// One launch geometry: WAVES waves of CB column blocks, RB row blocks, QS
+// 128-K groups per stage, PF stages in flight, non-temporal weight loads,
+// AR staged A rows.
+struct Cfg {
+    int waves, cb, rb, qs, pf;
+    bool nt;
+    int ar;
+};
+
+// The geometry table.  Every entry runs the same per-element arithmetic.
+constexpr Cfg kCfg[] = {
+    /* 0 */ {2, 1, 1, 2, 4, true, 16},    // 16 x 32 streaming, two waves
+    /* 1 */ {4, 1, 4, 1, 4, true, 64},    // 64 x 64
+    /* 2 */ {4, 2, 4, 1, 2, false, 64},   // 64 x 128, weights shared by row tiles
+};
+constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
+
+Geometry describe(int id, int64_t M, int64_t N)
 {
-    const int n_tiles = ((a.N + 15) / 16 + WAVES * CB - 1) / (WAVES * CB);
-    const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-    gemm_fp4_packed_kernel<WAVES, CB, RB, QS, PF, NT, AR><<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0,
-                                                    stream>>>(
-        a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
+    const Cfg& c = kCfg[id];
+    Geometry g;
+    g.id = id;
+    g.bm = 16 * c.rb;
+    g.bn = 16 * c.waves * c.cb;
+    g.waves = c.waves;
+    g.a_rows = c.ar;
+    g.k_stage = c.qs * 128;
+    g.stages = c.pf;
+    g.workgroups = ceil_div(ceil_div(N, 16), c.waves * c.cb) * ceil_div(M, 16 * c.rb);
+    return g;
+}
+
+template <int I>
+hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
+{
+    constexpr Cfg c = kCfg[I];
+    if (g.workgroups <= 0 || g.workgroups > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    const int m_tiles = (int)ceil_div(a.M, 16 * c.rb);
+    gemm_fp4_packed_kernel<c.waves, c.cb, c.rb, c.qs, c.pf, c.nt, c.ar>
+        <<<dim3((unsigned)g.workgroups), dim3(64 * c.waves), 0, stream>>>(
+            a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
     return hipGetLastError();
 }
 
@@ -319,20 +353,33 @@ hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 
 // Launch geometry (tile sharing only: the per-element arithmetic is the same
 // for all): 64 x 128 tiles once they still give each compute unit a
-// workgroup, 64 x 64 from 17 rows, else two waves of 16 x 16 streaming.
+// workgroup, 64 x 64 from 17 rows, else two waves of 16 x 16 streaming.  All
+// 16 rows of each A stage are staged even for a single row: with the MFMA
+// results kept in VGPRs, staging only the first 8 measured slower (K = 4096,
+// N = 14336, M = 1: 11.2 vs 10.7 us).
+Geometry geometry_fp4_packed(int64_t M, int64_t N, int64_t K)
+{
+    (void)K;
+    const int64_t nb = ceil_div(N, 16);
+    int id = 0;
+    if (M >= 64 && ceil_div(M, 64) * ceil_div(nb, 8) >= 256)
+        id = 2;
+    else if (M > 16)
+        id = 1;
+    return describe(id, M, N);
+}
+
 hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream)
 {
-    const int nb = (a.N + 15) / 16;
-    const int mt64 = (a.M + 63) / 64;
-    if (a.M >= 64 && mt64 * ((nb + 7) / 8) >= 256)
-        return launch_geometry<4, 2, 4, 1, 2, false>(a, stream);   // weights shared by row tiles
-    if (a.M > 16)
-        return launch_geometry<4, 1, 4, 1, 4>(a, stream);
-    // all 16 rows of each A stage are staged even for a single row: with the
-    // MFMA results kept in VGPRs, staging only the first 8 measured slower
-    // (K = 4096, N = 14336, M = 1: 11.2 vs 10.7 us)
-    return launch_geometry<2, 1, 1, 2, 4>(a, stream);
+    const Geometry g = geometry_fp4_packed(a.M, a.N, a.K);
+    switch (g.id) {
+    case 0: return launch_cfg<0>(a, g, stream);
+    case 1: return launch_cfg<1>(a, g, stream);
+    case 2: return launch_cfg<2>(a, g, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
+static_assert(kNumCfg == 3, "every table entry needs its case in launch_fp4w_packed");
 
 hipError_t launch_pack_fp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sB,
                            int64_t ldsb, uint8_t* Bp, hipStream_t stream)

@@ -233,12 +233,29 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(
 
 }  // namespace
 
-hipError_t launch_fp8bs(const GemmArgs& a, const Schedule& s, hipStream_t stream)
+// One geometry: BM x BN tiles, 6 stages in flight.
+Geometry geometry_fp8(int64_t M, int64_t N, int64_t K)
 {
-    (void)s;
-    const int n_tiles = (a.N + BN - 1) / BN;
-    const int m_tiles = (a.M + BM - 1) / BM;
-    gemm_fp8_kernel<6><<<dim3(n_tiles * m_tiles), dim3(256), 0, stream>>>(
+    (void)K;
+    Geometry g;
+    g.id = 0;
+    g.bm = BM;
+    g.bn = BN;
+    g.waves = 4;
+    g.a_rows = BM;
+    g.k_stage = BKS;
+    g.stages = 6;
+    g.workgroups = ceil_div(M, BM) * ceil_div(N, BN);
+    return g;
+}
+
+hipError_t launch_fp8bs(const GemmArgs& a, hipStream_t stream)
+{
+    const Geometry g = geometry_fp8(a.M, a.N, a.K);
+    if (g.workgroups > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    const int m_tiles = (int)ceil_div(a.M, BM);
+    gemm_fp8_kernel<6><<<dim3((unsigned)g.workgroups), dim3(256), 0, stream>>>(
         a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
         (const uint8_t*)a.B, a.ldb, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles);
     return hipGetLastError();

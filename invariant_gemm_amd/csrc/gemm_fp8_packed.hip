@@ -336,14 +336,52 @@ __global__ void pack_fp8_kernel(int N, int K, const uint8_t* __restrict__ B, int
     *reinterpret_cast<u32x4*>(Bp + u * 16) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool HALF = false,
-          int AR = 16 * RB>
-hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
+// One launch geometry: WAVES waves, RB x CB MFMA blocks per workgroup split
+// among the waves as WR x WC sub-tiles, KB_ST K blocks per stage, PF stages
+// in flight, half blocks, AR staged A rows.
+struct Cfg {
+    int waves, rb, cb, wr, wc, kb_st, pf;
+    bool half;
+    int ar;
+};
+
+// The geometry table.  Every entry runs the same per-element arithmetic.
+constexpr Cfg kCfg[] = {
+    /* 0 */ {8, 1, 1, 1, 1, 8, 4, false, 16},   // 16 x 16, eight waves streaming
+    /* 1 */ {8, 4, 1, 1, 1, 4, 4, false, 64},   // 64 x 16, eight waves
+    /* 2 */ {4, 4, 2, 2, 1, 2, 4, false, 64},   // 64 x 32
+    /* 3 */ {4, 4, 4, 2, 2, 2, 2, false, 64},   // 64 x 64
+    /* 4 */ {4, 1, 1, 1, 1, 8, 4, true, 16},    // 16 x 8 half blocks, four waves
+    /* 5 */ {4, 1, 1, 1, 1, 8, 4, true, 8},     //   the same, 8 rows of A staged
+};
+constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
+
+int64_t n_tiles_of(const Cfg& c, int64_t N) { return ceil_div(ceil_div(N, 16), c.cb) * (c.half ? 2 : 1); }
+
+Geometry describe(int id, int64_t M, int64_t N)
 {
-    const int n_tiles = ((a.N + 15) / 16 + CB - 1) / CB * (HALF ? 2 : 1);
-    const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-    gemm_fp8_packed_kernel<WAVES, RB, CB, WR, WC, KB_ST, PF, HALF, AR>
-        <<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0, stream>>>(
+    const Cfg& c = kCfg[id];
+    Geometry g;
+    g.id = id;
+    g.bm = 16 * c.rb;
+    g.bn = c.half ? 8 : 16 * c.cb;
+    g.waves = c.waves;
+    g.a_rows = c.ar;
+    g.k_stage = c.kb_st * KBK;
+    g.stages = c.pf;
+    g.workgroups = n_tiles_of(c, N) * ceil_div(M, 16 * c.rb);
+    return g;
+}
+
+template <int I>
+hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
+{
+    constexpr Cfg c = kCfg[I];
+    if (g.workgroups <= 0 || g.workgroups > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    const int m_tiles = (int)ceil_div(a.M, 16 * c.rb);
+    gemm_fp8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.half, c.ar>
+        <<<dim3((unsigned)g.workgroups), dim3(64 * c.waves), 0, stream>>>(
             a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
             (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles);
     return hipGetLastError();
@@ -356,36 +394,41 @@ hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 // unit a workgroup, 64 x 32 above 128 rows, 64 x 16 (eight waves) from 17
 // rows, and for M <= 16 one 16 x 16 block per workgroup with eight waves
 // streaming its weights -- or, while N/16 blocks would leave compute units
-// without a workgroup, half a block (8 columns, four waves) per workgroup.
-int fp8_packed_geometry(int M, int N)
+// without a workgroup, half a block (8 columns, four waves) per workgroup,
+// staging only the first 8 rows of A for calls of at most 8 rows (M = 1:
+// 9.4 -> 8.9 us at K = 7168, N = 2048; staging 4 measured slower).
+Geometry geometry_fp8_packed(int64_t M, int64_t N, int64_t K)
 {
-    const int nb = (N + 15) / 16;
-    const int mt64 = (M + 63) / 64;
-    if (M > 64 && mt64 * ((nb + 3) / 4) >= 256)
-        return 3;                                  // 64 x 64
-    if (M > 128)
-        return 2;                                  // 64 x 32
-    if (M > 16)
-        return 1;                                  // 64 x 16
-    if (nb < 256)
-        return 4;                                  // 16 x 8: N/8 workgroups
-    return 0;                                      // 16 x 16
+    (void)K;
+    const int64_t nb = ceil_div(N, 16);
+    int id;
+    if (M > 64 && ceil_div(M, 64) * ceil_div(nb, 4) >= 256)
+        id = 3;
+    else if (M > 128)
+        id = 2;
+    else if (M > 16)
+        id = 1;
+    else if (nb < 256)
+        id = M <= 8 ? 5 : 4;
+    else
+        id = 0;
+    return describe(id, M, N);
 }
 
 hipError_t launch_fp8_packed(const GemmArgs& a, hipStream_t stream)
 {
-    switch (fp8_packed_geometry(a.M, a.N)) {
-    case 3: return launch_geometry<4, 4, 4, 2, 2, 2, 2>(a, stream);
-    case 2: return launch_geometry<4, 4, 2, 2, 1, 2, 4>(a, stream);
-    case 1: return launch_geometry<8, 4, 1, 1, 1, 4, 4>(a, stream);
-    case 4:
-        // up to 8 rows: stage only the first 8 rows of A (M = 1: 9.4 -> 8.9 us
-        // at K = 7168, N = 2048); staging 4 measured slower
-        if (a.M <= 8) return launch_geometry<4, 1, 1, 1, 1, 8, 4, true, 8>(a, stream);
-        return launch_geometry<4, 1, 1, 1, 1, 8, 4, true>(a, stream);
-    default: return launch_geometry<8, 1, 1, 1, 1, 8, 4>(a, stream);
+    const Geometry g = geometry_fp8_packed(a.M, a.N, a.K);
+    switch (g.id) {
+    case 0: return launch_cfg<0>(a, g, stream);
+    case 1: return launch_cfg<1>(a, g, stream);
+    case 2: return launch_cfg<2>(a, g, stream);
+    case 3: return launch_cfg<3>(a, g, stream);
+    case 4: return launch_cfg<4>(a, g, stream);
+    case 5: return launch_cfg<5>(a, g, stream);
+    default: return hipErrorInvalidValue;
     }
 }
+static_assert(kNumCfg == 6, "every table entry needs its case in launch_fp8_packed");
 
 hipError_t launch_pack_fp8(int N, int K, const uint8_t* B, int64_t ldb, uint8_t* Bp,
                            hipStream_t stream)

@@ -310,14 +310,48 @@ __global__ void pack_mxfp4_kernel(int N, int K, const uint8_t* __restrict__ Bq, 
     Bp[(int64_t)NB * KB * CTILE + t * STILE + l] = n < N ? sE[(int64_t)(4 * kb + g) * ldse + n] : 0u;
 }
 
-template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool NT = true,
-          int AR = 16 * RB>
-hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
+// One launch geometry: WAVES waves, RB x CB MFMA blocks split among the
+// waves as WR x WC sub-tiles, KB_ST K blocks per stage, PF stages in flight,
+// non-temporal weight loads, AR staged A rows.
+struct Cfg {
+    int waves, rb, cb, wr, wc, kb_st, pf;
+    bool nt;
+    int ar;
+};
+
+// The geometry table.  Every entry runs the same per-element arithmetic.
+constexpr Cfg kCfg[] = {
+    /* 0 */ {4, 1, 4, 1, 1, 4, 4, true, 16},    // 16 x 64: four waves, one block each
+    /* 1 */ {4, 1, 4, 1, 1, 4, 4, true, 8},     //   the same, 8 rows of A staged
+    /* 2 */ {4, 4, 4, 2, 2, 2, 2, true, 64},    // 64 x 64, two K blocks per stage
+    /* 3 */ {4, 4, 4, 2, 2, 1, 4, false, 64},   // 64 x 64, one K block per stage, weights shared
+};
+constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
+
+Geometry describe(int id, int64_t M, int64_t N)
 {
-    const int n_tiles = ((a.N + 15) / 16 + CB - 1) / CB;
-    const int m_tiles = (a.M + 16 * RB - 1) / (16 * RB);
-    gemm_w4a8_packed_kernel<WAVES, RB, CB, WR, WC, KB_ST, PF, NT, AR>
-        <<<dim3(n_tiles * m_tiles), dim3(64 * WAVES), 0, stream>>>(
+    const Cfg& c = kCfg[id];
+    Geometry g;
+    g.id = id;
+    g.bm = 16 * c.rb;
+    g.bn = 16 * c.cb;
+    g.waves = c.waves;
+    g.a_rows = c.ar;
+    g.k_stage = c.kb_st * KBK;
+    g.stages = c.pf;
+    g.workgroups = ceil_div(ceil_div(N, 16), c.cb) * ceil_div(M, 16 * c.rb);
+    return g;
+}
+
+template <int I>
+hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
+{
+    constexpr Cfg c = kCfg[I];
+    if (g.workgroups <= 0 || g.workgroups > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    const int m_tiles = (int)ceil_div(a.M, 16 * c.rb);
+    gemm_w4a8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.nt, c.ar>
+        <<<dim3((unsigned)g.workgroups), dim3(64 * c.waves), 0, stream>>>(
             a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
             (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
     return hipGetLastError();
@@ -331,18 +365,33 @@ hipError_t launch_geometry(const GemmArgs& a, hipStream_t stream)
 // staged activation tile (of which only the first 8 rows are loaded when the
 // call has no more: LDS rows past them keep stale bytes, which reach only
 // output rows that are never stored, an MFMA output row depending on its own
-// A row alone); 64 x 64 tiles above that, with one K block per
-// stage once M > 128.
+// A row alone); 64 x 64 tiles above that, with one K block per stage once
+// M > 128.
+Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K)
+{
+    (void)K;
+    int id;
+    if (M > 128)
+        id = 3;
+    else if (M > 16)
+        id = 2;
+    else
+        id = M <= 8 ? 1 : 0;
+    return describe(id, M, N);
+}
+
 hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream)
 {
-    if (a.M > 128)
-        return launch_geometry<4, 4, 4, 2, 2, 1, 4, false>(a, stream);   // weights shared by row tiles
-    if (a.M > 16)
-        return launch_geometry<4, 4, 4, 2, 2, 2, 2>(a, stream);
-    if (a.M <= 8)
-        return launch_geometry<4, 1, 4, 1, 1, 4, 4, true, 8>(a, stream);   // 8 rows of A staged
-    return launch_geometry<4, 1, 4, 1, 1, 4, 4>(a, stream);
+    const Geometry g = geometry_w4a8_packed(a.M, a.N, a.K);
+    switch (g.id) {
+    case 0: return launch_cfg<0>(a, g, stream);
+    case 1: return launch_cfg<1>(a, g, stream);
+    case 2: return launch_cfg<2>(a, g, stream);
+    case 3: return launch_cfg<3>(a, g, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
+static_assert(kNumCfg == 4, "every table entry needs its case in launch_w4a8_packed");
 
 hipError_t launch_pack_mxfp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sE,
                              int64_t ldse, uint8_t* Bp, hipStream_t stream)

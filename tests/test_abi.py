@@ -144,9 +144,14 @@ def test_schedule_has_no_m_argument():
     decl = re.search(r"bi_status bi_schedule_query\(([^)]*)\)", hdr).group(1)
     params = [p.strip().split()[-1].lstrip("*") for p in decl.split(",")]
     assert params == ["dtype", "N", "K", "out"]
-    for dt in (bigemm.BI_BF16, bigemm.BI_FP8_BS, bigemm.BI_FP4_W):
+    for dt in (bigemm.BI_BF16, bigemm.BI_FP8_BS, bigemm.BI_FP4_W, bigemm.BI_W4A8):
         s = bigemm.schedule(dt, 8192, 8192)
-        assert s["mfma_m"] == 16 and s["waves"] == 4
+        assert s["mfma_m"] == 16 and s["mfma_n"] == 16
+        # the arithmetic is the same for every N and K the format accepts
+        for N, K in ((256, 512), (14336, 4096), (2048, 7168), (130, 1024)):
+            assert bigemm.schedule(dt, N, K) == s
+    assert bigemm.schedule(bigemm.BI_BF16, 8192, 8192)["order"] == bigemm.ORDER_SEQUENTIAL
+    assert bigemm.schedule(bigemm.BI_FP8_BS, 8192, 8192)["order"] == bigemm.ORDER_BLOCK_FMA
     assert lib.bi_schedule_query(7, 8192, 8192, ctypes.byref(bigemm.BiSchedule())) == UNSUP
     assert lib.bi_schedule_query(0, 8192, 8192, None) == NULL
     assert lib.bi_schedule_query(1, 8192, 100, ctypes.byref(bigemm.BiSchedule())) == SHAPE
@@ -281,3 +286,64 @@ def test_row_pitch_cap():
     assert lib.bi_gemm_bf16_packed(8, 64, 64, P, cap // 2 + 8, P, need, P, 64, None) == UNSUP
     need = bigemm.packed_b_bytes(bigemm.BI_W4A8, 64, 128)
     assert lib.bi_gemm_w4a8_packed(8, 64, 128, P, cap + 16, P, 1, P, need, P, 64, None) == UNSUP
+
+
+# ------------------------------------------------------------------ launch geometry
+
+GEOM_CASES = {
+    # entry: (N, K, Ms) -- the configs' shapes and M sweeps
+    "bf16": (8192, 8192, [2**i for i in range(9)] + [3, 17, 37, 100, 129, 255]),
+    "bf16_bt": (8192, 8192, [2**i for i in range(9)] + [3, 17, 37, 100, 129, 255]),
+    "bf16_packed": (8192, 8192, [2**i for i in range(9)] + [3, 17, 37, 100, 129, 160, 255]),
+    "fp8": (2048, 7168, list(range(1, 513))),
+    "fp8_packed": (2048, 7168, list(range(1, 513))),
+    "fp4": (14336, 4096, [1, 8, 64, 512, 3, 100, 257]),
+    "fp4_packed": (14336, 4096, [1, 8, 17, 33, 64, 65, 129, 512]),
+    "w4a8_packed": (14336, 4096, [1, 8, 16, 17, 64, 65, 129, 300, 512]),
+}
+
+
+@pytest.mark.parametrize("entry", sorted(GEOM_CASES))
+def test_geometry_query_covers_the_output(entry):
+    """At every M of the sweeps the geometry's tiles cover C exactly once:
+    workgroups = ceil(M / bm) * ceil(N / bn), the staged rows fit the tile, and
+    the geometry changes only with M (never its arithmetic: bi_schedule_query
+    has no M)."""
+    N, K, Ms = GEOM_CASES[entry]
+    ids = set()
+    for M in Ms:
+        g = bigemm.geometry(entry, M, N, K)
+        assert g["bm"] % 16 == 0 and g["bn"] in (8, 16, 32, 64, 128), g
+        assert 1 <= g["a_rows"] <= g["bm"] and 1 <= g["waves"] <= 8, g
+        assert g["k_stage"] > 0 and g["stages"] >= 1, g
+        assert g["workgroups"] == -(-M // g["bm"]) * -(-N // g["bn"]), (M, g)
+        if g["a_rows"] < g["bm"]:
+            assert M <= g["a_rows"], (M, g)      # only calls that fit the staged rows
+        ids.add(g["id"])
+    multi = {"bf16", "bf16_bt", "bf16_packed", "fp8_packed", "fp4_packed", "w4a8_packed"}
+    assert (len(ids) > 1) == (entry in multi), ids
+
+
+def test_geometry_query_headline_sweep():
+    # the headline sweep K = N = 8192: the packed kernel's tiles grow with M
+    # and every one fills the compute units once M allows it
+    seen = [bigemm.geometry("bf16_packed", M, 8192, 8192) for M in [2**i for i in range(9)]]
+    assert [g["bm"] for g in seen] == [16, 16, 16, 16, 16, 32, 32, 64, 64]
+    assert seen[-1]["bn"] == 128 and seen[-1]["workgroups"] == 256
+    assert all(g["workgroups"] >= 256 for g in seen)
+
+
+def test_geometry_query_grouped_and_errors():
+    g = bigemm.geometry("bf16_grouped_packed", 512, 2048, 7168, groups=8)
+    assert g["bm"] == 64
+    # at most one row slot per non-empty group at M = 1
+    g1 = bigemm.geometry("bf16_grouped_packed", 1, 2048, 7168, groups=8)
+    assert g1["workgroups"] == -(-2048 // g1["bn"])
+    out = ctypes.byref(bigemm.BiGeometry())
+    assert lib.bi_geometry_query(3, 8, 64, 64, 0, out) == SHAPE          # no groups
+    assert lib.bi_geometry_query(99, 8, 64, 64, 0, out) == UNSUP
+    assert lib.bi_geometry_query(0, 8, 64, 64, 0, None) == NULL
+    assert lib.bi_geometry_query(0, 0, 64, 64, 0, out) == SHAPE          # nothing launched
+    assert lib.bi_geometry_query(4, 8, 64, 100, 0, out) == SHAPE         # fp8 K % 128
+    assert lib.bi_geometry_query(6, 8, 63, 64, 0, out) == SHAPE          # fp4 odd N
+    assert lib.bi_geometry_query(0, -1, 64, 64, 0, out) == SHAPE
