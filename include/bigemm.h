@@ -30,7 +30,8 @@
  *   - All matrix pointers are DEVICE pointers (hipMalloc'd or torch tensors).
  *     The caller owns every buffer; the library never allocates, frees or
  *     synchronises, and keeps no mutable global state, so calls are
- *     thread-safe and reentrant.
+ *     thread-safe and reentrant -- except bi_decode_attention_bf16_noalloc,
+ *     whose fixed per-GPU scratch array is shared by its calls.
  *   - Matrices are row-major with an explicit leading dimension (elements
  *     for bf16/fp32, bytes for 8-bit and packed 4-bit data).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Each invariant
@@ -419,6 +420,34 @@ bi_status bi_decode_attention_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t D
                                    const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                                    const int32_t* seq_lens, float scale, uint16_t* O,
                                    void* workspace, size_t ws_bytes, int kernel, void* stream);
+
+/*
+ * bi_decode_attention_bf16 without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The split-KV group states go to
+ * a fixed scratch array of BI_ATTN_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends (its device address is looked
+ * up on the first call on each device, with that device current; the
+ * current device must be the one `stream` belongs to).  Nothing is
+ * allocated or freed by this call.
+ *
+ * Same arguments, results (bit for bit) and errors as
+ * bi_decode_attention_bf16, except: BI_ATTN_SPLIT returns BI_ERR_WORKSPACE
+ * (and launches nothing) when bi_decode_attention_workspace_bytes(B, Hq,
+ * Hkv, Lmax) exceeds BI_ATTN_SCRATCH_BYTES; BI_ATTN_AUTO then runs the
+ * single-pass kernel (same bits).  BI_ERR_LAUNCH if the scratch address
+ * cannot be obtained.
+ *
+ * All calls on one GPU share its scratch array and it keeps the last call's
+ * contents: calls that overlap on one GPU (concurrent streams, several host
+ * threads) race and must be serialised by the caller.
+ */
+#define BI_ATTN_SCRATCH_BYTES ((size_t)16 << 20)
+
+bi_status bi_decode_attention_bf16_noalloc(int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                           int64_t Lmax, const uint16_t* Q, const uint16_t* K,
+                                           const uint16_t* V, const int32_t* seq_lens,
+                                           float scale, uint16_t* O, int kernel, void* stream);
 
 /* The arithmetic of a format (bi_schedule).  There is no M argument by
  * design, and the result does not depend on N or K either: N and K are

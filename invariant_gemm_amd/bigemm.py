@@ -84,6 +84,9 @@ lib.bi_splitk_choose.restype = _i32
 lib.bi_splitk_choose.argtypes = [_i64, _i64, _i64]
 lib.bi_schedule_query.restype = _i32
 lib.bi_schedule_query.argtypes = [_i32, _i64, _i64, ctypes.POINTER(BiSchedule)]
+lib.bi_decode_attention_bf16_noalloc.restype = _i32
+lib.bi_decode_attention_bf16_noalloc.argtypes = [_i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
+                                                 ctypes.c_float, _vp, _i32, _vp]
 lib.bi_geometry_query.restype = _i32
 lib.bi_geometry_query.argtypes = [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(BiGeometry)]
 lib.bi_status_str.restype = ctypes.c_char_p
@@ -502,4 +505,35 @@ def decode_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, seq_lens
                                         V.data_ptr(), seq_lens.data_ptr(), float(scale),
                                         out.data_ptr(), wp, wb, k, _stream()),
            "bi_decode_attention_bf16")
+    return out
+
+
+ATTN_SCRATCH_BYTES = 16 << 20      # BI_ATTN_SCRATCH_BYTES
+
+
+def decode_attention_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                             seq_lens: torch.Tensor, scale: float, out: torch.Tensor,
+                             kernel: str = "auto") -> torch.Tensor:
+    """bi_decode_attention_bf16_noalloc: the same results as decode_attention,
+    with the split-KV states in the library's fixed per-GPU scratch array.
+    Nothing is allocated: the caller passes the output tensor."""
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if t.dtype not in _BF16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name}: expected a contiguous bf16 device tensor")
+    if Q.dim() != 3 or K.dim() != 4 or V.shape != K.shape:
+        raise ValueError("Q [B,Hq,D], K and V [B,Hkv,Lmax,D]")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or seq_lens.dim() != 1:
+        raise TypeError("seq_lens: int32 device vector")
+    B, Hq, D = Q.shape
+    Hkv, Lmax = K.shape[1], K.shape[2]
+    if K.shape[0] != B or K.shape[3] != D:
+        raise ValueError(f"K, V: expected [{B}, Hkv, Lmax, {D}], got {tuple(K.shape)}")
+    _shape(seq_lens, (B,), "seq_lens")
+    if out.dtype not in _BF16 or not out.is_contiguous() or tuple(out.shape) != (B, Hq, D):
+        raise ValueError(f"out: expected a contiguous bf16 tensor of shape {(B, Hq, D)}")
+    _same_device(Q.device, K=K, V=V, seq_lens=seq_lens, out=out)
+    _check(lib.bi_decode_attention_bf16_noalloc(B, Hq, Hkv, D, Lmax, Q.data_ptr(), K.data_ptr(),
+                                                V.data_ptr(), seq_lens.data_ptr(), float(scale),
+                                                out.data_ptr(), _ATTN_KERNELS[kernel], _stream()),
+           "bi_decode_attention_bf16_noalloc")
     return out

@@ -203,26 +203,56 @@ int bi_decode_attention_choice(int64_t B, int64_t Hq, int64_t Hkv, int64_t Lmax)
     return (B * Hkv < kAttnSplitBelow && attn_groups(Lmax) > 1) ? BI_ATTN_SPLIT : BI_ATTN_SINGLE;
 }
 
-bi_status bi_decode_attention_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Lmax,
-                                   const uint16_t* Q, const uint16_t* K, const uint16_t* V,
-                                   const int32_t* seq_lens, float scale, uint16_t* O,
-                                   void* workspace, size_t ws_bytes, int kernel, void* stream)
+namespace {
+
+// Validation shared by both attention entry points; *noop for B == 0 or
+// Hq == 0.  Touches no device.
+bi_status attn_validate(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Lmax,
+                        const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                        const int32_t* seq_lens, uint16_t* O, int kernel, int64_t* G, bool* noop)
 {
-    int64_t G = 0;
-    bi_status st = attn_sizes(B, Hq, Hkv, Lmax, &G);
+    *noop = false;
+    bi_status st = attn_sizes(B, Hq, Hkv, Lmax, G);
     if (st != BI_OK)
         return st;
     if (D < 0)
         return BI_ERR_SHAPE;
     if (D != BI_ATTN_HEAD_DIM || kernel < BI_ATTN_AUTO || kernel > BI_ATTN_SPLIT)
         return BI_ERR_UNSUPPORTED;
-    if (B == 0 || Hq == 0)
+    if (B == 0 || Hq == 0) {
+        *noop = true;
         return BI_OK;
+    }
     if (!Q || !O || !seq_lens || (Lmax > 0 && (!K || !V)))
         return BI_ERR_NULL;
     if (!aligned16(Q) || !aligned16(O) || ((uintptr_t)seq_lens & 3u) ||
         (Lmax > 0 && (!aligned16(K) || !aligned16(V))))
         return BI_ERR_ALIGN;
+    return BI_OK;
+}
+
+bi_status attn_run(int64_t B, int64_t Hq, int64_t Hkv, int64_t G, int64_t Lmax,
+                   const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                   const int32_t* seq_lens, float scale, uint16_t* O, float* ws, bool split,
+                   void* stream)
+{
+    const float c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
+    AttnArgs a{B, Hq, Hkv, G, Lmax, Q, K, V, seq_lens, c, O, ws};
+    return launched(launch_attn_decode(a, split, (hipStream_t)stream));
+}
+
+}  // namespace
+
+bi_status bi_decode_attention_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t Lmax,
+                                   const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                   const int32_t* seq_lens, float scale, uint16_t* O,
+                                   void* workspace, size_t ws_bytes, int kernel, void* stream)
+{
+    int64_t G = 0;
+    bool noop = false;
+    bi_status st = attn_validate(B, Hq, Hkv, D, Lmax, Q, K, V, seq_lens, O, kernel, &G, &noop);
+    if (st != BI_OK || noop)
+        return st;
     const size_t need = (size_t)attn_ws_floats(B, Hkv, G, Lmax) * sizeof(float);
     const bool ws_ok = need == 0 || (workspace && ws_bytes >= need);
     if (kernel == BI_ATTN_SPLIT && !ws_ok)
@@ -232,11 +262,34 @@ bi_status bi_decode_attention_bf16(int64_t B, int64_t Hq, int64_t Hkv, int64_t D
     bool split = kernel == BI_ATTN_SPLIT;
     if (kernel == BI_ATTN_AUTO)
         split = ws_ok && bi_decode_attention_choice(B, Hq, Hkv, Lmax) == BI_ATTN_SPLIT;
-    const float c = (float)((double)scale * 1.4426950408889634);   // scale * log2(e)
-    AttnArgs a{B, Hq, Hkv, G, Lmax, Q, K, V, seq_lens, c, O, (float*)workspace};
-    return launched(launch_attn_decode(a, split, (hipStream_t)stream));
+    return attn_run(B, Hq, Hkv, G, Lmax, Q, K, V, seq_lens, scale, O, (float*)workspace, split,
+                    stream);
 }
 
+static_assert(BI_ATTN_SCRATCH_BYTES == kAttnScratchBytes, "one scratch size");
+
+bi_status bi_decode_attention_bf16_noalloc(int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                           int64_t Lmax, const uint16_t* Q, const uint16_t* K,
+                                           const uint16_t* V, const int32_t* seq_lens,
+                                           float scale, uint16_t* O, int kernel, void* stream)
+{
+    int64_t G = 0;
+    bool noop = false;
+    bi_status st = attn_validate(B, Hq, Hkv, D, Lmax, Q, K, V, seq_lens, O, kernel, &G, &noop);
+    if (st != BI_OK || noop)
+        return st;
+    const size_t need = (size_t)attn_ws_floats(B, Hkv, G, Lmax) * sizeof(float);
+    const bool fits = need <= BI_ATTN_SCRATCH_BYTES;
+    if (kernel == BI_ATTN_SPLIT && !fits)
+        return BI_ERR_WORKSPACE;
+    bool split = kernel == BI_ATTN_SPLIT;
+    if (kernel == BI_ATTN_AUTO)
+        split = fits && bi_decode_attention_choice(B, Hq, Hkv, Lmax) == BI_ATTN_SPLIT;
+    float* ws = nullptr;
+    if (split && need > 0 && attn_scratch(&ws) != hipSuccess)
+        return BI_ERR_LAUNCH;
+    return attn_run(B, Hq, Hkv, G, Lmax, Q, K, V, seq_lens, scale, O, ws, split, stream);
+}
 
 bi_status bi_schedule_query(bi_dtype dtype, int64_t N, int64_t K, bi_schedule* out)
 {

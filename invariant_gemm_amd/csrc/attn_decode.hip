@@ -37,6 +37,8 @@
 // whose row addresses follow that permutation).  K and V are read once per
 // call and loaded non-temporal.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -423,6 +425,48 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(
 }
 
 }  // namespace
+
+// ------------------------------------------------------------ fixed scratch
+//
+// Split-KV group states for callers that cannot allocate (bi_decode_attention_
+// bf16_noalloc): a file-scope device array, one copy per GPU, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in); it takes the array's device address from
+// hipGetSymbolAddress, once per device with that device current, and passes
+// that address to the kernels as the workspace.  Every call on one GPU shares
+// the array, so calls that overlap on one GPU race.  Nothing in it needs to
+// start at zero: the split kernel writes every group state the merge kernel
+// uses before the merge reads it.
+static __device__ __align__(256) float scratch[kAttnScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t attn_scratch(float** ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return e;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = static_cast<float*>(p);
+    return hipSuccess;
+}
 
 int64_t attn_groups(int64_t Lmax) { return (Lmax + kGroup - 1) / kGroup; }
 

@@ -97,4 +97,9 @@ int64_t attn_groups(int64_t Lmax);
 int64_t attn_ws_floats(int64_t B, int64_t Hkv, int64_t G, int64_t Lmax);
 hipError_t launch_attn_decode(const AttnArgs& a, bool split, hipStream_t stream);
 
+// The fixed split-KV scratch of bi_decode_attention_bf16_noalloc: its size,
+// and its device address on the current device (looked up once per device).
+constexpr size_t kAttnScratchBytes = (size_t)16 << 20;
+hipError_t attn_scratch(float** ptr);
+
 }  // namespace bigemm
