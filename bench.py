@@ -432,32 +432,67 @@ def device_info(torch):
     return info
 
 
-def hbm_probe(torch, nbytes=1 << 30, rounds=5):
-    """Measured streaming rates over 1 GiB with torch's own device copy and
-    sum kernels: the practical HBM roof beside the 8 TB/s nominal one (context,
-    not part of the library)."""
-    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-    dst = torch.empty_like(src)
-    copy, read = [], []
-    for _ in range(rounds + 1):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e2 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        src.sum()
-        e2.record()
-        e2.synchronize()
-        copy.append(e0.elapsed_time(e1))
-        read.append(e1.elapsed_time(e2))
-    copy, read = sorted(copy[1:]), sorted(read[1:])
-    del src, dst
-    return {"bytes": nbytes,
-            "copy_GBps": round(2 * nbytes / (copy[len(copy) // 2] * 1e6), 1),
-            "read_GBps": round(nbytes / (read[len(read) // 2] * 1e6), 1),
-            "note": "median of torch's device copy (read + write counted) and fp32 sum "
-                    "(read) over 1 GiB; the nominal HBM peak is 8000 GB/s"}
+def measured_roof(torch, bg, rounds=5):
+    """The measured roofs the kernels are compared with, from the library's
+    own probes (bi_probe_stream_read, bi_probe_empty), timed like the GEMM
+    legs (graph replay of back-to-back launches, buffers rotated so that no
+    launch finds its data in the 256 MB Infinity Cache):
+
+    * read roof: one 128 MiB stream per launch (the size of the K = N = 8192
+      bf16 weights) over 8 rotated buffers, for 256..2048 workgroups, 4 or 8
+      loads in flight per thread, default or non-temporal loads -- the best
+      configuration is the measured roof; the same configuration over one
+      1 GiB buffer;
+    * small streams: 14.7 MB (the fp8 K = 7168, N = 2048 weights) and 31.2 MB
+      (the fp4 K = 4096, N = 14336 codes and scales) read by 256 workgroups,
+      rotated over windows of 1 GiB -- the floor a GEMM streaming that many
+      bytes cannot beat;
+    * launch floor: back-to-back launches of an empty kernel."""
+    one, nbuf = 128 << 20, 8
+    bufs = [torch.zeros(one, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+    sink = torch.zeros(2048 * 256, dtype=torch.int32, device="cuda")
+    state = {"i": 0}
+
+    def reader(views, wg, flags):
+        def fn():
+            v = views[state["i"] % len(views)]
+            state["i"] += 1
+            bg.probe_stream_read(v, wg, flags, sink)
+        return fn
+
+    best = None
+    table = {}
+    for wg in (256, 512, 1024, 2048):
+        for flags, name in ((0, "default"), (bg.PROBE_NONTEMPORAL, "nt"),
+                            (bg.PROBE_UNROLL8, "default_u8"),
+                            (bg.PROBE_NONTEMPORAL | bg.PROBE_UNROLL8, "nt_u8")):
+            med, mn = time_launches(torch, reader(bufs, wg, flags), reps=nbuf, rounds=rounds)
+            gbs = one / (med * 1e3)
+            table[f"wg{wg}_{name}"] = round(gbs, 1)
+            if best is None or gbs > best[0]:
+                best = (gbs, wg, flags, med)
+    del bufs
+    big = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
+    med1g, _ = time_launches(torch, reader([big], best[1], best[2]), reps=2, rounds=rounds)
+    small = {}
+    for label, nbytes in (("fp8_weights_14.7MB", 7168 * 2048),
+                          ("fp4_weights_31.2MB", 4096 * 14336 // 2 + (4096 // 32) * 14336)):
+        nb = (nbytes + 4095) // 4096 * 4096
+        views = [big[k * nb:(k + 1) * nb] for k in range(min(64, (1 << 30) // nb))]
+        med, mn = time_launches(torch, reader(views, 256, best[2]), reps=len(views), rounds=rounds)
+        small[label] = {"bytes": nbytes, "us": round(med, 2), "us_min": round(mn, 2),
+                        "GBps": round(nbytes / (med * 1e3), 1)}
+    del big
+    emp, emp_min = time_launches(torch, bg.probe_empty, reps=200, rounds=rounds)
+    return {"read_roof_GBps": round(best[0], 1),
+            "read_roof_config": {"workgroups": best[1], "flags": best[2],
+                                 "us_per_128MiB": round(best[3], 2)},
+            "read_1GiB_GBps": round((1 << 30) / (med1g * 1e3), 1),
+            "read_128MiB_GBps_by_config": table,
+            "small_streams": small,
+            "empty_launch_us": round(emp, 3), "empty_launch_us_min": round(emp_min, 3),
+            "note": "bi_probe_stream_read / bi_probe_empty, graph replay, HIP events on the "
+                    "launch stream; the nominal HBM peak is 8000 GB/s"}
 
 
 def single_launch_us(torch, fn, n=15):
@@ -740,12 +775,17 @@ def _derive(per_m):
 
 # ------------------------------------------------------------------ legs
 
+MEASURED_ROOF = {"GBps": None}
+
+
 def sweep(torch, wl, Ms, nbytes_fn, peak, rounds):
     out = {}
     for M in Ms:
         med, mn = time_launches(torch, lambda: wl.launch(M), reps=wl.nbuf, rounds=rounds)
         r = roof(M, wl.N, wl.K, nbytes_fn(M, wl.N, wl.K), med, peak)
         r["us_min"] = round(mn, 2)
+        if MEASURED_ROOF["GBps"]:
+            r["frac_hbm_measured"] = round(r["gbs"] / MEASURED_ROOF["GBps"], 4)
         out[str(M)] = r
     return out
 
@@ -819,32 +859,6 @@ def attention_probe(torch, bg, L=4096, Hq=64, Hkv=8):
     log("probe: 3 x split B=1 done")
 
 
-def vendor_matmul(torch, packed_us, rounds, K=8192, N=8192):
-    """Context only, not batch-invariant: torch.matmul (hipBLASLt) on the
-    headline shape, weights rotated over HBM copies as in the headline, next
-    to the packed invariant kernel's time at the same M."""
-    g = torch.Generator(device="cuda")
-    g.manual_seed(20262)
-    nb = max(2, -(-ROT_BYTES // (K * N * 2)))
-    Bs = [(torch.randn((K, N), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
-          for _ in range(nb)]
-    res = {}
-    for M in SWEEP_C2:
-        A = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
-        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        i = [0]
-
-        def fn():
-            torch.matmul(A, Bs[i[0] % nb], out=C)
-            i[0] += 1
-        med, _ = time_launches(torch, fn, reps=nb * 2, rounds=max(3, rounds // 2))
-        res[str(M)] = {"us": round(med, 2), "tflops": round(flops(M, N, K) / med / 1e6, 2),
-                       "packed_invariant_over_vendor_time": round(packed_us[str(M)] / med, 3)}
-    del Bs
-    torch.cuda.empty_cache()
-    return res
-
-
 def replay(torch, bg, inputs, steps=1000):
     """Dynamic-batching replay on the bf16 projection shape: pool of 4096 rows,
     `steps` batches of 1..256 distinct rows; GPU time of the GEMM launches."""
@@ -890,6 +904,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline only, no extra legs")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only run a known-size copy plus 3 launches per M (for rocprofv3 --pmc)")
+    ap.add_argument("--roof", action="store_true",
+                    help="only the measured roofs (streaming read, small streams, launch floor)")
     ap.add_argument("--attention", action="store_true",
                     help="only the decode-attention leg (one JSON object)")
     ap.add_argument("--attention-probe", action="store_true",
@@ -936,6 +952,9 @@ def main():
 
     if args.attention:
         print(json.dumps(decode_attention(torch, bigemm, args.rounds)), flush=True)
+        return
+    if args.roof:
+        print(json.dumps(measured_roof(torch, bigemm, args.rounds)), flush=True)
         return
     if args.attention_probe:
         attention_probe(torch, bigemm)
@@ -1000,6 +1019,9 @@ def main():
     }
 
     if not args.quick:
+        out["measured_roof"] = measured_roof(torch, bigemm)
+        MEASURED_ROOF["GBps"] = out["measured_roof"]["read_roof_GBps"]
+        out["roofline"]["frac_measured_roof"] = round(gbs / MEASURED_ROOF["GBps"], 4)
         out["per_m"] = sweep(torch, wl, SWEEP_C2, bytes_bf16, MFMA_PEAK_TFLOPS["bf16"], args.rounds)
         for M in SWEEP_C2:
             out["per_m"][str(M)]["us_single_launch"] = single_launch_us(torch, lambda: wl.launch(M))
@@ -1020,7 +1042,6 @@ def main():
                                round(out["bf16_rowmajor_K8192_N8192"][str(M)]["us"] / med, 3),
                            "packed_invariant_over_splitk_time": round(packed_us[str(M)] / med, 3)}
         out["splitk_gap"] = gap
-        out["vendor_matmul_bf16_K8192_N8192"] = vendor_matmul(torch, packed_us, args.rounds)
         del ws
         del c2
         c2t = C2T(torch, bigemm, inputs)
@@ -1055,7 +1076,6 @@ def main():
         del moe
         out["replay_bf16_K8192_N8192"] = replay(torch, bigemm, inputs)
         out["decode_attention_L4096_Hq64_Hkv8_D128"] = decode_attention(torch, bigemm, args.rounds)
-        out["hbm_probe"] = hbm_probe(torch)
         out["device"] = device_info(torch)
 
     if not args.no_cpu_baseline:

@@ -492,6 +492,31 @@ bi_status bi_gemm_bf16_splitk(int64_t M, int64_t N, int64_t K,
 /* Split count bi_gemm_bf16_splitk uses for splits == 0. */
 int bi_splitk_choose(int64_t M, int64_t N, int64_t K);
 
+/*
+ * Measurement probes (no GEMM): the reference points the GEMM kernels are
+ * measured against.
+ *
+ * bi_probe_stream_read reads `bytes` (a multiple of 16) of the device buffer
+ * `buf` (16-byte aligned) once with 16-byte loads: `workgroups` workgroups
+ * of 256 threads each stream a contiguous 4 KiB-aligned share.  It writes
+ * nothing to `out` in practice (a device buffer of workgroups * 256 uint32,
+ * written only if a thread's XOR of its data equals a fixed key), so the
+ * kernel's time is the time to read the buffer: the measured HBM read roof
+ * when the buffer is not cache-resident.  flags: BI_PROBE_NONTEMPORAL marks
+ * the loads non-temporal; BI_PROBE_UNROLL8 keeps 8 loads per thread in
+ * flight instead of 4.  Errors: BI_ERR_NULL, BI_ERR_ALIGN, BI_ERR_UNSUPPORTED
+ * (workgroups outside 1..65536, a share of 2 GiB or more, unknown flags).
+ *
+ * bi_probe_empty launches one empty kernel: back-to-back launches of it time
+ * the launch floor.
+ */
+#define BI_PROBE_NONTEMPORAL 1
+#define BI_PROBE_UNROLL8 2
+
+bi_status bi_probe_stream_read(const void* buf, size_t bytes, int workgroups, int flags,
+                               uint32_t* out, void* stream);
+bi_status bi_probe_empty(void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -87,6 +87,10 @@ lib.bi_schedule_query.argtypes = [_i32, _i64, _i64, ctypes.POINTER(BiSchedule)]
 lib.bi_decode_attention_bf16_noalloc.restype = _i32
 lib.bi_decode_attention_bf16_noalloc.argtypes = [_i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
                                                  ctypes.c_float, _vp, _i32, _vp]
+lib.bi_probe_stream_read.restype = _i32
+lib.bi_probe_stream_read.argtypes = [_vp, _sz, _i32, _i32, _vp, _vp]
+lib.bi_probe_empty.restype = _i32
+lib.bi_probe_empty.argtypes = [_vp]
 lib.bi_geometry_query.restype = _i32
 lib.bi_geometry_query.argtypes = [_i32, _i64, _i64, _i64, _i64, ctypes.POINTER(BiGeometry)]
 lib.bi_status_str.restype = ctypes.c_char_p
@@ -537,3 +541,20 @@ def decode_attention_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
                                                 out.data_ptr(), _ATTN_KERNELS[kernel], _stream()),
            "bi_decode_attention_bf16_noalloc")
     return out
+
+
+PROBE_NONTEMPORAL, PROBE_UNROLL8 = 1, 2
+
+
+def probe_stream_read(buf: torch.Tensor, workgroups: int, flags: int, out: torch.Tensor) -> None:
+    """bi_probe_stream_read: read every byte of `buf` once (measurement only)."""
+    if not buf.is_cuda or not buf.is_contiguous() or not out.is_cuda or out.dtype != torch.int32 \
+            or out.numel() < workgroups * 256:
+        raise ValueError("probe_stream_read: contiguous device buffer, int32 out of workgroups*256")
+    _check(lib.bi_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), workgroups,
+                                    flags, out.data_ptr(), _stream()), "bi_probe_stream_read")
+
+
+def probe_empty() -> None:
+    """bi_probe_empty: one empty kernel on the current stream."""
+    _check(lib.bi_probe_empty(_stream()), "bi_probe_empty")

@@ -716,4 +716,26 @@ bi_status bi_gemm_bf16_splitk(int64_t M, int64_t N, int64_t K, const uint16_t* A
     return launched(launch_bf16_splitk(a, workspace, S, (hipStream_t)stream));
 }
 
+bi_status bi_probe_stream_read(const void* buf, size_t bytes, int workgroups, int flags,
+                               uint32_t* out, void* stream)
+{
+    if (bytes == 0)
+        return BI_OK;
+    if (!buf || !out)
+        return BI_ERR_NULL;
+    if (!aligned16(buf) || bytes % 16 || ((uintptr_t)out & 3u))
+        return BI_ERR_ALIGN;
+    if (workgroups < 1 || workgroups > 65536 || (flags & ~3))
+        return BI_ERR_UNSUPPORTED;
+    // each workgroup's range is addressed with 32-bit offsets
+    if ((bytes + workgroups - 1) / workgroups + 4096 > 0x7FFFFFFFu)
+        return BI_ERR_UNSUPPORTED;
+    return launched(launch_probe_stream_read((const uint8_t*)buf, bytes, workgroups,
+                                             (flags & BI_PROBE_UNROLL8) ? 8 : 4,
+                                             (flags & BI_PROBE_NONTEMPORAL) != 0, out,
+                                             (hipStream_t)stream));
+}
+
+bi_status bi_probe_empty(void* stream) { return launched(launch_probe_empty((hipStream_t)stream)); }
+
 }  // extern "C"

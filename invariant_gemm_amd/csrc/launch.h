@@ -102,4 +102,9 @@ hipError_t launch_attn_decode(const AttnArgs& a, bool split, hipStream_t stream)
 constexpr size_t kAttnScratchBytes = (size_t)16 << 20;
 hipError_t attn_scratch(float** ptr);
 
+// Measurement kernels (bi_probe_stream_read, bi_probe_empty).
+hipError_t launch_probe_stream_read(const uint8_t* buf, uint64_t bytes, int workgroups, int unroll,
+                                    bool nt, uint32_t* out, hipStream_t stream);
+hipError_t launch_probe_empty(hipStream_t stream);
+
 }  // namespace bigemm
