@@ -904,6 +904,9 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline only, no extra legs")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="only run a known-size copy plus 3 launches per M (for rocprofv3 --pmc)")
+    ap.add_argument("--legs", default=None,
+                    help="only these per-M sweeps, comma separated (bf16_packed, bf16, bf16_bt, "
+                         "fp8, fp8_packed, fp4, fp4_packed, w4a8, moe); one JSON object")
     ap.add_argument("--roof", action="store_true",
                     help="only the measured roofs (streaming read, small streams, launch floor)")
     ap.add_argument("--attention", action="store_true",
@@ -955,6 +958,22 @@ def main():
         return
     if args.roof:
         print(json.dumps(measured_roof(torch, bigemm, args.rounds)), flush=True)
+        return
+    if args.legs:
+        legs = {"bf16_packed": (C2P, SWEEP_C2, bytes_bf16, "bf16"), "bf16": (C2, SWEEP_C2, bytes_bf16, "bf16"),
+                "bf16_bt": (C2T, SWEEP_C2, bytes_bf16, "bf16"), "fp8": (C3, SWEEP_C3, bytes_fp8, "fp8"),
+                "fp8_packed": (C3P, SWEEP_C3, bytes_fp8, "fp8"), "fp4": (C4, SWEEP_C4, bytes_fp4, "bf16"),
+                "fp4_packed": (C4P, SWEEP_C4, bytes_fp4, "bf16"),
+                "w4a8": (W4A8, W4A8.SWEEP, bytes_w4a8, "fp8"), "moe": (MoE, MoE.SWEEP, None, "bf16")}
+        res = {}
+        for name in args.legs.split(","):
+            cls, Ms, nb, peak = legs[name]
+            wl = cls(torch, bigemm, inputs)
+            res[name] = sweep(torch, wl, Ms, nb if nb else wl.nbytes, MFMA_PEAK_TFLOPS[peak], args.rounds)
+            res[name + "_us"] = {m: v["us"] for m, v in res[name].items()}
+            del wl
+            torch.cuda.empty_cache()
+        print(json.dumps(res), flush=True)
         return
     if args.attention_probe:
         attention_probe(torch, bigemm)
