@@ -175,6 +175,27 @@ def gemm_bf16_grouped(A: np.ndarray, offsets, Bs):
     return C, S
 
 
+def gemm_fp8bs_grouped(qA: np.ndarray, sA: np.ndarray, offsets, qBs, sBs):
+    """Grouped (mixture-of-experts) fp8 block-scaled GEMM by its definition:
+    rows [offsets[g], offsets[g+1]) of (qA, sA) times expert g's (qBs[g],
+    sBs[g]), one plain gemm_fp8bs per group.  Returns (C, S) fp64 [M,N]."""
+    qA = _rows(qA, np.uint8, "qA")
+    sA = _rows(sA, np.float32, "sA")
+    offsets = [int(o) for o in offsets]
+    if len(offsets) != len(qBs) + 1 or len(sBs) != len(qBs) or offsets[0] != 0 \
+            or offsets[-1] != qA.shape[0] or any(b < a for a, b in zip(offsets, offsets[1:])):
+        raise ValueError("offsets must run from 0 to M, non-decreasing, one more than groups")
+    N = qBs[0].shape[1]
+    C = np.zeros((qA.shape[0], N), np.float64)
+    S = np.zeros((qA.shape[0], N), np.float64)
+    for g, (qB, sB) in enumerate(zip(qBs, sBs)):
+        lo, hi = offsets[g], offsets[g + 1]
+        if hi > lo:
+            C[lo:hi], S[lo:hi] = gemm_fp8bs(np.ascontiguousarray(qA[lo:hi]),
+                                            np.ascontiguousarray(sA[lo:hi]), qB, sB)
+    return C, S
+
+
 def gemm_fp8bs(qA: np.ndarray, sA: np.ndarray, qB: np.ndarray, sB: np.ndarray):
     """qA uint8 e4m3fn [M,K], sA fp32 [M,K/128], qB uint8 e4m3fn [K,N],
     sB fp32 [K/128, ceil(N/128)] -> (C, S) fp64 [M,N]."""

@@ -352,6 +352,49 @@ def test_grouped_exact_vs_fraction():
         oracle.gemm_bf16_grouped(A, [0, 3, 2, 7], Bs)
 
 
+def test_grouped_fp8_exact_vs_fraction():
+    """The grouped fp8 block-scaled GEMM is one block-scaled GEMM per group of
+    rows (including an empty group), each value sum_k (e4m3(qa) sA)(e4m3(qb) sB)
+    over the 128-long blocks; checked against exact rational arithmetic with
+    the e4m3fn values written out from the format definition."""
+    from fractions import Fraction
+
+    def e4m3(c):
+        s, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+        v = Fraction(m, 8) * Fraction(1, 2**6) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2)**(e - 7)
+        return -v if s else v
+
+    g = np.random.default_rng(31)
+    M, N, K, E = 7, 132, 256, 3                       # N: a ragged second 128-column block
+    qA = g.integers(0, 256, size=(M, K)).astype(np.uint8)
+    qA[(qA & 0x7F) == 0x7F] = 0x38                    # no NaN codes
+    sA = np.ldexp(1.0, g.integers(-4, 4, size=(M, K // 128))).astype(np.float32) * \
+        np.float32(1.5)
+    qBs, sBs = [], []
+    for _ in range(E):
+        qB = g.integers(0, 256, size=(K, N)).astype(np.uint8)
+        qB[(qB & 0x7F) == 0x7F] = 0x30
+        qBs.append(qB)
+        sBs.append(np.ldexp(1.0, g.integers(-4, 4, size=(K // 128, 2))).astype(np.float32))
+    offsets = [0, 3, 3, 7]                            # group 1 is empty
+    C, S = oracle.gemm_fp8bs_grouped(qA, sA, offsets, qBs, sBs)
+    for e in range(E):
+        for m in range(offsets[e], offsets[e + 1]):
+            for n in (0, 5, 127, 128, 131):
+                terms = [e4m3(int(qA[m, k])) * Fraction(float(sA[m, k // 128])) *
+                         e4m3(int(qBs[e][k, n])) * Fraction(float(sBs[e][k // 128, n // 128]))
+                         for k in range(K)]
+                exact = sum(terms)
+                assert abs(C[m, n] - float(exact)) <= 2.0**-52 * K * float(sum(abs(t) for t in terms))
+                assert abs(S[m, n] - float(sum(abs(t) for t in terms))) <= \
+                    2.0**-52 * K * float(sum(abs(t) for t in terms))
+    # each group's rows are exactly its expert's plain GEMM
+    C2, _ = oracle.gemm_fp8bs(np.ascontiguousarray(qA[3:]), np.ascontiguousarray(sA[3:]), qBs[2], sBs[2])
+    assert np.array_equal(C[3:], C2)
+    with pytest.raises(ValueError):
+        oracle.gemm_fp8bs_grouped(qA, sA, [0, 4, 3, 7], qBs, sBs)
+
+
 # ------------------------------------------------------------------ W4A8 (fp8 x OCP MXFP4)
 
 
