@@ -330,6 +330,56 @@ class MoE:
         return self.routes[T][2] * K * N * 2 + 2 * T * K + 2 * T * N
 
 
+class MoE8:
+    """Grouped (mixture-of-experts) fp8 block-scaled GEMM: E = 8 experts,
+    K = 7168, N = 2048, e4m3fn activations with 1x128 scales, e4m3fn weights
+    with 128x128 scales, T tokens routed top-1 uniformly (seeded); packed
+    expert weights rotated over HBM copies."""
+    E, K, N = 8, 7168, 2048
+    SWEEP = [1, 8, 64, 512]
+
+    def __init__(self, torch, bg, inputs):
+        self.torch, self.bg = torch, bg
+        T = max(self.SWEEP)
+        qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((T, self.K), 1.0, 611))
+        self.A = torch.from_numpy(qA).cuda()
+        self.sA = torch.from_numpy(sA).cuda()
+        Bs, sBs = [], []
+        for e in range(self.E):
+            qB, sB = inputs.quant_fp8_tiles(inputs.normal_f32((self.K, self.N), 1.0, 612 + e))
+            Bs.append(torch.from_numpy(qB).cuda())
+            sBs.append(sB)
+        one = bg.pack_b_fp8_grouped(Bs)
+        del Bs
+        self.sB = torch.from_numpy(np.concatenate(sBs, axis=0)).cuda()
+        self.nbuf = rotation(one.data.numel())
+        self.Bp = [one] + [bg.PackedWeights(one.dtype, one.K, one.N, one.data.clone())
+                           for _ in range(self.nbuf - 1)]
+        for b in self.Bp:
+            b.groups = self.E
+        self.routes = {}
+        for t in self.SWEEP:
+            expert = inputs.route_tokens(t, self.E, 613 + t, 0.0)
+            order, offsets = inputs.group_by_expert(expert, self.E)
+            perm = torch.as_tensor(order, device="cuda")
+            self.routes[t] = (self.A[:t].index_select(0, perm), self.sA[:t].index_select(0, perm),
+                              torch.as_tensor(offsets, device="cuda"),
+                              int(np.count_nonzero(np.diff(offsets))))
+        self.C = torch.empty((T, self.N), dtype=torch.bfloat16, device="cuda")
+        self.i = 0
+
+    def launch(self, T):
+        j = self.i % self.nbuf
+        self.i += 1
+        A, sA, off, _ = self.routes[T]
+        self.bg.gemm_fp8_blockscaled_grouped_packed(A, sA, off, self.Bp[j], self.sB, out=self.C[:T])
+
+    def nbytes(self, T, N, K):
+        hit = self.routes[T][3]
+        return bytes_fp8(T, N, K) - K * N - 4 * (K // 128) * ((N + 127) // 128) + \
+            hit * (K * N + 4 * (K // 128) * ((N + 127) // 128))
+
+
 # ------------------------------------------------------------------ cpu baseline
 
 def cpu_baseline(budget_s=12.0):
@@ -906,7 +956,7 @@ def main():
                     help="only run a known-size copy plus 3 launches per M (for rocprofv3 --pmc)")
     ap.add_argument("--legs", default=None,
                     help="only these per-M sweeps, comma separated (bf16_packed, bf16, bf16_bt, "
-                         "fp8, fp8_packed, fp4, fp4_packed, w4a8, moe); one JSON object")
+                         "fp8, fp8_packed, fp4, fp4_packed, w4a8, moe, moe_fp8); one JSON object")
     ap.add_argument("--roof", action="store_true",
                     help="only the measured roofs (streaming read, small streams, launch floor)")
     ap.add_argument("--attention", action="store_true",
@@ -964,7 +1014,8 @@ def main():
                 "bf16_bt": (C2T, SWEEP_C2, bytes_bf16, "bf16"), "fp8": (C3, SWEEP_C3, bytes_fp8, "fp8"),
                 "fp8_packed": (C3P, SWEEP_C3, bytes_fp8, "fp8"), "fp4": (C4, SWEEP_C4, bytes_fp4, "bf16"),
                 "fp4_packed": (C4P, SWEEP_C4, bytes_fp4, "bf16"),
-                "w4a8": (W4A8, W4A8.SWEEP, bytes_w4a8, "fp8"), "moe": (MoE, MoE.SWEEP, None, "bf16")}
+                "w4a8": (W4A8, W4A8.SWEEP, bytes_w4a8, "fp8"), "moe": (MoE, MoE.SWEEP, None, "bf16"),
+                "moe_fp8": (MoE8, MoE8.SWEEP, None, "fp8")}
         res = {}
         for name in args.legs.split(","):
             cls, Ms, nb, peak = legs[name]
@@ -1093,6 +1144,10 @@ def main():
         out["moe_grouped_bf16_E8_K7168_N2048"] = sweep(torch, moe, MoE.SWEEP, moe.nbytes,
                                                        MFMA_PEAK_TFLOPS["bf16"], args.rounds)
         del moe
+        moe8 = MoE8(torch, bigemm, inputs)
+        out["moe_grouped_fp8_E8_K7168_N2048"] = sweep(torch, moe8, MoE8.SWEEP, moe8.nbytes,
+                                                      MFMA_PEAK_TFLOPS["fp8"], args.rounds)
+        del moe8
         out["replay_bf16_K8192_N8192"] = replay(torch, bigemm, inputs)
         out["decode_attention_L4096_Hq64_Hkv8_D128"] = decode_attention(torch, bigemm, args.rounds)
         out["device"] = device_info(torch)

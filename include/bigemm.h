@@ -111,7 +111,8 @@ typedef enum bi_entry {
     BI_ENTRY_FP8_PACKED = 5,          /* bi_gemm_fp8_blockscaled_packed  */
     BI_ENTRY_FP4 = 6,                 /* bi_gemm_fp4_w                   */
     BI_ENTRY_FP4_PACKED = 7,          /* bi_gemm_fp4_w_packed            */
-    BI_ENTRY_W4A8_PACKED = 8          /* bi_gemm_w4a8_packed             */
+    BI_ENTRY_W4A8_PACKED = 8,         /* bi_gemm_w4a8_packed             */
+    BI_ENTRY_FP8_GROUPED_PACKED = 9   /* bi_gemm_fp8_blockscaled_grouped_packed */
 } bi_entry;
 
 /* The launch geometry an entry point uses for one call: how the output
@@ -302,6 +303,32 @@ bi_status bi_gemm_fp8_blockscaled_packed(int64_t M, int64_t N, int64_t K,
                                          const void* Bp, size_t bp_bytes,
                                          const float* sB, int64_t ldsb,
                                          uint16_t* C, int64_t ldc, void* stream);
+
+/*
+ * Grouped GEMM for mixture-of-experts layers in the fp8 block-scaled format:
+ * rows of A (and sA) are grouped by expert, and group g is multiplied by its
+ * own packed weights and weight scales.
+ *   offsets : device int32 [G + 1], as for bi_gemm_bf16_grouped_packed
+ *             (read on the device, clamped into [0, M] and made
+ *             non-decreasing; rows a malformed table leaves uncovered are not
+ *             written)
+ *   A, sA   : as for bi_gemm_fp8_blockscaled, [M,K] and [M, K/128]
+ *   Bp      : G packed fp8 matrices [K,N] (bi_pack_b_fp8 layout), each
+ *             bi_packed_b_bytes(BI_FP8_BS, N, K) bytes, back to back
+ *   sB      : G fp32 weight-scale matrices [K/128, ceil(N/128)] with row
+ *             pitch ldsb, back to back (expert g's at sB + g*(K/128)*ldsb)
+ *   C       : bf16 [M,N], ldc >= N
+ * Each row's arithmetic is exactly that of bi_gemm_fp8_blockscaled with its
+ * expert's weights and scales, so a token's output is bit-identical whatever
+ * the routing of the other tokens.  Requires K % 128 == 0.  One kernel on
+ * `stream`.
+ */
+bi_status bi_gemm_fp8_blockscaled_grouped_packed(int64_t G, const int32_t* offsets, int64_t M,
+                                                 int64_t N, int64_t K, const uint8_t* A,
+                                                 int64_t lda, const float* sA, int64_t ldsa,
+                                                 const void* Bp, size_t bp_bytes, const float* sB,
+                                                 int64_t ldsb, uint16_t* C, int64_t ldc,
+                                                 void* stream);
 
 /* Pack e2m1 codes Bq[K, N/2] (pitch ldbq >= N/2) and e4m3fn scales
  * sB[K/32, N] (pitch ldsb >= N) -- the operands of bi_gemm_fp4_w -- into Bp

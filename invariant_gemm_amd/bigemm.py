@@ -43,7 +43,7 @@ class BiGeometry(ctypes.Structure):
 
 ORDER_SEQUENTIAL, ORDER_BLOCK_FMA = 0, 1
 ENTRIES = {"bf16": 0, "bf16_bt": 1, "bf16_packed": 2, "bf16_grouped_packed": 3, "fp8": 4,
-           "fp8_packed": 5, "fp4": 6, "fp4_packed": 7, "w4a8_packed": 8}
+           "fp8_packed": 5, "fp4": 6, "fp4_packed": 7, "w4a8_packed": 8, "fp8_grouped_packed": 9}
 
 
 lib.bi_gemm_bf16.restype = _i32
@@ -73,6 +73,9 @@ lib.bi_pack_b_fp8.argtypes = [_i64, _i64, _vp, _i64, _vp, _sz, _vp]
 lib.bi_gemm_fp8_blockscaled_packed.restype = _i32
 lib.bi_gemm_fp8_blockscaled_packed.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz,
                                                _vp, _i64, _vp, _i64, _vp]
+lib.bi_gemm_fp8_blockscaled_grouped_packed.restype = _i32
+lib.bi_gemm_fp8_blockscaled_grouped_packed.argtypes = [_i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp,
+                                                       _i64, _vp, _sz, _vp, _i64, _vp, _i64, _vp]
 lib.bi_pack_b_fp4.restype = _i32
 lib.bi_pack_b_fp4.argtypes = [_i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
 lib.bi_gemm_fp4_w_packed.restype = _i32
@@ -362,6 +365,48 @@ def gemm_fp8_blockscaled_packed(A: torch.Tensor, sA: torch.Tensor, Bp: PackedWei
                                               _ld(sA), Bp.data.data_ptr(), Bp.data.numel(),
                                               sB.data_ptr(), _ld(sB), C.data_ptr(), _ld(C),
                                               _stream()), "bi_gemm_fp8_blockscaled_packed")
+    return C
+
+
+def pack_b_fp8_grouped(Bs) -> PackedWeights:
+    """Pack G row-major e4m3fn matrices [K,N] (one per expert) back to back."""
+    Bs = [_mat(B, _U8, "B") for B in Bs]
+    K, N = Bs[0].shape
+    if any(tuple(B.shape) != (K, N) for B in Bs):
+        raise ValueError("all experts' weight matrices must have the same shape")
+    one = packed_b_bytes(BI_FP8_BS, N, K)
+    buf = torch.empty(max(one * len(Bs), 16), dtype=torch.uint8, device=Bs[0].device)
+    for g, B in enumerate(Bs):
+        _check(lib.bi_pack_b_fp8(N, K, B.data_ptr(), _ld(B), buf.data_ptr() + g * one, one, _stream()),
+               "bi_pack_b_fp8")
+    pw = PackedWeights(BI_FP8_BS, K, N, buf)
+    pw.groups = len(Bs)
+    return pw
+
+
+def gemm_fp8_blockscaled_grouped_packed(A: torch.Tensor, sA: torch.Tensor, offsets: torch.Tensor,
+                                        Bp: PackedWeights, sB: torch.Tensor,
+                                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rows [offsets[g], offsets[g+1]) of (A, sA) times expert g's packed fp8
+    weights and scales; sB holds the G scale matrices stacked: [G*K/128, ceil(N/128)]."""
+    A = _mat(A, _U8, "A")
+    sA = _mat(sA, (torch.float32,), "sA")
+    sB = _mat(sB, (torch.float32,), "sB")
+    M, K = A.shape
+    if Bp.dtype != BI_FP8_BS or Bp.K != K or not hasattr(Bp, "groups"):
+        raise ValueError("grouped packed fp8 weights do not match A")
+    kb = _blocks(K, 128, "gemm_fp8_blockscaled_grouped_packed")
+    _shape(sA, (M, kb), "sA")
+    _shape(sB, (Bp.groups * kb, (Bp.N + 127) // 128), "sB")
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1 \
+            or offsets.numel() != Bp.groups + 1 or (offsets.numel() > 1 and offsets.stride(0) != 1):
+        raise ValueError("offsets: a contiguous int32 device tensor of G + 1 entries")
+    _same_device(A.device, sA=sA, Bp=Bp.data, sB=sB, offsets=offsets)
+    C = _out(M, Bp.N, A.device, out)
+    _check(lib.bi_gemm_fp8_blockscaled_grouped_packed(
+        Bp.groups, offsets.data_ptr(), M, Bp.N, K, A.data_ptr(), _ld(A), sA.data_ptr(), _ld(sA),
+        Bp.data.data_ptr(), Bp.data.numel(), sB.data_ptr(), _ld(sB), C.data_ptr(), _ld(C), _stream()),
+        "bi_gemm_fp8_blockscaled_grouped_packed")
     return C
 
 

@@ -349,6 +349,15 @@ bi_status bi_geometry_query(bi_entry entry, int64_t M, int64_t N, int64_t K, int
             return BI_ERR_SHAPE;
         g = entry == BI_ENTRY_FP4 ? geometry_fp4(M, N, K) : geometry_fp4_packed(M, N, K);
         break;
+    case BI_ENTRY_FP8_GROUPED_PACKED:
+        if (K % 128)
+            return BI_ERR_SHAPE;
+        if (groups < 1)
+            return BI_ERR_SHAPE;
+        if (groups > 65536)
+            return BI_ERR_UNSUPPORTED;
+        g = geometry_fp8_grouped(M, N, K, groups);
+        break;
     case BI_ENTRY_W4A8_PACKED:
         if (K % 128 || N % 2)
             return BI_ERR_SHAPE;
@@ -560,6 +569,44 @@ bi_status bi_gemm_fp8_blockscaled_packed(int64_t M, int64_t N, int64_t K, const 
         return BI_ERR_UNSUPPORTED;
     GemmArgs a{(int)M, (int)N, (int)K, A, lda, sA, ldsa, Bp, 0, sB, ldsb, C, ldc};
     return launched(launch_fp8_packed(a, (hipStream_t)stream));
+}
+
+bi_status bi_gemm_fp8_blockscaled_grouped_packed(int64_t G, const int32_t* offsets, int64_t M,
+                                                 int64_t N, int64_t K, const uint8_t* A,
+                                                 int64_t lda, const float* sA, int64_t ldsa,
+                                                 const void* Bp, size_t bp_bytes, const float* sB,
+                                                 int64_t ldsb, uint16_t* C, int64_t ldc,
+                                                 void* stream)
+{
+    bi_status st = check_dims(M, N, K);
+    if (st != BI_OK)
+        return st;
+    if (G < 0 || K % 128)
+        return BI_ERR_SHAPE;
+    if (G > 65536)
+        return BI_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0)
+        return BI_OK;
+    if (G == 0)
+        return BI_ERR_SHAPE;                          // rows but no group to own them
+    const int64_t kb = K / 128, nb = (N + 127) / 128;
+    if (!offsets || !C || (K > 0 && (!A || !sA || !Bp || !sB)))
+        return BI_ERR_NULL;
+    if ((K > 0 && (lda < K || ldsa < kb || ldsb < nb)) || ldc < N)
+        return BI_ERR_STRIDE;
+    if (K > 0 && (!pitch_ok(lda, 1) || !pitch_ok(ldsa, 4) || !pitch_ok(ldsb, 4)))
+        return BI_ERR_UNSUPPORTED;
+    if (((uintptr_t)C & 1u) || ((uintptr_t)offsets & 3u) ||
+        (K > 0 && (!aligned16(A) || lda % 16 || !aligned16(Bp) || !aligned4(sA) || !aligned4(sB))))
+        return BI_ERR_ALIGN;
+    const size_t one = bi_packed_b_bytes(BI_FP8_BS, N, K);
+    if (bp_bytes / (size_t)G < one)
+        return BI_ERR_WORKSPACE;
+    if (((M + 15) / 16 + G) * ((N + 15) / 16) * 2 > 0x7FFFFFFF)
+        return BI_ERR_UNSUPPORTED;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, sA, ldsa, Bp, 0, sB, ldsb, C, ldc};
+    GroupArgs g{offsets, (int)G, (int64_t)one};
+    return launched(launch_fp8_grouped_packed(a, g, kb * ldsb, (hipStream_t)stream));
 }
 
 bi_status bi_pack_b_fp4(int64_t N, int64_t K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sB,

@@ -34,6 +34,8 @@
 // keep stale bytes, which reach only output rows that are never stored -- an
 // MFMA output row depends on its own A row alone, and each row's scale FMA on
 // its own sA value.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -43,12 +45,23 @@ namespace {
 constexpr int KBK = 128;       // K per scale block = one MFMA
 constexpr int BTILE = 2048;    // packed bytes per (column block, K block)
 
-template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool HALF, int AR>
+//
+// GROUPED: rows [offsets[g], offsets[g+1]) of A, sA and C belong to group g,
+// which uses the g-th packed weight matrix (b_stride bytes apart) and the
+// g-th weight-scale matrix (sb_stride floats apart).  Row slot mt enumerates
+// the groups' row tiles in order; a workgroup finds its group by walking the
+// offsets (clamped into [0, M] and made non-decreasing, so no table can send
+// an access outside A, sA or C), and slots past the last tile exit at once.
+// A row's arithmetic is that of the ungrouped kernel with its group's
+// weights, whatever the other groups hold.
+template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool HALF, int AR,
+          bool GROUPED>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     int M, int N, int K,
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t ldsa,
     const uint8_t* __restrict__ Bp, const float* __restrict__ sB, int64_t ldsb,
-    uint16_t* __restrict__ C, int64_t ldc, int m_tiles)
+    uint16_t* __restrict__ C, int64_t ldc, int m_tiles,
+    const int32_t* __restrict__ offsets, int n_groups, int64_t b_stride, int64_t sb_stride)
 {
     constexpr int NTHR = 64 * WAVES;
     constexpr int BM = 16 * RB;
@@ -82,14 +95,33 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     const int mt = tile - ntile * m_tiles;
     const int nt = HALF ? ntile >> 1 : ntile;          // column tile
     const int ch = HALF ? ntile & 1 : 0;               // which 8 columns of the block
-    const int m0 = mt * BM;
+    int m0 = mt * BM;
+    int row_end = M;                                  // rows [m0, row_end) are this tile's
+    if constexpr (GROUPED) {
+        int first = 0, g = 0, lo = 0, hi = 0;
+        for (; g < n_groups; ++g) {
+            lo = min(max(offsets[g], lo), M);
+            hi = min(max(offsets[g + 1], lo), M);
+            const int tiles_g = (hi - lo + BM - 1) / BM;
+            if (mt < first + tiles_g)
+                break;
+            first += tiles_g;
+            lo = hi;
+        }
+        if (g == n_groups)
+            return;                                   // an unused slot (uniform per workgroup)
+        m0 = lo + (mt - first) * BM;
+        row_end = hi;
+        Bp += g * b_stride;
+        sB += g * sb_stride;
+    }
     const int NB = (N + 15) >> 4;
     const int nkb = K / KBK;
     const int ncb = (N + 127) >> 7;                   // columns of sB in use
     const int nbw = nt * CB;                          // first column block of the workgroup
 
     const int nst = (nkb + KB_ST - 1) / KB_ST;
-    const int rows_valid = M - m0 < BM ? M - m0 : BM;
+    const int rows_valid = row_end - m0 < BM ? row_end - m0 : BM;
     const int li = lane & 15;
     const int lg = lane >> 4;
     const uint32_t OOB = 0x80000000u;
@@ -299,7 +331,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = m0 + 16 * (wr0 + r) + 4 * lg + j;
-                    if (row < M && col < N && (!HALF || li < 8))
+                    if (row < row_end && col < N && (!HALF || li < 8))
                         C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc[r][c][j]);
                 }
             }
@@ -358,7 +390,9 @@ constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
 int64_t n_tiles_of(const Cfg& c, int64_t N) { return ceil_div(ceil_div(N, 16), c.cb) * (c.half ? 2 : 1); }
 
-Geometry describe(int id, int64_t M, int64_t N)
+int64_t m_tiles_of(const Cfg& c, int64_t M, int64_t groups);
+
+Geometry describe(int id, int64_t M, int64_t N, int64_t groups = 0)
 {
     const Cfg& c = kCfg[id];
     Geometry g;
@@ -369,23 +403,59 @@ Geometry describe(int id, int64_t M, int64_t N)
     g.a_rows = c.ar;
     g.k_stage = c.kb_st * KBK;
     g.stages = c.pf;
-    g.workgroups = n_tiles_of(c, N) * ceil_div(M, 16 * c.rb);
+    g.workgroups = n_tiles_of(c, N) * m_tiles_of(c, M, groups);
     return g;
 }
 
+// Row slots of a grouped call: at most k = min(groups, M) groups hold rows,
+// and sum ceil(r_g / BM) <= floor((M + k (BM - 1)) / BM) -- one slot at M = 1.
+int64_t m_tiles_of(const Cfg& c, int64_t M, int64_t groups)
+{
+    const int64_t bm = 16 * c.rb;
+    if (groups <= 0)
+        return ceil_div(M, bm);
+    const int64_t k = std::min<int64_t>(groups, M);
+    return (M + k * (bm - 1)) / bm;
+}
+
 template <int I>
-hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
+hipError_t launch_cfg(const GemmArgs& a, const GroupArgs* grp, int64_t sb_stride, const Geometry& g,
+                      hipStream_t stream)
 {
     constexpr Cfg c = kCfg[I];
     if (g.workgroups <= 0 || g.workgroups > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
-    const int m_tiles = (int)ceil_div(a.M, 16 * c.rb);
-    gemm_fp8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.half, c.ar>
-        <<<dim3((unsigned)g.workgroups), dim3(64 * c.waves), 0, stream>>>(
-            a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
-            (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles);
+    const int m_tiles = (int)m_tiles_of(c, a.M, grp ? grp->n_groups : 0);
+    const dim3 grid((unsigned)g.workgroups), block(64 * c.waves);
+    if (grp)
+        gemm_fp8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.half, c.ar, true>
+            <<<grid, block, 0, stream>>>(
+                a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
+                (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles,
+                grp->offsets, grp->n_groups, grp->b_stride, sb_stride);
+    else
+        gemm_fp8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.half, c.ar, false>
+            <<<grid, block, 0, stream>>>(
+                a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
+                (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles,
+                nullptr, 0, 0, 0);
     return hipGetLastError();
 }
+
+hipError_t launch_id(const GemmArgs& a, const GroupArgs* grp, int64_t sb_stride, const Geometry& g,
+                     hipStream_t stream)
+{
+    switch (g.id) {
+    case 0: return launch_cfg<0>(a, grp, sb_stride, g, stream);
+    case 1: return launch_cfg<1>(a, grp, sb_stride, g, stream);
+    case 2: return launch_cfg<2>(a, grp, sb_stride, g, stream);
+    case 3: return launch_cfg<3>(a, grp, sb_stride, g, stream);
+    case 4: return launch_cfg<4>(a, grp, sb_stride, g, stream);
+    case 5: return launch_cfg<5>(a, grp, sb_stride, g, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+static_assert(kNumCfg == 6, "every table entry needs its case in launch_id");
 
 }  // namespace
 
@@ -397,38 +467,51 @@ hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
 // without a workgroup, half a block (8 columns, four waves) per workgroup,
 // staging only the first 8 rows of A for calls of at most 8 rows (M = 1:
 // 9.4 -> 8.9 us at K = 7168, N = 2048; staging 4 measured slower).
+namespace {
+int fp8_family(int64_t M, int64_t N)
+{
+    const int64_t nb = ceil_div(N, 16);
+    if (M > 64 && ceil_div(M, 64) * ceil_div(nb, 4) >= 256)
+        return 3;
+    if (M > 128)
+        return 2;
+    if (M > 16)
+        return 1;
+    if (nb < 256)
+        return M <= 8 ? 5 : 4;
+    return 0;
+}
+}  // namespace
+
 Geometry geometry_fp8_packed(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
-    const int64_t nb = ceil_div(N, 16);
-    int id;
-    if (M > 64 && ceil_div(M, 64) * ceil_div(nb, 4) >= 256)
-        id = 3;
-    else if (M > 128)
-        id = 2;
-    else if (M > 16)
-        id = 1;
-    else if (nb < 256)
-        id = M <= 8 ? 5 : 4;
-    else
-        id = 0;
-    return describe(id, M, N);
+    return describe(fp8_family(M, N), M, N);
+}
+
+// Grouped calls: the geometry follows the mean rows per group (any choice
+// gives the same bits); the 8-row variant only when the whole call has at
+// most 8 rows (all of them may fall into one group).
+Geometry geometry_fp8_grouped(int64_t M, int64_t N, int64_t K, int64_t groups)
+{
+    (void)K;
+    const int64_t mean = ceil_div(M, groups);
+    int id = fp8_family(mean > 0 ? mean : 1, N);
+    if (id == 5 && M > 8)
+        id = 4;
+    return describe(id, M, N, groups);
 }
 
 hipError_t launch_fp8_packed(const GemmArgs& a, hipStream_t stream)
 {
-    const Geometry g = geometry_fp8_packed(a.M, a.N, a.K);
-    switch (g.id) {
-    case 0: return launch_cfg<0>(a, g, stream);
-    case 1: return launch_cfg<1>(a, g, stream);
-    case 2: return launch_cfg<2>(a, g, stream);
-    case 3: return launch_cfg<3>(a, g, stream);
-    case 4: return launch_cfg<4>(a, g, stream);
-    case 5: return launch_cfg<5>(a, g, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_id(a, nullptr, 0, geometry_fp8_packed(a.M, a.N, a.K), stream);
 }
-static_assert(kNumCfg == 6, "every table entry needs its case in launch_fp8_packed");
+
+hipError_t launch_fp8_grouped_packed(const GemmArgs& a, const GroupArgs& g, int64_t sb_stride,
+                                     hipStream_t stream)
+{
+    return launch_id(a, &g, sb_stride, geometry_fp8_grouped(a.M, a.N, a.K, g.n_groups), stream);
+}
 
 hipError_t launch_pack_fp8(int N, int K, const uint8_t* B, int64_t ldb, uint8_t* Bp,
                            hipStream_t stream)

@@ -59,6 +59,7 @@ Geometry geometry_bf16_packed(int64_t M, int64_t N, int64_t K);
 Geometry geometry_bf16_grouped(int64_t M, int64_t N, int64_t K, int64_t groups);
 Geometry geometry_fp8(int64_t M, int64_t N, int64_t K);
 Geometry geometry_fp8_packed(int64_t M, int64_t N, int64_t K);
+Geometry geometry_fp8_grouped(int64_t M, int64_t N, int64_t K, int64_t groups);
 Geometry geometry_fp4(int64_t M, int64_t N, int64_t K);
 Geometry geometry_fp4_packed(int64_t M, int64_t N, int64_t K);
 Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K);
@@ -72,6 +73,8 @@ hipError_t launch_bf16_grouped_packed(const GemmArgs& a, const GroupArgs& g, hip
 hipError_t launch_fp8bs(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_fp4w(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_fp8_packed(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_fp8_grouped_packed(const GemmArgs& a, const GroupArgs& g, int64_t sb_stride,
+                                     hipStream_t stream);
 hipError_t launch_pack_fp8(int N, int K, const uint8_t* B, int64_t ldb, uint8_t* Bp,
                            hipStream_t stream);
 hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream);

@@ -224,6 +224,25 @@ def test_grouped_validation():
     assert f(1 << 20, 8) == UNSUP
 
 
+def test_grouped_fp8_validation():
+    need = bigemm.packed_b_bytes(bigemm.BI_FP8_BS, 64, 256)
+    f = lambda G, M, N=64, K=256, off=P, A=P, sA=P, Bp=P, nb=None, sB=P, ldsb=1, C=P: \
+        lib.bi_gemm_fp8_blockscaled_grouped_packed(G, off, M, N, K, A, K, sA, K // 128, Bp,
+                                                   need * G if nb is None else nb, sB, ldsb, C, N, None)
+    assert f(-1, 8) == SHAPE
+    assert f(0, 8) == SHAPE                    # rows but no group
+    assert f(3, 8, K=200) == SHAPE             # K % 128
+    assert f(0, 0) == OK
+    assert f(3, 0, off=None, A=None, sA=None, Bp=None, sB=None, C=None) == OK
+    assert f(3, 8, off=None) == NULL
+    assert f(3, 8, sB=None) == NULL
+    assert f(3, 8, ldsb=0) == STRIDE
+    assert f(3, 8, nb=need * 3 - 1) == WS
+    assert f(3, 8, off=P + 2) == ALIGN
+    assert f(3, 8, sB=P + 2) == ALIGN
+    assert f(1 << 20, 8) == UNSUP
+
+
 def test_w4a8_validation():
     need = lambda N, K: bigemm.packed_b_bytes(bigemm.BI_W4A8, N, K)
     assert need(2048, 7168) == 128 * 56 * 1088 and need(64, 100) == 0 and need(63, 128) == 0
@@ -339,6 +358,10 @@ def test_geometry_query_grouped_and_errors():
     # at most one row slot per non-empty group at M = 1
     g1 = bigemm.geometry("bf16_grouped_packed", 1, 2048, 7168, groups=8)
     assert g1["workgroups"] == -(-2048 // g1["bn"])
+    for M in (1, 8, 64, 512, 4096):
+        g8 = bigemm.geometry("fp8_grouped_packed", M, 2048, 7168, groups=8)
+        assert g8["workgroups"] >= -(-M // g8["bm"]) * -(-2048 // g8["bn"])
+    assert lib.bi_geometry_query(9, 8, 64, 100, 2, ctypes.byref(bigemm.BiGeometry())) == SHAPE
     out = ctypes.byref(bigemm.BiGeometry())
     assert lib.bi_geometry_query(3, 8, 64, 64, 0, out) == SHAPE          # no groups
     assert lib.bi_geometry_query(99, 8, 64, 64, 0, out) == UNSUP
