@@ -13,8 +13,8 @@
 // or batch composition (the invariance definition in section
 // "什么是batch invariance" of the QbitAI article).
 //
-// Workgroup: 256 threads = 4 waves, output tile 64 x 16; wave w owns rows
-// 16w .. 16w+15 of the tile.  N is covered by N/16 workgroups.
+// Workgroup: 256 threads = 4 waves, output tile (16 RB) x 16 (or x 8 on
+// half blocks); wave w owns rows 16w .. 16w+15 of the tile.
 // Stage = 256 K rows (two scale blocks):
 //   A [M,K] bytes --buffer_load_dwordx4--> VGPR --> LDS [m][k] (16-byte
 //     chunks XOR-swizzled by row) --ds_read_b128 x2--> 32 k per lane
@@ -29,15 +29,11 @@ namespace bigemm {
 namespace {
 
 constexpr int BN = 16;
-constexpr int BM = 64;
 constexpr int BKS = 256;                  // K rows per stage
 constexpr int KB = 128;                   // scale block = one MFMA
 constexpr int KB_PER_ST = BKS / KB;       // 2
-constexpr int A_STAGE = BM * BKS;         // 16 KiB
-constexpr int A_LD = A_STAGE / (256 * 16);   // 4 chunks per lane
 constexpr int B_STAGE = BKS * 16 + (BKS / 32) * 128;   // 5 KiB
 constexpr int S_STAGE = 2 * 256 * 4;                  // one sA and one sB slot per lane
-constexpr int STAGE = A_STAGE + B_STAGE + S_STAGE;
 
 typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
@@ -56,13 +52,25 @@ __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
 }
 
-template <int PF>
+// RB row blocks of 16 per workgroup (BM = 16 RB rows, wave w computing rows
+// 16w .. 16w+15).  HALF: the workgroup owns 8 of a 16-column block's
+// columns, so twice as many workgroups share the weights at small M; it
+// loads only those 8 bytes of each B row and places them in both halves of
+// the LDS row, so the MFMA's other 8 output columns repeat them and are not
+// stored -- each stored column sees exactly the operands, K order and
+// scales of the full-block path.
+template <int PF, int RB, bool HALF>
 __global__ __launch_bounds__(256) void gemm_fp8_kernel(
     int M, int N, int K,
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t ldsa,
     const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ sB, int64_t ldsb,
     uint16_t* __restrict__ C, int64_t ldc, int m_tiles)
 {
+    constexpr int BM = 16 * RB;
+    constexpr int A_STAGE = BM * BKS;            // bytes
+    constexpr int A_LD = A_STAGE / (256 * 16);   // chunks per lane
+    constexpr int STAGE = A_STAGE + B_STAGE + S_STAGE;
+    static_assert(A_LD * 256 * 16 == A_STAGE, "A stage must split evenly over the threads");
     static_assert(PF % 2 == 0, "the LDS double buffer is indexed by stage parity");
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
@@ -70,9 +78,9 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int tile = xcd_remap(blockIdx.x, gridDim.x);
-    const int nt = tile / m_tiles;
-    const int mt = tile - nt * m_tiles;
-    const int n0 = nt * BN;
+    const int ntile = tile / m_tiles;
+    const int mt = tile - ntile * m_tiles;
+    const int n0 = HALF ? (ntile >> 1) * BN + 8 * (ntile & 1) : ntile * BN;
     const int m0 = mt * BM;
     const int nb = n0 / 128;                    // column block of sB
 
@@ -91,10 +99,11 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(
     }
     const uint32_t b_voff = (uint32_t)(tid * ldb);          // row tid of the stage
     const int b_lds = b_row_addr(tid);
-    // scales: lanes 0..127 fetch sA[m0 + (tid & 63)][kb0 + (tid >> 6)];
+    // scales: lanes below 2*BM fetch sA[m0 + tid % BM][kb0 + tid / BM];
     //         lanes 0..1 fetch sB[kb0 + tid][nb]; other lanes point past the extent
     const uint32_t OOB = 0x80000000u;
-    const uint32_t sa_voff = tid < 128 ? (uint32_t)(((tid & 63) * ldsa + (tid >> 6)) * 4) : OOB;
+    const uint32_t sa_voff =
+        tid < KB_PER_ST * BM ? (uint32_t)(((tid % BM) * ldsa + tid / BM) * 4) : OOB;
     const uint32_t sb_voff = tid < 2 ? (uint32_t)(tid * ldsb * 4) : OOB;
     // every lane stores both values (zeros past the extent) to its own slot,
     // so the stores need no branch: sA slot kb*64 + row, sB slot 256 + kb
@@ -149,7 +158,12 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(
 #pragma unroll
         for (int j = 0; j < A_LD; ++j)
             ar[j] = buf_load16(ra, a_voff[j]);
-        br = buf_load16(rb, b_voff);
+        if constexpr (HALF) {
+            const u32x2 h = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rb, (int)b_voff, 0, 0));
+            br = u32x4{h[0], h[1], h[0], h[1]};
+        } else {
+            br = buf_load16(rb, b_voff);
+        }
         sa = buf_load_f32(rsa, sa_voff);
         sb = buf_load_f32(rsb, sb_voff);
     };
@@ -175,7 +189,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(
                     if (((c & 15) ^ ((c >> 4) & 7)) >= 8 * qv)
                         areg[p][j] = u32x4{0u, 0u, 0u, 0u};
                 }
-                if ((tid >> 6) >= qv)
+                if (tid / BM >= qv)
                     sareg[p] = 0.f;
             }
 #pragma unroll
@@ -225,7 +239,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = m0 + 16 * wave + 4 * lg + j;
-            if (row < M && col < N)
+            if (row < M && col < N && (!HALF || li < 8))
                 C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc[j]);
         }
     }
@@ -233,19 +247,54 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(
 
 }  // namespace
 
-// One geometry: BM x BN tiles, 6 stages in flight.
+namespace {
+// One launch geometry: RB row blocks, half blocks, PF stages in flight.
+struct Cfg {
+    int rb;
+    bool half;
+    int pf;
+};
+constexpr Cfg kCfg[] = {
+    /* 0 */ {4, false, 6},   // 64 x 16
+    /* 1 */ {1, true, 6},    // 16 x 8
+    /* 2 */ {2, true, 6},    // 32 x 8
+    /* 3 */ {4, true, 6},    // 64 x 8
+};
+
+template <int I>
+hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
+{
+    constexpr Cfg c = kCfg[I];
+    const int m_tiles = (int)ceil_div(a.M, 16 * c.rb);
+    gemm_fp8_kernel<c.pf, c.rb, c.half><<<dim3((unsigned)g.workgroups), dim3(256), 0, stream>>>(
+        a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
+        (const uint8_t*)a.B, a.ldb, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles);
+    return hipGetLastError();
+}
+}  // namespace
+
+// Launch geometry (tile sharing only; every choice runs the same arithmetic
+// per element): 64 x 16 tiles once they give each compute unit a workgroup;
+// below that, tiles of 16, 32 or 64 rows (as few as hold the call's rows)
+// on half blocks of 8 columns, which doubles the workgroups sharing the
+// weights.
 Geometry geometry_fp8(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
+    const int64_t nb = ceil_div(N, BN);
+    int id = 0;
+    if (ceil_div(M, 64) * nb < 256)
+        id = M <= 16 ? 1 : M <= 32 ? 2 : 3;
+    const Cfg& c = kCfg[id];
     Geometry g;
-    g.id = 0;
-    g.bm = BM;
-    g.bn = BN;
+    g.id = id;
+    g.bm = 16 * c.rb;
+    g.bn = c.half ? 8 : BN;
     g.waves = 4;
-    g.a_rows = BM;
+    g.a_rows = g.bm;
     g.k_stage = BKS;
-    g.stages = 6;
-    g.workgroups = ceil_div(M, BM) * ceil_div(N, BN);
+    g.stages = c.pf;
+    g.workgroups = ceil_div(M, g.bm) * nb * (c.half ? 2 : 1);
     return g;
 }
 
@@ -254,11 +303,13 @@ hipError_t launch_fp8bs(const GemmArgs& a, hipStream_t stream)
     const Geometry g = geometry_fp8(a.M, a.N, a.K);
     if (g.workgroups > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
-    const int m_tiles = (int)ceil_div(a.M, BM);
-    gemm_fp8_kernel<6><<<dim3((unsigned)g.workgroups), dim3(256), 0, stream>>>(
-        a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
-        (const uint8_t*)a.B, a.ldb, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles);
-    return hipGetLastError();
+    switch (g.id) {
+    case 0: return launch_cfg<0>(a, g, stream);
+    case 1: return launch_cfg<1>(a, g, stream);
+    case 2: return launch_cfg<2>(a, g, stream);
+    case 3: return launch_cfg<3>(a, g, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace bigemm

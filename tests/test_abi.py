@@ -339,7 +339,7 @@ def test_geometry_query_covers_the_output(entry):
         if g["a_rows"] < g["bm"]:
             assert M <= g["a_rows"], (M, g)      # only calls that fit the staged rows
         ids.add(g["id"])
-    multi = {"bf16", "bf16_bt", "bf16_packed", "fp8_packed", "fp4_packed", "w4a8_packed"}
+    multi = {"bf16", "bf16_bt", "bf16_packed", "fp8", "fp8_packed", "fp4_packed", "w4a8_packed"}
     assert (len(ids) > 1) == (entry in multi), ids
 
 
