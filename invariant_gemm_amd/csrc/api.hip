@@ -35,7 +35,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // A kernel addresses up to 128 rows of an input from one buffer resource
 // (a tile's A rows, a stage's B rows) with 32-bit offsets below 2^31; row
 // pitches are capped so that such a span always fits.
-bool pitch_ok(int64_t ld, int64_t elem_bytes) { return ld * elem_bytes <= BI_MAX_PITCH_BYTES; }
+bool pitch_ok(int64_t ld, int64_t elem_bytes)
+{
+    return ld <= BI_MAX_PITCH_BYTES / elem_bytes;   // no product, so no overflow for any ld
+}
 
 bi_status check_dims(int64_t M, int64_t N, int64_t K)
 {
@@ -774,8 +777,9 @@ bi_status bi_probe_stream_read(const void* buf, size_t bytes, int workgroups, in
         return BI_ERR_ALIGN;
     if (workgroups < 1 || workgroups > 65536 || (flags & ~3))
         return BI_ERR_UNSUPPORTED;
-    // each workgroup's range is addressed with 32-bit offsets
-    if ((bytes + workgroups - 1) / workgroups + 4096 > 0x7FFFFFFFu)
+    // each workgroup's range is addressed with 32-bit offsets (written so
+    // that no intermediate wraps for any size_t byte count)
+    if (bytes / (size_t)workgroups + 1 > 0x7FFFFFFFu - 4096)
         return BI_ERR_UNSUPPORTED;
     return launched(launch_probe_stream_read((const uint8_t*)buf, bytes, workgroups,
                                              (flags & BI_PROBE_UNROLL8) ? 8 : 4,
