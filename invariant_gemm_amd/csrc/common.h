@@ -114,4 +114,40 @@ __device__ __forceinline__ uint32_t clamp_bytes(int64_t b)
     return b <= 0 ? 0u : (b >= 0x7FFFFFFF ? 0x7FFFFFFFu : (uint32_t)b);
 }
 
+// Row slot -> group of a grouped (mixture-of-experts) call.  Group g owns the
+// rows [offsets[g], offsets[g+1]) -- clamped into [0, M] and made
+// non-decreasing here, so no table can send an access outside the operands --
+// and slot mt enumerates the groups' BM-row tiles in group order.  Returns
+// the group and its tile's first row and row end, or n_groups for a slot past
+// the last tile.  The table is read 64 entries per vector load (one per lane)
+// and walked with lane reads, so a workgroup waits for one load per 63 groups
+// instead of a chain of dependent scalar loads.  Called by every lane of a
+// wave with the same arguments (the result is uniform).
+__device__ __forceinline__ int group_of_slot(const int32_t* __restrict__ offsets, int n_groups, int M,
+                                             int BM, int mt, int& m0, int& row_end)
+{
+    const int lane = threadIdx.x & 63;
+    int first = 0, lo = 0;
+    for (int base = 0; base < n_groups; base += 63) {
+        const int idx = base + lane;
+        const int v = idx <= n_groups ? offsets[idx] : M;
+        const int cnt = n_groups - base < 63 ? n_groups - base : 63;
+        for (int j = 0; j < cnt; ++j) {
+            const int o0 = __builtin_amdgcn_readlane(v, j);
+            const int o1 = __builtin_amdgcn_readlane(v, j + 1);
+            lo = min(max(o0, lo), M);
+            const int hi = min(max(o1, lo), M);
+            const int tiles_g = (hi - lo + BM - 1) / BM;
+            if (mt < first + tiles_g) {
+                m0 = lo + (mt - first) * BM;
+                row_end = hi;
+                return base + j;
+            }
+            first += tiles_g;
+            lo = hi;
+        }
+    }
+    return n_groups;
+}
+
 }  // namespace bigemm

@@ -124,22 +124,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_bf16_packed_kernel(
     int m0 = mt * BM;
     int row_end = M;                                  // rows [m0, row_end) are this tile's
     if constexpr (GROUPED) {
-        // offsets are clamped into [0, M] and made monotone here, so no
-        // table can send a load or store outside A or C
-        int first = 0, g = 0, lo = 0, hi = 0;
-        for (; g < n_groups; ++g) {
-            lo = min(max(offsets[g], lo), M);
-            hi = min(max(offsets[g + 1], lo), M);
-            const int tiles_g = (hi - lo + BM - 1) / BM;
-            if (mt < first + tiles_g)
-                break;
-            first += tiles_g;
-            lo = hi;
-        }
+        const int g = group_of_slot(offsets, n_groups, M, BM, mt, m0, row_end);
         if (g == n_groups)
             return;                                   // an unused slot (uniform per workgroup)
-        m0 = lo + (mt - first) * BM;
-        row_end = hi;
         Bp += g * b_stride;
     }
     const int NB = (N + 15) >> 4;

@@ -98,20 +98,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     int m0 = mt * BM;
     int row_end = M;                                  // rows [m0, row_end) are this tile's
     if constexpr (GROUPED) {
-        int first = 0, g = 0, lo = 0, hi = 0;
-        for (; g < n_groups; ++g) {
-            lo = min(max(offsets[g], lo), M);
-            hi = min(max(offsets[g + 1], lo), M);
-            const int tiles_g = (hi - lo + BM - 1) / BM;
-            if (mt < first + tiles_g)
-                break;
-            first += tiles_g;
-            lo = hi;
-        }
+        const int g = group_of_slot(offsets, n_groups, M, BM, mt, m0, row_end);
         if (g == n_groups)
             return;                                   // an unused slot (uniform per workgroup)
-        m0 = lo + (mt - first) * BM;
-        row_end = hi;
         Bp += g * b_stride;
         sB += g * sb_stride;
     }
@@ -378,13 +367,20 @@ struct Cfg {
 };
 
 // The geometry table.  Every entry runs the same per-element arithmetic.
+// The tiled entries (1-4) run eight waves: the waves that own no output
+// sub-tile only load, so each SIMD holds a loading wave beside a computing
+// one and the loads of the next stage overlap the LDS reads and MFMAs of the
+// current one (measured at K = 7168, N = 2048 against four-wave versions of
+// the same tiles: M = 128 22.8 -> 14 us, M = 256 25.5 -> 18.7 us, M = 512
+// 35 -> 27.5 us).
 constexpr Cfg kCfg[] = {
     /* 0 */ {8, 1, 1, 1, 1, 8, 4, false, 16},   // 16 x 16, eight waves streaming
-    /* 1 */ {8, 4, 1, 1, 1, 4, 4, false, 64},   // 64 x 16, eight waves
-    /* 2 */ {4, 4, 2, 2, 1, 2, 4, false, 64},   // 64 x 32
-    /* 3 */ {4, 4, 4, 2, 2, 2, 2, false, 64},   // 64 x 64
-    /* 4 */ {4, 1, 1, 1, 1, 8, 4, true, 16},    // 16 x 8 half blocks, four waves
-    /* 5 */ {4, 1, 1, 1, 1, 8, 4, true, 8},     //   the same, 8 rows of A staged
+    /* 1 */ {8, 2, 1, 1, 1, 8, 2, false, 32},   // 32 x 16
+    /* 2 */ {8, 2, 2, 1, 1, 4, 2, false, 32},   // 32 x 32
+    /* 3 */ {8, 4, 2, 2, 1, 4, 2, false, 64},   // 64 x 32
+    /* 4 */ {8, 4, 4, 2, 2, 2, 2, false, 64},   // 64 x 64
+    /* 5 */ {4, 1, 1, 1, 1, 8, 4, true, 16},    // 16 x 8 half blocks, four waves
+    /* 6 */ {4, 1, 1, 1, 1, 8, 4, true, 8},     //   the same, 8 rows of A staged
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -452,34 +448,40 @@ hipError_t launch_id(const GemmArgs& a, const GroupArgs* grp, int64_t sb_stride,
     case 3: return launch_cfg<3>(a, grp, sb_stride, g, stream);
     case 4: return launch_cfg<4>(a, grp, sb_stride, g, stream);
     case 5: return launch_cfg<5>(a, grp, sb_stride, g, stream);
+    case 6: return launch_cfg<6>(a, grp, sb_stride, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 6, "every table entry needs its case in launch_id");
+static_assert(kNumCfg == 7, "every table entry needs its case in launch_id");
 
 }  // namespace
 
 // Launch geometry (tile sharing only: every geometry runs the same
-// per-element arithmetic).  64 x 64 tiles once they still give each compute
-// unit a workgroup, 64 x 32 above 128 rows, 64 x 16 (eight waves) from 17
-// rows, and for M <= 16 one 16 x 16 block per workgroup with eight waves
-// streaming its weights -- or, while N/16 blocks would leave compute units
-// without a workgroup, half a block (8 columns, four waves) per workgroup,
-// staging only the first 8 rows of A for calls of at most 8 rows (M = 1:
-// 9.4 -> 8.9 us at K = 7168, N = 2048; staging 4 measured slower).
+// per-element arithmetic).  For M <= 16 one 16 x 16 block per workgroup with
+// eight waves streaming its weights -- or, while N/16 blocks would leave
+// compute units without a workgroup, half a block (8 columns, four waves) per
+// workgroup, staging only the first 8 rows of A for calls of at most 8 rows
+// (M = 1: 9.4 -> 8.9 us at K = 7168, N = 2048; staging 4 measured slower).
+// Above 16 rows: the smallest tile (16 x 16, 32 x 16, 32 x 32, 64 x 32,
+// 64 x 64) whose grid still fits on the compute units in one round, else the
+// largest.  A second, partial round of workgroups costs more than the larger
+// tile's extra rows: at K = 7168, N = 2048, M = 257 runs 33.8 us on 320
+// 64 x 32 tiles and 26.5 us on 160 64 x 64 tiles.
 namespace {
+constexpr int64_t kComputeUnits = 256;
+
 int fp8_family(int64_t M, int64_t N)
 {
     const int64_t nb = ceil_div(N, 16);
-    if (M > 64 && ceil_div(M, 64) * ceil_div(nb, 4) >= 256)
-        return 3;
-    if (M > 128)
-        return 2;
-    if (M > 16)
-        return 1;
-    if (nb < 256)
-        return M <= 8 ? 5 : 4;
-    return 0;
+    if (M <= 16) {
+        if (nb < kComputeUnits)
+            return M <= 8 ? 6 : 5;
+        return 0;
+    }
+    for (int id = 0; id < 4; ++id)
+        if (ceil_div(M, 16 * kCfg[id].rb) * ceil_div(nb, kCfg[id].cb) <= kComputeUnits)
+            return id;
+    return 4;
 }
 }  // namespace
 
@@ -489,17 +491,28 @@ Geometry geometry_fp8_packed(int64_t M, int64_t N, int64_t K)
     return describe(fp8_family(M, N), M, N);
 }
 
-// Grouped calls: the geometry follows the mean rows per group (any choice
-// gives the same bits); the 8-row variant only when the whole call has at
-// most 8 rows (all of them may fall into one group).
+// Grouped calls: the tiles must cover every group's rows, so the grid holds
+// sum over groups of ceil(rows / BM) row slots per column tile (bounded by
+// m_tiles_of).  The same rule as above on that grid: the smallest tile whose
+// workgroups fit on the compute units in one round (half blocks first while
+// the groups average at most 16 rows), else the largest; the 8-row variant
+// only when the whole call has at most 8 rows (all of them may fall into one
+// group).
 Geometry geometry_fp8_grouped(int64_t M, int64_t N, int64_t K, int64_t groups)
 {
     (void)K;
     const int64_t mean = ceil_div(M, groups);
-    int id = fp8_family(mean > 0 ? mean : 1, N);
-    if (id == 5 && M > 8)
-        id = 4;
-    return describe(id, M, N, groups);
+    if (mean <= 16 && ceil_div(N, 16) < kComputeUnits) {
+        const Geometry h = describe(M <= 8 ? 6 : 5, M, N, groups);
+        if (h.workgroups <= kComputeUnits)
+            return h;
+    }
+    for (int id = 0; id < 4; ++id) {
+        const Geometry g = describe(id, M, N, groups);
+        if (g.workgroups <= kComputeUnits)
+            return g;
+    }
+    return describe(4, M, N, groups);
 }
 
 hipError_t launch_fp8_packed(const GemmArgs& a, hipStream_t stream)
