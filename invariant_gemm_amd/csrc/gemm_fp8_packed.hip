@@ -72,11 +72,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     constexpr int A_LD = A_BYTES / (NTHR * 16);
     constexpr int A_LDU = (AR * CPR + NTHR - 1) / NTHR;   // loads that cover rows < AR
     constexpr int B_LD = B_BYTES / (NTHR * 16);
-    constexpr int SA_N = BM * KB_ST;
     constexpr int SB_N = CB * KB_ST;
-    constexpr int SA_LD = (SA_N + NTHR - 1) / NTHR;
-    constexpr int SB_OFF = A_BYTES + B_BYTES + SA_LD * NTHR * 4;
+    constexpr int SB_OFF = A_BYTES + B_BYTES;
     constexpr int STAGE = SB_OFF + NTHR * 4;
+    // Activation scales are staged per chunk of SAC K blocks -- 128 bytes of
+    // each row of sA, one 16-byte load per (row, quarter) -- into an LDS
+    // buffer [SAC][BM] (block-major, so four rows of one block are one
+    // 16-byte read), double-buffered by chunk parity.  A row's scales thus
+    // cost one cache line per 32 K blocks instead of one scattered load per
+    // block and stage.
+    constexpr int SAC = 32;
+    constexpr int SPC = SAC / KB_ST;                  // stages per scale chunk
+    constexpr int CH_N = BM * (SAC / 4);              // 16-byte pieces per chunk
+    constexpr int CH_LD = (CH_N + NTHR - 1) / NTHR;
+    constexpr int SAS_BYTES = SAC * BM * 4;
     constexpr int WGR = RB / WR;                      // compute waves along M
     constexpr int WGC = CB / WC;                      // compute waves along N
     static_assert(A_LD * NTHR * 16 == A_BYTES, "A stage must split evenly over the threads");
@@ -85,7 +94,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     static_assert(SB_N <= NTHR, "one weight scale per thread and stage");
     static_assert(WGR * WR == RB && WGC * WC == CB && WGR * WGC <= WAVES, "wave tiling");
     static_assert(PF % 2 == 0, "the LDS double buffer is indexed by stage parity");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+    static_assert(SAC % KB_ST == 0, "a stage lies in one scale chunk");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE + 2 * SAS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,13 +157,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     // Every load below is issued unconditionally, in the same order in every
     // stage, so the compiler's wait counts keep PF stages in flight (a
     // conditional load would make it assume the shortest history).
-    // sA value v = (K block q, row) -> LDS slot v = q*BM + row
-    uint32_t sa_voff[SA_LD];
+    // scale piece u = (row, quarter): sA[row][kc + 4*quarter .. +3] of the
+    // chunk starting at K block kc
+    uint32_t ch_voff[CH_LD];
 #pragma unroll
-    for (int j = 0; j < SA_LD; ++j) {
-        const int v = j * NTHR + tid;
-        const int q = v / BM, row = v % BM;
-        sa_voff[j] = v < SA_N ? (uint32_t)((row * ldsa + q) * 4) : OOB;
+    for (int j = 0; j < CH_LD; ++j) {
+        const int u = j * NTHR + tid;
+        ch_voff[j] = u < CH_N ? (uint32_t)(((u >> 3) * ldsa + 4 * (u & 7)) * 4) : OOB;
     }
     // sB value t = (column block c, K block q) -> LDS slot t = c*KB_ST + q
     uint32_t sb_voff;
@@ -170,7 +180,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
 
     u32x4 areg[PF][A_LD];
     u32x4 breg[PF][B_LD];
-    float sareg[PF][SA_LD];
+    u32x4 sacreg[PF][CH_LD];
     float sbreg[PF];
     f32x4 acc[WR][WC];
 #pragma unroll
@@ -179,7 +189,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
         for (int c = 0; c < WC; ++c)
             acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto issue = [&](int s, u32x4 (&ar)[A_LD], u32x4 (&br)[B_LD], float (&sar)[SA_LD], float& sbr) {
+    // The scale-chunk loads are issued in every stage (on an empty extent
+    // except at a chunk's first stage), so every stage issues the same loads
+    // in the same order.  A load whose extent ends inside it returns zero for
+    // the dwords past the end only.
+    auto issue = [&](int s, u32x4 (&ar)[A_LD], u32x4 (&br)[B_LD], u32x4 (&sac)[CH_LD], float& sbr) {
         const bool live = s < nst;
         const int kb0 = s * KB_ST;
         const int kst = kb0 * KBK;
@@ -188,7 +202,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
             live ? clamp_bytes((int64_t)(rows_valid - 1) * lda + K - kst) : 0u);
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
             sA + (int64_t)m0 * ldsa + kb0,
-            live ? clamp_bytes(((int64_t)(rows_valid - 1) * ldsa + nkb - kb0) * 4) : 0u);
+            live && s % SPC == 0 ? clamp_bytes(((int64_t)(rows_valid - 1) * ldsa + nkb - kb0) * 4) : 0u);
         const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
             sB + (int64_t)kb0 * ldsb,
             live ? clamp_bytes(((int64_t)(nkb - 1 - kb0) * ldsb + ncb) * 4) : 0u);
@@ -204,15 +218,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
             br[j] = buf_load16_nt(rb, b_voff[j]);
         }
 #pragma unroll
-        for (int j = 0; j < SA_LD; ++j)
-            sar[j] = __builtin_bit_cast(float,
-                                        __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)sa_voff[j], 0, 0));
+        for (int j = 0; j < CH_LD; ++j)
+            sac[j] = buf_load16(rsa, ch_voff[j]);
         sbr = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsb, (int)sb_voff, 0, 0));
     };
 
 #pragma unroll
     for (int p = 0; p < PF; ++p)
-        issue(p, areg[p], breg[p], sareg[p], sbreg[p]);
+        issue(p, areg[p], breg[p], sacreg[p], sbreg[p]);
 
     const int nst_pad = (nst + PF - 1) / PF * PF;
     for (int s0 = 0; s0 < nst_pad; s0 += PF) {
@@ -223,8 +236,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
             if ((s + 1) * KB_ST > nkb) {
                 // K tail: the stage's blocks at kb >= K/128 must contribute
                 // exactly zero.  B and sB read as zero there (outside their
-                // buffer extents); A and sA may hold anything in their row
-                // pitch, so they are cleared here.
+                // buffer extents); A may hold anything in its row pitch, so
+                // it is cleared here (and sA where its chunk is written).
                 const int qv = nkb - s * KB_ST;              // valid blocks of this stage
 #pragma unroll
                 for (int j = 0; j < A_LDU; ++j) {
@@ -233,10 +246,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
                     if (cg >= 8 * qv)
                         areg[p][j] = u32x4{0u, 0u, 0u, 0u};
                 }
-#pragma unroll
-                for (int j = 0; j < SA_LD; ++j)
-                    if ((j * NTHR + tid) / BM >= qv)
-                        sareg[p][j] = 0.f;
             }
 #pragma unroll
             for (int j = 0; j < A_LDU; ++j)
@@ -244,11 +253,29 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
 #pragma unroll
             for (int j = 0; j < B_LD; ++j)
                 *reinterpret_cast<u32x4*>(buf + A_BYTES + (j * NTHR + tid) * 16) = breg[p][j];
-#pragma unroll
-            for (int j = 0; j < SA_LD; ++j)
-                *reinterpret_cast<float*>(buf + A_BYTES + B_BYTES + (j * NTHR + tid) * 4) = sareg[p][j];
             *reinterpret_cast<float*>(buf + SB_OFF + tid * 4) = sbreg[p];
-            issue(s + PF, areg[p], breg[p], sareg[p], sbreg[p]);
+            float* sas = reinterpret_cast<float*>(smem + 2 * STAGE + ((s / SPC) & 1) * SAS_BYTES);
+            if (s % SPC == 0 && s < nst) {
+                // a new scale chunk: blocks past K/128 (which may hold
+                // anything from the row pitch) are written as zero
+                const int kc = s * KB_ST;
+#pragma unroll
+                for (int j = 0; j < CH_LD; ++j) {
+                    const int u = j * NTHR + tid;
+                    if (u < CH_N) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            // the element is read as a value first: a bit
+                            // cast of the vector element itself compiles to
+                            // element 0 for every e
+                            const uint32_t w = sacreg[p][j][e];
+                            const int q = 4 * (u & 7) + e;
+                            sas[q * BM + (u >> 3)] = kc + q < nkb ? __builtin_bit_cast(float, w) : 0.f;
+                        }
+                    }
+                }
+            }
+            issue(s + PF, areg[p], breg[p], sacreg[p], sbreg[p]);
             __syncthreads();
             if (computes) {
                 // Two phases per stage.  (1) every block product P of the
@@ -296,10 +323,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
 #pragma unroll
                     for (int c = 0; c < WC; ++c)
                         sb[c] = *reinterpret_cast<const float*>(buf + SB_OFF + ((wc0 + c) * KB_ST + q) * 4);
+                    const int qc = (s % SPC) * KB_ST + q;      // block within the scale chunk
 #pragma unroll
                     for (int r = 0; r < WR; ++r) {
                         const f32x4 sa4 = *reinterpret_cast<const f32x4*>(
-                            buf + A_BYTES + B_BYTES + (q * BM + 16 * (wr0 + r) + 4 * lg) * 4);
+                            sas + qc * BM + 16 * (wr0 + r) + 4 * lg);
 #pragma unroll
                         for (int c = 0; c < WC; ++c)
 #pragma unroll
