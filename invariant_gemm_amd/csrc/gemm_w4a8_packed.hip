@@ -325,6 +325,7 @@ constexpr Cfg kCfg[] = {
     /* 1 */ {4, 1, 4, 1, 1, 4, 4, true, 8},     //   the same, 8 rows of A staged
     /* 2 */ {4, 4, 4, 2, 2, 2, 2, true, 64},    // 64 x 64, two K blocks per stage
     /* 3 */ {4, 4, 4, 2, 2, 1, 4, false, 64},   // 64 x 64, one K block per stage, weights shared
+    /* 4 */ {8, 4, 4, 2, 2, 4, 2, true, 64},    // 64 x 64, eight waves (four only load), four K blocks per stage
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -365,18 +366,21 @@ hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
 // staged activation tile (of which only the first 8 rows are loaded when the
 // call has no more: LDS rows past them keep stale bytes, which reach only
 // output rows that are never stored, an MFMA output row depending on its own
-// A row alone); 64 x 64 tiles above that, with one K block per stage once
-// M > 128.
+// A row alone); 64 x 64 tiles above that: while they fit on the compute
+// units in one round, eight waves of which four only load, four K blocks per
+// stage (M = 17 16.0 -> 13.6 us, M = 64 16.1 -> 14.7 us); past one round
+// four waves, with one K block per stage once M > 128 (the eight-wave
+// version measured 20-30 % slower there).
 Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
     int id;
-    if (M > 128)
-        id = 3;
-    else if (M > 16)
-        id = 2;
-    else
+    if (M <= 16)
         id = M <= 8 ? 1 : 0;
+    else if (ceil_div(M, 64) * ceil_div(ceil_div(N, 16), 4) <= 256)
+        id = 4;
+    else
+        id = M > 128 ? 3 : 2;
     return describe(id, M, N);
 }
 
@@ -388,10 +392,11 @@ hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream)
     case 1: return launch_cfg<1>(a, g, stream);
     case 2: return launch_cfg<2>(a, g, stream);
     case 3: return launch_cfg<3>(a, g, stream);
+    case 4: return launch_cfg<4>(a, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 4, "every table entry needs its case in launch_w4a8_packed");
+static_assert(kNumCfg == 5, "every table entry needs its case in launch_w4a8_packed");
 
 hipError_t launch_pack_mxfp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sE,
                              int64_t ldse, uint8_t* Bp, hipStream_t stream)
