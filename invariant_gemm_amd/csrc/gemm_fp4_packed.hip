@@ -316,8 +316,9 @@ struct Cfg {
 // The geometry table.  Every entry runs the same per-element arithmetic.
 constexpr Cfg kCfg[] = {
     /* 0 */ {2, 1, 1, 2, 4, true, 16},    // 16 x 32 streaming, two waves
-    /* 1 */ {4, 1, 4, 1, 4, true, 64},    // 64 x 64
+    /* 1 */ {4, 1, 4, 2, 2, true, 64},    // 64 x 64
     /* 2 */ {4, 2, 4, 1, 2, false, 64},   // 64 x 128, weights shared by row tiles
+    /* 3 */ {4, 1, 1, 4, 2, true, 16},    // 16 x 64 streaming, four waves, 512 K per stage
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -353,19 +354,25 @@ hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
 
 // Launch geometry (tile sharing only: the per-element arithmetic is the same
 // for all): 64 x 128 tiles once they still give each compute unit a
-// workgroup, 64 x 64 from 17 rows, else two waves of 16 x 16 streaming.  All
-// 16 rows of each A stage are staged even for a single row: with the MFMA
-// results kept in VGPRs, staging only the first 8 measured slower (K = 4096,
-// N = 14336, M = 1: 11.2 vs 10.7 us).
+// workgroup; below that, for wide weights (N/16 >= 256), 16-row tiles of 64
+// columns on four waves with 512 K per stage up to 64 rows -- even when
+// their grid takes several rounds they beat 64 x 64 tiles there (K = 4096,
+// N = 14336: M = 1 11.1 -> 9.5 us, M = 17..32 30 -> 14.5 us, M = 64 31 ->
+// 24.9 us) -- and 64 x 64 above; for narrow weights two waves of 16 x 16
+// streaming up to 16 rows, 64 x 64 above.  All 16 rows of each A stage are
+// staged even for a single row: with the MFMA results kept in VGPRs, staging
+// only the first 8 measured slower (M = 1: 11.2 vs 10.7 us).
 Geometry geometry_fp4_packed(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
     const int64_t nb = ceil_div(N, 16);
-    int id = 0;
+    int id;
     if (M >= 64 && ceil_div(M, 64) * ceil_div(nb, 8) >= 256)
         id = 2;
-    else if (M > 16)
-        id = 1;
+    else if (nb >= 256)
+        id = M <= 64 ? 3 : 1;
+    else
+        id = M <= 16 ? 0 : 1;
     return describe(id, M, N);
 }
 
@@ -376,10 +383,11 @@ hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream)
     case 0: return launch_cfg<0>(a, g, stream);
     case 1: return launch_cfg<1>(a, g, stream);
     case 2: return launch_cfg<2>(a, g, stream);
+    case 3: return launch_cfg<3>(a, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 3, "every table entry needs its case in launch_fp4w_packed");
+static_assert(kNumCfg == 4, "every table entry needs its case in launch_fp4w_packed");
 
 hipError_t launch_pack_fp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sB,
                            int64_t ldsb, uint8_t* Bp, hipStream_t stream)
