@@ -326,6 +326,7 @@ constexpr Cfg kCfg[] = {
     /* 2 */ {4, 4, 4, 2, 2, 2, 2, true, 64},    // 64 x 64, two K blocks per stage
     /* 3 */ {4, 4, 4, 2, 2, 1, 4, false, 64},   // 64 x 64, one K block per stage, weights shared
     /* 4 */ {8, 4, 4, 2, 2, 4, 2, true, 64},    // 64 x 64, eight waves (four only load), four K blocks per stage
+    /* 5 */ {4, 2, 4, 1, 2, 4, 2, true, 32},    // 32 x 64, four waves of 16 x 32, four K blocks per stage
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -366,18 +367,22 @@ hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
 // staged activation tile (of which only the first 8 rows are loaded when the
 // call has no more: LDS rows past them keep stale bytes, which reach only
 // output rows that are never stored, an MFMA output row depending on its own
-// A row alone); 64 x 64 tiles above that: while they fit on the compute
-// units in one round, eight waves of which four only load, four K blocks per
-// stage (M = 17 16.0 -> 13.6 us, M = 64 16.1 -> 14.7 us); past one round
-// four waves, with one K block per stage once M > 128 (the eight-wave
-// version measured 20-30 % slower there).
+// A row alone).  Up to 32 rows, 32 x 64 tiles on four waves while they fit
+// on the compute units in one round (M = 17 16.0 -> 11.0 us, M = 32 16.2 ->
+// 11.2 us); above that 64 x 64 tiles: while they fit in one round, eight
+// waves of which four only load, four K blocks per stage (M = 64 16.1 ->
+// 14.7 us); past one round four waves, with one K block per stage once
+// M > 128 (the eight-wave version measured 20-30 % slower there).
 Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
+    const int64_t col_tiles = ceil_div(ceil_div(N, 16), 4);
     int id;
     if (M <= 16)
         id = M <= 8 ? 1 : 0;
-    else if (ceil_div(M, 64) * ceil_div(ceil_div(N, 16), 4) <= 256)
+    else if (M <= 32 && ceil_div(M, 32) * col_tiles <= 256)
+        id = 5;
+    else if (ceil_div(M, 64) * col_tiles <= 256)
         id = 4;
     else
         id = M > 128 ? 3 : 2;
@@ -393,10 +398,11 @@ hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream)
     case 2: return launch_cfg<2>(a, g, stream);
     case 3: return launch_cfg<3>(a, g, stream);
     case 4: return launch_cfg<4>(a, g, stream);
+    case 5: return launch_cfg<5>(a, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 5, "every table entry needs its case in launch_w4a8_packed");
+static_assert(kNumCfg == 6, "every table entry needs its case in launch_w4a8_packed");
 
 hipError_t launch_pack_mxfp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sE,
                              int64_t ldse, uint8_t* Bp, hipStream_t stream)
