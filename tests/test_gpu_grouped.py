@@ -154,3 +154,27 @@ def test_empty_batch(bg, moe):
     Ah, Bh, A, Bp, ref = moe
     C = run(bg, A[:0], [0] * (len(Bh) + 1), Bp)
     assert C.shape[0] == 0
+
+
+@pytest.mark.parametrize("G", [63, 64, 127, 200])
+def test_many_groups(bg, G):
+    # more groups than one 63-entry chunk of the offsets lookup: tokens spread
+    # over G experts with many empty ones; each expert's rows equal its
+    # ungrouped packed GEMM bit for bit, and the batch matches the oracle
+    K, N, T = 256, 64, 300
+    Ah = inputs.normal_bf16((T, K), 1.0, 1301 + G)
+    Bh = [inputs.normal_bf16((K, N), 0.02, 1400 + g) for g in range(G)]
+    Bd = [dev_bf16(b) for b in Bh]
+    Bp = bg.pack_b_bf16_grouped(Bd)
+    expert = inputs.route_tokens(T, G, 1350 + G, 1.0)
+    order, offsets = inputs.group_by_expert(expert, G)
+    A = dev_bf16(np.ascontiguousarray(Ah[order]))
+    got = host_codes(run(bg, A, offsets, Bp))
+    C64, S = oracle.gemm_bf16_grouped(np.ascontiguousarray(Ah[order]), offsets, Bh)
+    check_parity(got, C64, S, K, f"grouped, {G} groups")
+    assert int(np.count_nonzero(np.diff(offsets) == 0)) > 0      # some experts get no token
+    for g in range(G):
+        lo, hi = offsets[g], offsets[g + 1]
+        if hi > lo:
+            ref = host_codes(bg.gemm_bf16_packed(A[lo:hi], bg.pack_b_bf16(Bd[g])))
+            assert np.array_equal(got[lo:hi], ref), f"group {g} of {G}"

@@ -161,3 +161,27 @@ def test_empty_batch(bg, moe):
     qA, sA, qBs, sBs, A, sAd, Bp, sB, ref = moe
     C = run(bg, A[:0], sAd[:0], [0] * (len(qBs) + 1), Bp, sB)
     assert C.shape[0] == 0
+
+
+@pytest.mark.parametrize("G", [63, 64, 130])
+def test_many_groups(bg, G):
+    # more groups than one 63-entry chunk of the offsets lookup (many of them
+    # empty): each expert's rows equal its ungrouped GEMM bit for bit, and the
+    # batch matches the grouped oracle
+    K, N, T = 256, 128, 200
+    qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((T, K), 1.0, 2601 + G))
+    qBs, sBs = experts(G, K, N, 2700)
+    Bd, Bp, sB = upload(bg, qBs, sBs)
+    expert = inputs.route_tokens(T, G, 2650 + G, 1.0)
+    order, offsets = inputs.group_by_expert(expert, G)
+    qAo, sAo = np.ascontiguousarray(qA[order]), np.ascontiguousarray(sA[order])
+    A, sAd = dev_u8(qAo), dev_f32(sAo)
+    got = host_codes(run(bg, A, sAd, offsets, Bp, sB))
+    C64, S = oracle.gemm_fp8bs_grouped(qAo, sAo, offsets, qBs, sBs)
+    check_parity(got, C64, S, K, f"grouped fp8, {G} groups")
+    assert int(np.count_nonzero(np.diff(offsets) == 0)) > 0
+    for g in range(G):
+        lo, hi = offsets[g], offsets[g + 1]
+        if hi > lo:
+            ref = host_codes(bg.gemm_fp8_blockscaled(A[lo:hi], sAd[lo:hi], Bd[g], dev_f32(sBs[g])))
+            assert np.array_equal(got[lo:hi], ref), f"group {g} of {G}"
