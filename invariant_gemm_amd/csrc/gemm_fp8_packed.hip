@@ -188,6 +188,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
 #pragma unroll
         for (int c = 0; c < WC; ++c)
             acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The block product and scale product of the last block formed but not
+    // yet accumulated (zero before the first block: fma(+0, +0, acc) leaves
+    // every nonzero acc unchanged, and a -0 acc turns +0, which the epilogue
+    // writes as +0 anyway).  Accumulating block q-1 after issuing block q's
+    // MFMAs lets those MFMAs run while the scale FMAs wait for the previous
+    // products; the FMAs of one element still run in block order.
+    f32x4 Pc[WR][WC], Sc[WR][WC];
+#pragma unroll
+    for (int r = 0; r < WR; ++r)
+#pragma unroll
+        for (int c = 0; c < WC; ++c) {
+            Pc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            Sc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 
     // The scale-chunk loads are issued in every stage (on an empty extent
     // except at a chunk's first stage), so every stage issues the same loads
@@ -278,15 +292,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
             issue(s + PF, areg[p], breg[p], sacreg[p], sbreg[p]);
             __syncthreads();
             if (computes) {
-                // Two phases per stage.  (1) every block product P of the
-                // stage, each into its own registers, so that the LDS reads
-                // and MFMAs of different blocks overlap; (2) the ordered
-                // accumulation acc = fma(P, sA*sB, acc), blocks ascending.
-                // No per-block guard: blocks past K are all-zero (tail
-                // clearing above) and fma(+0, +0, acc) == acc for every
-                // nonzero acc; a -0 acc turns +0, which the epilogue writes
-                // as +0 anyway (gemm_out_bf16), so the bits are the same.
-                f32x4 P[KB_ST][WR][WC];
+                // Per block q of the stage: its products P (one MFMA per
+                // sub-block, into a zero accumulator), then the accumulation
+                // of the block before it, acc = fma(P, sA*sB, acc).  No
+                // per-block guard: blocks past K are all-zero (tail clearing
+                // above, zero scales past K/128).
 #pragma unroll
                 for (int q = 0; q < KB_ST; ++q) {
                     i32x8 bv[WC];
@@ -300,6 +310,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
                         bv[c] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
                                       (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
                     }
+                    f32x4 P[WR][WC];
 #pragma unroll
                     for (int r = 0; r < WR; ++r) {
                         const int row = 16 * (wr0 + r) + li;
@@ -313,12 +324,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
 #pragma unroll
                         for (int c = 0; c < WC; ++c)
                             // fp8 e4m3 x fp8 e4m3, unit E8M0 block scales (127 = 2^0)
-                            P[q][r][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            P[r][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 av, bv[c], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
                     }
-                }
 #pragma unroll
-                for (int q = 0; q < KB_ST; ++q) {
+                    for (int r = 0; r < WR; ++r)
+#pragma unroll
+                        for (int c = 0; c < WC; ++c)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                acc[r][c][j] = __builtin_fmaf(Pc[r][c][j], Sc[r][c][j], acc[r][c][j]);
                     float sb[WC];
 #pragma unroll
                     for (int c = 0; c < WC; ++c)
@@ -329,15 +344,25 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
                         const f32x4 sa4 = *reinterpret_cast<const f32x4*>(
                             sas + qc * BM + 16 * (wr0 + r) + 4 * lg);
 #pragma unroll
-                        for (int c = 0; c < WC; ++c)
+                        for (int c = 0; c < WC; ++c) {
+                            Pc[r][c] = P[r][c];
 #pragma unroll
                             for (int j = 0; j < 4; ++j)
-                                acc[r][c][j] = __builtin_fmaf(P[q][r][c][j], sa4[j] * sb[c], acc[r][c][j]);
+                                Sc[r][c][j] = sa4[j] * sb[c];
+                        }
                     }
                 }
             }
         }
     }
+    // the last block
+#pragma unroll
+    for (int r = 0; r < WR; ++r)
+#pragma unroll
+        for (int c = 0; c < WC; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[r][c][j] = __builtin_fmaf(Pc[r][c][j], Sc[r][c][j], acc[r][c][j]);
 
     if (computes) {
 #pragma unroll
@@ -406,7 +431,7 @@ constexpr Cfg kCfg[] = {
     /* 1 */ {8, 2, 1, 1, 1, 8, 2, false, 32},   // 32 x 16
     /* 2 */ {8, 2, 2, 1, 1, 4, 2, false, 32},   // 32 x 32
     /* 3 */ {8, 4, 2, 2, 1, 4, 2, false, 64},   // 64 x 32
-    /* 4 */ {8, 4, 4, 2, 2, 2, 2, false, 64},   // 64 x 64
+    /* 4 */ {8, 4, 4, 2, 2, 4, 2, false, 64},   // 64 x 64
     /* 5 */ {4, 1, 1, 1, 1, 8, 4, true, 16},    // 16 x 8 half blocks, four waves
     /* 6 */ {4, 1, 1, 1, 1, 8, 4, true, 8},     //   the same, 8 rows of A staged
 };
