@@ -166,8 +166,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                 // conversions and MFMAs of the group overlap; (2) the ordered
                 // accumulation acc = fma(P, scale, acc), steps ascending.  No
                 // per-step guard: steps past K have zero A (cleared above),
-                // zero codes and zero scales, and fma(+0, +0, acc) leaves acc
-                // unchanged (acc is never -0).
+                // zero codes and zero scales, and fma(+0, +0, acc) leaves a
+                // nonzero acc unchanged (a -0 acc turns +0, which the
+                // epilogue writes as +0 anyway).
 #pragma unroll
                 for (int q = 0; q < QS; ++q) {
 #pragma unroll

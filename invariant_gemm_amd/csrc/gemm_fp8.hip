@@ -204,7 +204,9 @@ __global__ __launch_bounds__(256) void gemm_fp8_kernel(
                 // (1) the stage's block products, each into its own registers
                 // (their LDS reads and MFMAs overlap), then (2) the ordered
                 // accumulation.  No per-block guard: blocks past K are
-                // all-zero and fma(+0, +0, acc) == acc (acc is never -0).
+                // all-zero and fma(+0, +0, acc) leaves a nonzero acc
+                // unchanged (a -0 acc turns +0, which the epilogue writes as
+                // +0 anyway).
                 f32x4 P[KB_PER_ST];
 #pragma unroll
                 for (int kb = 0; kb < KB_PER_ST; ++kb) {

@@ -137,6 +137,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
 #pragma unroll
         for (int c = 0; c < WC; ++c)
             acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The block product and activation scales of the last block formed but
+    // not yet accumulated (zero before the first block: fma(+0, +0, acc)
+    // leaves every nonzero acc unchanged, and a -0 acc turns +0, which the
+    // epilogue writes as +0 anyway).  Accumulating block q-1 after issuing
+    // block q's MFMAs lets them run while the FMAs wait for the previous
+    // products; the FMAs of one element still run in block order.
+    f32x4 Pc[WR][WC], Sc[WR];
+#pragma unroll
+    for (int r = 0; r < WR; ++r) {
+        Sc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < WC; ++c)
+            Pc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     auto issue = [&](int s, u32x4 (&ar)[A_LD], u32x4 (&br)[B_LD], float (&sar)[SA_LD], uint32_t& scr) {
         const bool live = s < nst;
@@ -211,10 +225,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
             issue(s + PF, areg[p], breg[p], sareg[p], screg[p]);
             __syncthreads();
             if (computes) {
-                // (1) the stage's block products, each into its own
-                // registers; (2) the ordered accumulation.  Blocks past K
-                // are all-zero and fma(+0, +0, acc) == acc (acc is never -0).
-                f32x4 P[KB_ST][WR][WC];
+                // Per block q of the stage: its products P (one scaled MFMA
+                // per sub-block, into a zero accumulator), then the
+                // accumulation of the block before it, acc = fma(P, sA, acc).
+                // Blocks past K are all-zero.
 #pragma unroll
                 for (int q = 0; q < KB_ST; ++q) {
                     i32x8 bv[WC];
@@ -227,6 +241,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
                         bv[c] = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], 0, 0, 0, 0};
                         bsc[c] = buf[SC_OFF + t * STILE + lane];
                     }
+                    f32x4 P[WR][WC];
 #pragma unroll
                     for (int r = 0; r < WR; ++r) {
                         // A lane group g: K = 16g.. (16-byte chunk 8q+g of
@@ -243,25 +258,36 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
                         for (int c = 0; c < WC; ++c)
                             // A fp8 e4m3 (format 0) with unit scale (E8M0 127);
                             // B fp4 e2m1 (format 4) with the lane's MX block scale
-                            P[q][r][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            P[r][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                                 av, bv[c], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, bsc[c]);
                     }
-                }
 #pragma unroll
-                for (int q = 0; q < KB_ST; ++q)
-#pragma unroll
-                    for (int r = 0; r < WR; ++r) {
-                        const f32x4 sa4 = *reinterpret_cast<const f32x4*>(
-                            buf + A_BYTES + B_BYTES + (q * BM + 16 * (wr0 + r) + 4 * lg) * 4);
+                    for (int r = 0; r < WR; ++r)
 #pragma unroll
                         for (int c = 0; c < WC; ++c)
 #pragma unroll
                             for (int j = 0; j < 4; ++j)
-                                acc[r][c][j] = __builtin_fmaf(P[q][r][c][j], sa4[j], acc[r][c][j]);
+                                acc[r][c][j] = __builtin_fmaf(Pc[r][c][j], Sc[r][j], acc[r][c][j]);
+#pragma unroll
+                    for (int r = 0; r < WR; ++r) {
+                        Sc[r] = *reinterpret_cast<const f32x4*>(
+                            buf + A_BYTES + B_BYTES + (q * BM + 16 * (wr0 + r) + 4 * lg) * 4);
+#pragma unroll
+                        for (int c = 0; c < WC; ++c)
+                            Pc[r][c] = P[r][c];
                     }
+                }
             }
         }
     }
+    // the last block
+#pragma unroll
+    for (int r = 0; r < WR; ++r)
+#pragma unroll
+        for (int c = 0; c < WC; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[r][c][j] = __builtin_fmaf(Pc[r][c][j], Sc[r][j], acc[r][c][j]);
 
     if (computes) {
 #pragma unroll
