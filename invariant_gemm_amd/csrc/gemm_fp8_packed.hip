@@ -425,15 +425,17 @@ struct Cfg {
 // one and the loads of the next stage overlap the LDS reads and MFMAs of the
 // current one (measured at K = 7168, N = 2048 against four-wave versions of
 // the same tiles: M = 128 22.8 -> 14 us, M = 256 25.5 -> 18.7 us, M = 512
-// 35 -> 27.5 us).
+// 35 -> 27.5 us).  The half-block entries take 16 K blocks per stage with two
+// stages in flight (against 8 blocks and four stages: M = 1 8.8 -> 8.4 us,
+// M = 4 9.2 -> 8.8 us, M = 16 10.2 -> 10.0 us).
 constexpr Cfg kCfg[] = {
     /* 0 */ {8, 1, 1, 1, 1, 8, 4, false, 16},   // 16 x 16, eight waves streaming
     /* 1 */ {8, 2, 1, 1, 1, 8, 2, false, 32},   // 32 x 16
     /* 2 */ {8, 2, 2, 1, 1, 4, 2, false, 32},   // 32 x 32
     /* 3 */ {8, 4, 2, 2, 1, 4, 2, false, 64},   // 64 x 32
     /* 4 */ {8, 4, 4, 2, 2, 4, 2, false, 64},   // 64 x 64
-    /* 5 */ {4, 1, 1, 1, 1, 8, 4, true, 16},    // 16 x 8 half blocks, four waves
-    /* 6 */ {4, 1, 1, 1, 1, 8, 4, true, 8},     //   the same, 8 rows of A staged
+    /* 5 */ {4, 1, 1, 1, 1, 16, 2, true, 16},   // 16 x 8 half blocks, four waves
+    /* 6 */ {4, 1, 1, 1, 1, 16, 2, true, 8},    //   the same, 8 rows of A staged
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
