@@ -353,6 +353,7 @@ constexpr Cfg kCfg[] = {
     /* 3 */ {4, 4, 4, 2, 2, 1, 4, false, 64},   // 64 x 64, one K block per stage, weights shared
     /* 4 */ {8, 4, 4, 2, 2, 4, 2, true, 64},    // 64 x 64, eight waves (four only load), four K blocks per stage
     /* 5 */ {4, 2, 4, 1, 2, 4, 2, true, 32},    // 32 x 64, four waves of 16 x 32, four K blocks per stage
+    /* 6 */ {4, 4, 8, 2, 4, 1, 2, false, 64},   // 64 x 128, four waves of 32 x 64, weights shared
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -398,7 +399,11 @@ hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
 // 11.2 us); above that 64 x 64 tiles: while they fit in one round, eight
 // waves of which four only load, four K blocks per stage (M = 64 16.1 ->
 // 14.7 us); past one round four waves, with one K block per stage once
-// M > 128 (the eight-wave version measured 20-30 % slower there).
+// M > 128 (the eight-wave version measured 20-30 % slower there); above 192
+// rows, while they still give every compute unit a workgroup, 64 x 128
+// tiles of four 32 x 64 waves, which halve the activation rows each
+// compute unit re-reads (M = 256 40.8 -> 32.5 us, M = 384 56.5 -> 50.5 us,
+// M = 512 65.4 -> 61 us).
 Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
@@ -410,6 +415,8 @@ Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K)
         id = 5;
     else if (ceil_div(M, 64) * col_tiles <= 256)
         id = 4;
+    else if (M > 192 && ceil_div(M, 64) * ceil_div(ceil_div(N, 16), 8) >= 256)
+        id = 6;
     else
         id = M > 128 ? 3 : 2;
     return describe(id, M, N);
@@ -425,10 +432,11 @@ hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream)
     case 3: return launch_cfg<3>(a, g, stream);
     case 4: return launch_cfg<4>(a, g, stream);
     case 5: return launch_cfg<5>(a, g, stream);
+    case 6: return launch_cfg<6>(a, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 6, "every table entry needs its case in launch_w4a8_packed");
+static_assert(kNumCfg == 7, "every table entry needs its case in launch_w4a8_packed");
 
 hipError_t launch_pack_mxfp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sE,
                              int64_t ldse, uint8_t* Bp, hipStream_t stream)

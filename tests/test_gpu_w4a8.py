@@ -104,7 +104,7 @@ def test_parity_random(bg, M, N, K):
 def test_k_tail_ignores_pitch_padding(bg):
     # K = 384: a partial last stage at every geometry; NaN codes / scales in
     # A's and sA's row-pitch padding must not reach the result
-    for M, N, K in ((3, 272, 384), (8, 144, 640), (70, 144, 640), (300, 2048, 384)):
+    for M, N, K in ((3, 272, 384), (8, 144, 640), (70, 144, 640), (300, 2048, 384), (300, 8192, 384)):
         qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((M, K), 1.0, 1701 + M))
         Bq, sE = inputs.quant_mxfp4_weights(inputs.normal_f32((K, N), 0.02, 1702 + N))
         Ap = np.full((M, K + 128), 0x7F, np.uint8)
