@@ -771,11 +771,21 @@ def pmc_counters(dirs):
 
 
 def pmc_counters_legs(dirs):
-    """The same per-M counter summary for the runs of `--pmc-probe-legs`."""
+    """The same per-M counter summary for the runs of `--pmc-probe-legs`,
+    with the MFMA work issued (SQ_INSTS_VALU_MFMA_MOPS_* count 512 flops each:
+    bf16 for the fp4 weight-only kernel, whose codes enter the MFMA as bf16;
+    fp8 and f6f4 for the scaled f8f6f4 MFMAs) against 2MNK."""
     import csv
     import glob
     legs = legs_pmc()
     res = _counters_per_m(dirs, [(kern, sweep_ms) for _, kern, _, sweep_ms, _ in legs], csv, glob)
+    mops = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
+    for (_, _, cls, _, _), r in zip(legs, res):
+        for M, row in r["per_m"].items():
+            if any(c in row for c in mops):
+                fl = sum(row.get(c, 0.0) for c in mops) * 512.0
+                row["derived"]["mfma_flops"] = fl
+                row["derived"]["mfma_flops_over_2mnk"] = round(fl / flops(int(M), cls.N, cls.K), 4)
     return {name: r for (name, *_), r in zip(legs, res)}
 
 
