@@ -45,13 +45,15 @@ __device__ __forceinline__ float e4m3_byte_to_f32(uint32_t w, int b)
     }
 }
 
-// WAVES waves; wave w owns column blocks nb0 + w*CB .. +CB-1; RB row blocks.
+// WAVES waves in WGR groups along M: wave w owns column blocks
+// nb0 = nt*WGC*CB + (w % WGC)*CB .. +CB-1 and row blocks (w / WGC)*RB/WGR ..
+// of the tile's RB (one group: every wave all RB row blocks).
 // Stage = QS 128-K groups (4*QS K steps).
 // Only the first AR rows of each A stage are loaded (AR = BM, or fewer when
 // the call has at most AR rows): LDS rows past them keep stale values, which
 // reach only output rows that are never stored -- an MFMA output row depends
 // on its own A row alone.
-template <int WAVES, int CB, int RB, int QS, int PF, bool NT, int AR>
+template <int WAVES, int CB, int RB, int QS, int PF, bool NT, int AR, int WGR>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     int M, int N, int K,
     const uint16_t* __restrict__ A, int64_t lda,
@@ -64,8 +66,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     constexpr int CPR = BKS * 2 / 16;
     constexpr int A_STAGE = BM * BKS * 2;
     constexpr int A_LD = A_STAGE / (NTHR * 16);
+    // WGR groups of waves along M: a wave computes RBW of the tile's row
+    // blocks for its CB column blocks (WGC waves along N)
+    constexpr int WGC = WAVES / WGR;
+    constexpr int RBW = RB / WGR;
+    static_assert(WGC * WGR == WAVES && RBW * WGR == RB, "wave grid");
     // K steps per product group of the small-tile path: 4 or 2 steps
-    constexpr int SG = RB * CB >= 2 ? 2 : 4;
+    constexpr int SG = RBW * CB >= 2 ? 2 : 4;
     constexpr int A_LDU = (AR * CPR + NTHR - 1) / NTHR;   // loads that cover rows < AR
     static_assert(A_LD * NTHR * 16 == A_STAGE, "A stage must split evenly over the threads");
     static_assert(AR >= 1 && AR <= BM, "staged rows must lie in the tile");
@@ -81,7 +88,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     const int m0 = mt * BM;
     const int NB = (N + 15) >> 4;
     const int KQ = (K + 127) / 128;
-    const int nb0 = nt * (WAVES * CB) + wave * CB;
+    const int nb0 = nt * (WGC * CB) + (WGR == 1 ? wave : wave % WGC) * CB;   // first column block of this wave
+    const int wr0 = WGR == 1 ? 0 : (wave / WGC) * RBW;                       // first row block of this wave
     const uint8_t* scales = Bp + (int64_t)NB * KQ * 1024;
 
     const int nst = (K + BKS - 1) / BKS;
@@ -100,9 +108,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     u32x4 areg[PF][A_LD];
     u32x4 qreg[PF][QS][CB];
     uint32_t sreg[PF][QS][CB];
-    f32x4 acc[RB][CB];
+    f32x4 acc[RBW][CB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
+    for (int r = 0; r < RBW; ++r)
 #pragma unroll
         for (int c = 0; c < CB; ++c)
             acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
             for (int j = 0; j < A_LDU; ++j)
                 *reinterpret_cast<u32x4*>(abuf + (j * NTHR + tid) * 16) = areg[p][j];
             __syncthreads();
-            if constexpr (RB * CB <= 2) {
+            if constexpr (RBW * CB <= 2) {
                 // Small tiles.  Per group of SG K steps: (1) the block
                 // products P, each into its own registers, so the LDS reads,
                 // conversions and MFMAs of the group overlap; (2) the ordered
@@ -173,7 +181,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                 for (int q = 0; q < QS; ++q) {
 #pragma unroll
                     for (int t0 = 0; t0 < 4; t0 += SG) {
-                        f32x4 P[SG][RB][CB];
+                        f32x4 P[SG][RBW][CB];
                         float sc[SG][CB];
 #pragma unroll
                         for (int tt = 0; tt < SG; ++tt) {
@@ -188,8 +196,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                                 sc[tt][c] = e4m3_byte_to_f32(sreg[p][q][c], t);
                             }
 #pragma unroll
-                            for (int r = 0; r < RB; ++r) {
-                                const int row = 16 * r + li;
+                            for (int r = 0; r < RBW; ++r) {
+                                const int row = 16 * (wr0 + r) + li;
                                 const u32x4 afrag = *reinterpret_cast<const u32x4*>(
                                     abuf + (row * CPR + ((ks * 4 + lg) ^ swz<CPR>(row))) * 16);
 #pragma unroll
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
 #pragma unroll
                         for (int tt = 0; tt < SG; ++tt)
 #pragma unroll
-                            for (int r = 0; r < RB; ++r)
+                            for (int r = 0; r < RBW; ++r)
 #pragma unroll
                                 for (int c = 0; c < CB; ++c)
 #pragma unroll
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                     }
                 }
             } else {
-                // Large tiles: RB*CB independent products per K step already
+                // Large tiles: RBW*CB independent products per K step already
                 // keep the MFMA unit busy; steps past K are skipped.
 #pragma unroll
                 for (int q = 0; q < QS; ++q) {
@@ -227,8 +235,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
                                 sc[c] = e4m3_byte_to_f32(sreg[p][q][c], t);
                             }
 #pragma unroll
-                            for (int r = 0; r < RB; ++r) {
-                                const int row = 16 * r + li;
+                            for (int r = 0; r < RBW; ++r) {
+                                const int row = 16 * (wr0 + r) + li;
                                 const u32x4 afrag = *reinterpret_cast<const u32x4*>(
                                     abuf + (row * CPR + ((ks * 4 + lg) ^ swz<CPR>(row))) * 16);
 #pragma unroll
@@ -251,10 +259,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     for (int c = 0; c < CB; ++c) {
         const int col = 16 * (nb0 + c) + li;
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
+        for (int r = 0; r < RBW; ++r) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = m0 + 16 * r + 4 * lg + j;
+                const int row = m0 + 16 * (wr0 + r) + 4 * lg + j;
                 if (row < M && col < N)
                     C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc[r][c][j]);
             }
@@ -307,19 +315,21 @@ __global__ void pack_fp4_kernel(int N, int K, const uint8_t* __restrict__ Bq, in
 
 // One launch geometry: WAVES waves of CB column blocks, RB row blocks, QS
 // 128-K groups per stage, PF stages in flight, non-temporal weight loads,
-// AR staged A rows.
+// AR staged A rows, WGR wave groups along M.
 struct Cfg {
     int waves, cb, rb, qs, pf;
     bool nt;
-    int ar;
+    int ar, wgr;
 };
 
 // The geometry table.  Every entry runs the same per-element arithmetic.
 constexpr Cfg kCfg[] = {
-    /* 0 */ {2, 1, 1, 2, 4, true, 16},    // 16 x 32 streaming, two waves
-    /* 1 */ {4, 1, 4, 2, 2, true, 64},    // 64 x 64
-    /* 2 */ {4, 2, 4, 1, 2, false, 64},   // 64 x 128, weights shared by row tiles
-    /* 3 */ {4, 1, 1, 4, 2, true, 16},    // 16 x 64 streaming, four waves, 512 K per stage
+    /* 0 */ {2, 1, 1, 2, 4, true, 16, 1},    // 16 x 32 streaming, two waves
+    /* 1 */ {4, 1, 4, 2, 2, true, 64, 1},    // 64 x 64
+    /* 2 */ {4, 2, 4, 1, 2, false, 64, 1},   // 64 x 128, weights shared by row tiles
+    /* 3 */ {4, 1, 1, 4, 2, true, 16, 1},    // 16 x 64 streaming, four waves, 512 K per stage
+    /* 4 */ {8, 1, 2, 2, 2, true, 32, 2},    // 32 x 64, eight waves of 16 x 16 (two per SIMD)
+    /* 5 */ {8, 1, 4, 2, 2, true, 64, 2},    // 64 x 64, eight waves of 32 x 16
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -329,12 +339,12 @@ Geometry describe(int id, int64_t M, int64_t N)
     Geometry g;
     g.id = id;
     g.bm = 16 * c.rb;
-    g.bn = 16 * c.waves * c.cb;
+    g.bn = 16 * (c.waves / c.wgr) * c.cb;
     g.waves = c.waves;
     g.a_rows = c.ar;
     g.k_stage = c.qs * 128;
     g.stages = c.pf;
-    g.workgroups = ceil_div(ceil_div(N, 16), c.waves * c.cb) * ceil_div(M, 16 * c.rb);
+    g.workgroups = ceil_div(ceil_div(N, 16), (c.waves / c.wgr) * c.cb) * ceil_div(M, 16 * c.rb);
     return g;
 }
 
@@ -345,7 +355,7 @@ hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
     if (g.workgroups <= 0 || g.workgroups > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     const int m_tiles = (int)ceil_div(a.M, 16 * c.rb);
-    gemm_fp4_packed_kernel<c.waves, c.cb, c.rb, c.qs, c.pf, c.nt, c.ar>
+    gemm_fp4_packed_kernel<c.waves, c.cb, c.rb, c.qs, c.pf, c.nt, c.ar, c.wgr>
         <<<dim3((unsigned)g.workgroups), dim3(64 * c.waves), 0, stream>>>(
             a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
     return hipGetLastError();
@@ -356,11 +366,14 @@ hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
 // Launch geometry (tile sharing only: the per-element arithmetic is the same
 // for all): 64 x 128 tiles once they still give each compute unit a
 // workgroup; below that, for wide weights (N/16 >= 256), 16-row tiles of 64
-// columns on four waves with 512 K per stage up to 64 rows -- even when
-// their grid takes several rounds they beat 64 x 64 tiles there (K = 4096,
-// N = 14336: M = 1 11.1 -> 9.5 us, M = 17..32 30 -> 14.5 us, M = 64 31 ->
-// 24.9 us) -- and 64 x 64 above; for narrow weights two waves of 16 x 16
-// streaming up to 16 rows, 64 x 64 above.  All 16 rows of each A stage are
+// columns on four waves with 512 K per stage up to 16 rows (K = 4096,
+// N = 14336: M = 1 11.1 -> 9.5 us), then tiles of 64 columns on eight waves
+// that split the rows two ways, so each SIMD holds two waves: 32 x 64 while
+// the call has at most three 32-row tiles beyond the first 64 rows' worth
+// (M = 17..32 14.5 -> 13.2 us, M = 65..96 35.6 -> 29 us) and 64 x 64
+// otherwise (M = 33..64 20.4..25.2 -> 18.3..19.3 us, M = 97..128 36 ->
+// 35 us); for narrow weights two waves of 16 x 16 streaming up to 16 rows,
+// 64 x 64 above.  All 16 rows of each A stage are
 // staged even for a single row: with the MFMA results kept in VGPRs, staging
 // only the first 8 measured slower (M = 1: 11.2 vs 10.7 us).
 Geometry geometry_fp4_packed(int64_t M, int64_t N, int64_t K)
@@ -371,7 +384,7 @@ Geometry geometry_fp4_packed(int64_t M, int64_t N, int64_t K)
     if (M >= 64 && ceil_div(M, 64) * ceil_div(nb, 8) >= 256)
         id = 2;
     else if (nb >= 256)
-        id = M <= 64 ? 3 : 1;
+        id = M <= 16 ? 3 : (M <= 32 || (M > 64 && M <= 96)) ? 4 : 5;
     else
         id = M <= 16 ? 0 : 1;
     return describe(id, M, N);
@@ -385,10 +398,12 @@ hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream)
     case 1: return launch_cfg<1>(a, g, stream);
     case 2: return launch_cfg<2>(a, g, stream);
     case 3: return launch_cfg<3>(a, g, stream);
+    case 4: return launch_cfg<4>(a, g, stream);
+    case 5: return launch_cfg<5>(a, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 4, "every table entry needs its case in launch_fp4w_packed");
+static_assert(kNumCfg == 6, "every table entry needs its case in launch_fp4w_packed");
 
 hipError_t launch_pack_fp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sB,
                            int64_t ldsb, uint8_t* Bp, hipStream_t stream)
