@@ -46,7 +46,7 @@ def bf16_vals(codes: np.ndarray) -> np.ndarray:
 
 
 def check_parity(C_codes: np.ndarray, C64: np.ndarray, S: np.ndarray, K: int, what: str = ""):
-    """Spec tolerance |err| <= 2^-7 S + 1e-6 and the tight diagnostic bound
+    """Parity tolerance |err| <= 2^-7 S + 1e-6 and the tight diagnostic bound
     |err| <= 2^-8 |C64| + K 2^-23 S + 1e-6, on every element; finite outputs only."""
     got = bf16_vals(C_codes)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"

@@ -1,6 +1,6 @@
 """GPU parity and batch-invariance tests of bi_gemm_bf16 (through the C ABI).
 
-Parity: every element within the benchmark spec's tolerance of the fp64 oracle and
+Parity: every element within |err| <= 2^-7 S + 1e-6 of the fp64 oracle and
 within the tight diagnostic bound; on exact-input closed forms the GPU must
 equal the oracle's correctly rounded result bit for bit.
 Invariance: each row computed alone (M = 1) must be bit-identical to the same
