@@ -436,6 +436,8 @@ constexpr Cfg kCfg[] = {
     /* 4 */ {8, 4, 4, 2, 2, 4, 2, false, 64},   // 64 x 64
     /* 5 */ {4, 1, 1, 1, 1, 16, 2, true, 16},   // 16 x 8 half blocks, four waves
     /* 6 */ {4, 1, 1, 1, 1, 16, 2, true, 8},    //   the same, 8 rows of A staged
+    /* 7 */ {8, 1, 2, 1, 1, 8, 2, false, 16},   // 16 x 32, two computing waves (grouped calls)
+    /* 8 */ {8, 1, 4, 1, 1, 4, 2, false, 16},   // 16 x 64, four computing waves (grouped calls)
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -504,10 +506,12 @@ hipError_t launch_id(const GemmArgs& a, const GroupArgs* grp, int64_t sb_stride,
     case 4: return launch_cfg<4>(a, grp, sb_stride, g, stream);
     case 5: return launch_cfg<5>(a, grp, sb_stride, g, stream);
     case 6: return launch_cfg<6>(a, grp, sb_stride, g, stream);
+    case 7: return launch_cfg<7>(a, grp, sb_stride, g, stream);
+    case 8: return launch_cfg<8>(a, grp, sb_stride, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 7, "every table entry needs its case in launch_id");
+static_assert(kNumCfg == 9, "every table entry needs its case in launch_id");
 
 }  // namespace
 
@@ -552,7 +556,13 @@ Geometry geometry_fp8_packed(int64_t M, int64_t N, int64_t K)
 // workgroups fit on the compute units in one round (half blocks first while
 // the groups average at most 16 rows), else the largest; the 8-row variant
 // only when the whole call has at most 8 rows (all of them may fall into one
-// group).
+// group).  While the groups average at most 8 rows, 16-row tiles of 16, 32
+// or 64 columns come next: the narrowest whose occupied slots -- at least one
+// per group that holds rows, min(groups, M) -- times its column tiles fit in
+// one round (the slots past the occupied ones exit at once).  E = 8, N = 2048,
+// K = 7168, tokens routed uniformly: T = 8 26.6 -> 19.5 us, T = 16 26.6 ->
+// 20.8 us, T = 64 27.1 -> 24.8 us; at 16 rows per group many groups need two
+// 16-row slots and the 64-row tiles stay faster (T = 128 28.7 against 36.5 us).
 Geometry geometry_fp8_grouped(int64_t M, int64_t N, int64_t K, int64_t groups)
 {
     (void)K;
@@ -561,6 +571,12 @@ Geometry geometry_fp8_grouped(int64_t M, int64_t N, int64_t K, int64_t groups)
         const Geometry h = describe(M <= 8 ? 6 : 5, M, N, groups);
         if (h.workgroups <= kComputeUnits)
             return h;
+    }
+    if (mean <= 8) {
+        const int64_t occupied = std::min<int64_t>(groups, M);
+        for (int id : {0, 7, 8})
+            if (occupied * n_tiles_of(kCfg[id], N) <= kComputeUnits)
+                return describe(id, M, N, groups);
     }
     for (int id = 0; id < 4; ++id) {
         const Geometry g = describe(id, M, N, groups);
