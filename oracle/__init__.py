@@ -196,6 +196,27 @@ def gemm_fp8bs_grouped(qA: np.ndarray, sA: np.ndarray, offsets, qBs, sBs):
     return C, S
 
 
+def gemm_w4a8_grouped(qA: np.ndarray, sA: np.ndarray, offsets, Bqs, sEs, N: int):
+    """Grouped (mixture-of-experts) W4A8 GEMM by its definition: rows
+    [offsets[g], offsets[g+1]) of (qA, sA) times expert g's MXFP4 weights
+    (Bqs[g] packed e2m1 [K, N/2], sEs[g] E8M0 [K/32, N]), one plain gemm_w4a8
+    per group.  Returns (C, S) fp64 [M,N]."""
+    qA = _rows(qA, np.uint8, "qA")
+    sA = _rows(sA, np.float32, "sA")
+    offsets = [int(o) for o in offsets]
+    if len(offsets) != len(Bqs) + 1 or len(sEs) != len(Bqs) or offsets[0] != 0 \
+            or offsets[-1] != qA.shape[0] or any(b < a for a, b in zip(offsets, offsets[1:])):
+        raise ValueError("offsets must run from 0 to M, non-decreasing, one more than groups")
+    C = np.zeros((qA.shape[0], N), np.float64)
+    S = np.zeros((qA.shape[0], N), np.float64)
+    for g, (Bq, sE) in enumerate(zip(Bqs, sEs)):
+        lo, hi = offsets[g], offsets[g + 1]
+        if hi > lo:
+            C[lo:hi], S[lo:hi] = gemm_w4a8(np.ascontiguousarray(qA[lo:hi]),
+                                           np.ascontiguousarray(sA[lo:hi]), Bq, sE, N)
+    return C, S
+
+
 def gemm_fp8bs(qA: np.ndarray, sA: np.ndarray, qB: np.ndarray, sB: np.ndarray):
     """qA uint8 e4m3fn [M,K], sA fp32 [M,K/128], qB uint8 e4m3fn [K,N],
     sB fp32 [K/128, ceil(N/128)] -> (C, S) fp64 [M,N]."""

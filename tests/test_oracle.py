@@ -442,6 +442,42 @@ def test_w4a8_vs_dequantised_numpy():
     assert np.allclose(S, np.abs(a) @ np.abs(b), rtol=1e-12, atol=0)
 
 
+def test_grouped_w4a8_exact_vs_fraction():
+    """The grouped W4A8 GEMM is one W4A8 GEMM per group of rows (including an
+    empty group), each value sum_k (e4m3(qa) sA)(e2m1(c) 2^(sE - 127)) with
+    the 1x128 activation scales and the per-32 E8M0 weight scales; checked
+    against exact rational arithmetic on sampled elements."""
+    g = np.random.default_rng(41)
+    M, N, K, E = 6, 132, 256, 3                       # N: a ragged second 128-column block
+    qA = g.integers(0, 256, size=(M, K)).astype(np.uint8)
+    qA[(qA & 0x7F) == 0x7F] = 0x38                    # no NaN codes
+    sA = np.ldexp(1.0, g.integers(-3, 4, size=(M, K // 128))).astype(np.float32) * np.float32(1.25)
+    codes, Bqs, sEs = [], [], []
+    for _ in range(E):
+        c = g.integers(0, 16, size=(K, N)).astype(np.uint8)
+        codes.append(c)
+        Bqs.append((c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8))
+        sEs.append(g.integers(118, 137, size=(K // 32, N)).astype(np.uint8))
+    offsets = [0, 2, 2, 6]                            # group 1 is empty
+    C, S = oracle.gemm_w4a8_grouped(qA, sA, offsets, Bqs, sEs, N)
+    e4 = torch.from_numpy(qA).view(torch.float8_e4m3fn).double().numpy()
+    for e in range(E):
+        for m in range(offsets[e], offsets[e + 1]):
+            for n in (0, 7, 127, 128, 131):
+                terms = [Fraction(float(e4[m, k])) * Fraction(float(sA[m, k // 128])) *
+                         Fraction(E2M1[int(codes[e][k, n])]) * Fraction(2) ** (int(sEs[e][k // 32, n]) - 127)
+                         for k in range(K)]
+                exact = sum(terms)
+                total = sum(abs(t) for t in terms)
+                assert abs(C[m, n] - float(exact)) <= 2.0**-52 * K * float(total)
+                assert abs(S[m, n] - float(total)) <= 2.0**-52 * K * float(total)
+    # each group's rows are exactly its expert's plain W4A8 GEMM
+    C2, _ = oracle.gemm_w4a8(np.ascontiguousarray(qA[2:]), np.ascontiguousarray(sA[2:]), Bqs[2], sEs[2], N)
+    assert np.array_equal(C[2:], C2)
+    with pytest.raises(ValueError):
+        oracle.gemm_w4a8_grouped(qA, sA, [0, 4, 3, 6], Bqs, sEs, N)
+
+
 def test_w4a8_scale_block_indexing():
     # one weight block carries a huge scale: it must show up exactly in
     # columns n and rows k of that block only
