@@ -380,6 +380,55 @@ class MoE8:
             hit * (K * N + 4 * (K // 128) * ((N + 127) // 128))
 
 
+class MoEW4A8:
+    """Grouped (mixture-of-experts) W4A8 GEMM: E = 8 experts, K = 7168,
+    N = 2048, e4m3fn activations with 1x128 scales, OCP MXFP4 expert weights
+    (N(0, 0.02) before quantisation), T tokens routed top-1 uniformly (seeded);
+    packed expert weights rotated over HBM copies."""
+    E, K, N = 8, 7168, 2048
+    SWEEP = [1, 8, 64, 512]
+
+    def __init__(self, torch, bg, inputs):
+        self.torch, self.bg = torch, bg
+        T = max(self.SWEEP)
+        qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((T, self.K), 1.0, 621))
+        self.A = torch.from_numpy(qA).cuda()
+        self.sA = torch.from_numpy(sA).cuda()
+        Bqs, sEs = [], []
+        for e in range(self.E):
+            Bq, sE = inputs.quant_mxfp4_weights(inputs.normal_f32((self.K, self.N), 0.02, 622 + e))
+            Bqs.append(torch.from_numpy(Bq).cuda())
+            sEs.append(torch.from_numpy(sE).cuda())
+        one = bg.pack_b_mxfp4_grouped(Bqs, sEs, self.N)
+        del Bqs, sEs
+        self.nbuf = rotation(one.data.numel())
+        self.Bp = [one] + [bg.PackedWeights(one.dtype, one.K, one.N, one.data.clone())
+                           for _ in range(self.nbuf - 1)]
+        for b in self.Bp:
+            b.groups = self.E
+        self.routes = {}
+        for t in self.SWEEP:
+            expert = inputs.route_tokens(t, self.E, 623 + t, 0.0)
+            order, offsets = inputs.group_by_expert(expert, self.E)
+            perm = torch.as_tensor(order, device="cuda")
+            self.routes[t] = (self.A[:t].index_select(0, perm), self.sA[:t].index_select(0, perm),
+                              torch.as_tensor(offsets, device="cuda"),
+                              int(np.count_nonzero(np.diff(offsets))))
+        self.C = torch.empty((T, self.N), dtype=torch.bfloat16, device="cuda")
+        self.i = 0
+
+    def launch(self, T):
+        j = self.i % self.nbuf
+        self.i += 1
+        A, sA, off, _ = self.routes[T]
+        self.bg.gemm_w4a8_grouped_packed(A, sA, off, self.Bp[j], out=self.C[:T])
+
+    def nbytes(self, T, N, K):
+        hit = self.routes[T][3]
+        w = K * N // 2 + (K // 32) * N
+        return bytes_w4a8(T, N, K) - w + hit * w
+
+
 # ------------------------------------------------------------------ cpu baseline
 
 def cpu_baseline(budget_s=12.0):
@@ -1025,7 +1074,7 @@ def main():
                 "fp8_packed": (C3P, SWEEP_C3, bytes_fp8, "fp8"), "fp4": (C4, SWEEP_C4, bytes_fp4, "bf16"),
                 "fp4_packed": (C4P, SWEEP_C4, bytes_fp4, "bf16"),
                 "w4a8": (W4A8, W4A8.SWEEP, bytes_w4a8, "fp8"), "moe": (MoE, MoE.SWEEP, None, "bf16"),
-                "moe_fp8": (MoE8, MoE8.SWEEP, None, "fp8")}
+                "moe_fp8": (MoE8, MoE8.SWEEP, None, "fp8"), "moe_w4a8": (MoEW4A8, MoEW4A8.SWEEP, None, "fp8")}
         res = {}
         for name in args.legs.split(","):
             cls, Ms, nb, peak = legs[name]
@@ -1169,6 +1218,10 @@ def main():
         out["moe_grouped_fp8_E8_K7168_N2048"] = sweep(torch, moe8, MoE8.SWEEP, moe8.nbytes,
                                                       MFMA_PEAK_TFLOPS["fp8"], args.rounds)
         del moe8
+        moew4 = MoEW4A8(torch, bigemm, inputs)
+        out["moe_grouped_w4a8_E8_K7168_N2048"] = sweep(torch, moew4, MoEW4A8.SWEEP, moew4.nbytes,
+                                                       MFMA_PEAK_TFLOPS["fp8"], args.rounds)
+        del moew4
         out["replay_bf16_K8192_N8192"] = replay(torch, bigemm, inputs)
         out["decode_attention_L4096_Hq64_Hkv8_D128"] = decode_attention(torch, bigemm, args.rounds)
         out["device"] = device_info(torch)

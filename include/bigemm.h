@@ -112,7 +112,8 @@ typedef enum bi_entry {
     BI_ENTRY_FP4 = 6,                 /* bi_gemm_fp4_w                   */
     BI_ENTRY_FP4_PACKED = 7,          /* bi_gemm_fp4_w_packed            */
     BI_ENTRY_W4A8_PACKED = 8,         /* bi_gemm_w4a8_packed             */
-    BI_ENTRY_FP8_GROUPED_PACKED = 9   /* bi_gemm_fp8_blockscaled_grouped_packed */
+    BI_ENTRY_FP8_GROUPED_PACKED = 9,  /* bi_gemm_fp8_blockscaled_grouped_packed */
+    BI_ENTRY_W4A8_GROUPED_PACKED = 10 /* bi_gemm_w4a8_grouped_packed     */
 } bi_entry;
 
 /* The launch geometry an entry point uses for one call: how the output
@@ -381,6 +382,30 @@ bi_status bi_gemm_w4a8_packed(int64_t M, int64_t N, int64_t K,
                               uint16_t* C, int64_t ldc, void* stream);
 
 /*
+ * Grouped GEMM for mixture-of-experts layers in the W4A8 format (fp8
+ * activations x OCP MXFP4 expert weights; MoE experts sit beside FP4/FP8 in
+ * the QbitAI article's list of V4 components): rows of A (and sA) are grouped
+ * by expert, and group g is multiplied by its own packed MXFP4 weights.
+ *   offsets : device int32 [G + 1], as for bi_gemm_bf16_grouped_packed
+ *             (read on the device, clamped into [0, M] and made
+ *             non-decreasing; rows a malformed table leaves uncovered are not
+ *             written)
+ *   A, sA   : as for bi_gemm_w4a8_packed, [M,K] and [M, K/128]
+ *   Bp      : G packed MXFP4 matrices [K,N] (bi_pack_b_mxfp4 layout: codes,
+ *             then their scales), each bi_packed_b_bytes(BI_W4A8, N, K)
+ *             bytes, back to back
+ *   C       : bf16 [M,N], ldc >= N
+ * Each row's arithmetic is exactly that of bi_gemm_w4a8_packed with its
+ * expert's weights, so a token's output is bit-identical whatever the
+ * routing of the other tokens.  Requires K % 128 == 0 and N even.  One kernel
+ * on `stream`.
+ */
+bi_status bi_gemm_w4a8_grouped_packed(int64_t G, const int32_t* offsets, int64_t M,
+                                      int64_t N, int64_t K, const uint8_t* A, int64_t lda,
+                                      const float* sA, int64_t ldsa, const void* Bp,
+                                      size_t bp_bytes, uint16_t* C, int64_t ldc, void* stream);
+
+/*
  * Batch-invariant decode attention, in two kernels with identical results.
  *
  * The pages pair the batch-invariant GEMM with a "dual-kernel" decode
@@ -484,7 +509,7 @@ bi_status bi_decode_attention_bf16_noalloc(int64_t B, int64_t Hq, int64_t Hkv, i
 bi_status bi_schedule_query(bi_dtype dtype, int64_t N, int64_t K, bi_schedule* out);
 
 /* The launch geometry `entry` uses for a call of M x N x K (and `groups`
- * groups for BI_ENTRY_BF16_GROUPED_PACKED; ignored otherwise).  Informational:
+ * groups for the grouped entries; ignored otherwise).  Informational:
  * no geometry changes any output bit.  Returns BI_ERR_NULL for out == NULL,
  * BI_ERR_UNSUPPORTED for an unknown entry or sizes beyond the limits,
  * BI_ERR_SHAPE for sizes the entry point rejects or M == 0 or N == 0 (no

@@ -43,7 +43,8 @@ class BiGeometry(ctypes.Structure):
 
 ORDER_SEQUENTIAL, ORDER_BLOCK_FMA = 0, 1
 ENTRIES = {"bf16": 0, "bf16_bt": 1, "bf16_packed": 2, "bf16_grouped_packed": 3, "fp8": 4,
-           "fp8_packed": 5, "fp4": 6, "fp4_packed": 7, "w4a8_packed": 8, "fp8_grouped_packed": 9}
+           "fp8_packed": 5, "fp4": 6, "fp4_packed": 7, "w4a8_packed": 8, "fp8_grouped_packed": 9,
+           "w4a8_grouped_packed": 10}
 
 
 lib.bi_gemm_bf16.restype = _i32
@@ -68,6 +69,9 @@ lib.bi_pack_b_mxfp4.restype = _i32
 lib.bi_pack_b_mxfp4.argtypes = [_i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]
 lib.bi_gemm_w4a8_packed.restype = _i32
 lib.bi_gemm_w4a8_packed.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp, _i64, _vp]
+lib.bi_gemm_w4a8_grouped_packed.restype = _i32
+lib.bi_gemm_w4a8_grouped_packed.argtypes = [_i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
+                                            _sz, _vp, _i64, _vp]
 lib.bi_pack_b_fp8.restype = _i32
 lib.bi_pack_b_fp8.argtypes = [_i64, _i64, _vp, _i64, _vp, _sz, _vp]
 lib.bi_gemm_fp8_blockscaled_packed.restype = _i32
@@ -472,6 +476,46 @@ def gemm_w4a8_packed(A: torch.Tensor, sA: torch.Tensor, Bp: PackedWeights,
     _check(lib.bi_gemm_w4a8_packed(M, Bp.N, K, A.data_ptr(), _ld(A), sA.data_ptr(), _ld(sA),
                                    Bp.data.data_ptr(), Bp.data.numel(), C.data_ptr(), _ld(C),
                                    _stream()), "bi_gemm_w4a8_packed")
+    return C
+
+
+def pack_b_mxfp4_grouped(Bqs, sEs, N: int) -> PackedWeights:
+    """Pack G experts' OCP MXFP4 weights (codes Bq [K, N/2], E8M0 scales
+    sE [K/32, N] each) back to back, one bi_pack_b_mxfp4 layout per expert."""
+    if len(Bqs) != len(sEs) or not Bqs:
+        raise ValueError("pack_b_mxfp4_grouped: one scale matrix per code matrix, at least one expert")
+    parts = [pack_b_mxfp4(Bq, sE, N) for Bq, sE in zip(Bqs, sEs)]
+    K = parts[0].K
+    if any(p.K != K for p in parts):
+        raise ValueError("all experts' weight matrices must have the same shape")
+    one = packed_b_bytes(BI_W4A8, N, K)
+    buf = torch.empty(max(one * len(parts), 16), dtype=torch.uint8, device=parts[0].data.device)
+    for g, p in enumerate(parts):
+        buf[g * one:(g + 1) * one].copy_(p.data[:one])
+    pw = PackedWeights(BI_W4A8, K, N, buf)
+    pw.groups = len(parts)
+    return pw
+
+
+def gemm_w4a8_grouped_packed(A: torch.Tensor, sA: torch.Tensor, offsets: torch.Tensor,
+                             Bp: PackedWeights, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Rows [offsets[g], offsets[g+1]) of (A, sA) times expert g's packed MXFP4 weights
+    (pack_b_mxfp4_grouped), via bi_gemm_w4a8_grouped_packed."""
+    A = _mat(A, _U8, "A")
+    sA = _mat(sA, (torch.float32,), "sA")
+    M, K = A.shape
+    if Bp.dtype != BI_W4A8 or Bp.K != K or not hasattr(Bp, "groups"):
+        raise ValueError("grouped packed MXFP4 weights do not match A")
+    _shape(sA, (M, _blocks(K, 128, "gemm_w4a8_grouped_packed")), "sA")
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1 \
+            or offsets.numel() != Bp.groups + 1 or (offsets.numel() > 1 and offsets.stride(0) != 1):
+        raise ValueError("offsets: a contiguous int32 device tensor of G + 1 entries")
+    _same_device(A.device, sA=sA, Bp=Bp.data, offsets=offsets)
+    C = _out(M, Bp.N, A.device, out)
+    _check(lib.bi_gemm_w4a8_grouped_packed(
+        Bp.groups, offsets.data_ptr(), M, Bp.N, K, A.data_ptr(), _ld(A), sA.data_ptr(), _ld(sA),
+        Bp.data.data_ptr(), Bp.data.numel(), C.data_ptr(), _ld(C), _stream()),
+        "bi_gemm_w4a8_grouped_packed")
     return C
 
 

@@ -366,6 +366,15 @@ bi_status bi_geometry_query(bi_entry entry, int64_t M, int64_t N, int64_t K, int
             return BI_ERR_SHAPE;
         g = geometry_w4a8_packed(M, N, K);
         break;
+    case BI_ENTRY_W4A8_GROUPED_PACKED:
+        if (K % 128 || N % 2)
+            return BI_ERR_SHAPE;
+        if (groups < 1)
+            return BI_ERR_SHAPE;
+        if (groups > 65536)
+            return BI_ERR_UNSUPPORTED;
+        g = geometry_w4a8_grouped(M, N, K, groups);
+        break;
     default: return BI_ERR_UNSUPPORTED;
     }
     if (g.workgroups > 0x7FFFFFFF)
@@ -714,6 +723,41 @@ bi_status bi_gemm_w4a8_packed(int64_t M, int64_t N, int64_t K, const uint8_t* A,
         return BI_ERR_UNSUPPORTED;
     GemmArgs a{(int)M, (int)N, (int)K, A, lda, sA, ldsa, Bp, 0, nullptr, 0, C, ldc};
     return launched(launch_w4a8_packed(a, (hipStream_t)stream));
+}
+
+bi_status bi_gemm_w4a8_grouped_packed(int64_t G, const int32_t* offsets, int64_t M, int64_t N,
+                                      int64_t K, const uint8_t* A, int64_t lda, const float* sA,
+                                      int64_t ldsa, const void* Bp, size_t bp_bytes, uint16_t* C,
+                                      int64_t ldc, void* stream)
+{
+    bi_status st = check_dims(M, N, K);
+    if (st != BI_OK)
+        return st;
+    if (G < 0 || K % 128 || N % 2)
+        return BI_ERR_SHAPE;
+    if (G > 65536)
+        return BI_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0)
+        return BI_OK;
+    if (G == 0)
+        return BI_ERR_SHAPE;                          // rows but no group to own them
+    if (!offsets || !C || (K > 0 && (!A || !sA || !Bp)))
+        return BI_ERR_NULL;
+    if ((K > 0 && (lda < K || ldsa < K / 128)) || ldc < N)
+        return BI_ERR_STRIDE;
+    if (K > 0 && (!pitch_ok(lda, 1) || !pitch_ok(ldsa, 4)))
+        return BI_ERR_UNSUPPORTED;
+    if (((uintptr_t)C & 1u) || ((uintptr_t)offsets & 3u) ||
+        (K > 0 && (!aligned16(A) || lda % 16 || !aligned16(Bp) || !aligned4(sA))))
+        return BI_ERR_ALIGN;
+    const size_t one = bi_packed_b_bytes(BI_W4A8, N, K);
+    if (bp_bytes / (size_t)G < one)
+        return BI_ERR_WORKSPACE;
+    if (one > 0x7FFFFFFFu || ((M + 15) / 16 + G) * ((N + 15) / 16) > 0x7FFFFFFF)
+        return BI_ERR_UNSUPPORTED;
+    GemmArgs a{(int)M, (int)N, (int)K, A, lda, sA, ldsa, Bp, 0, nullptr, 0, C, ldc};
+    GroupArgs g{offsets, (int)G, (int64_t)one};
+    return launched(launch_w4a8_grouped_packed(a, g, (hipStream_t)stream));
 }
 
 int bi_splitk_choose(int64_t M, int64_t N, int64_t K)

@@ -28,6 +28,8 @@
 //
 // Weight codes and scales are read once and loaded non-temporal, except in
 // the largest-M geometry, whose row tiles share each column strip.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -38,11 +40,17 @@ constexpr int KBK = 128;       // K per MFMA (and per activation scale)
 constexpr int CTILE = 1024;    // code bytes per (column block, K block)
 constexpr int STILE = 64;      // scale bytes per (column block, K block)
 
-template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool NT, int AR>
+// GROUPED (mixture-of-experts): rows [offsets[g], offsets[g+1]) use the
+// g-th packed matrix (codes and scales, b_stride bytes apart); row slot mt
+// enumerates the groups' row tiles in order, and slots past the last tile
+// exit at once.  A row's arithmetic is that of the ungrouped kernel with its
+// group's weights, so it does not depend on how the other rows are routed.
+template <int WAVES, int RB, int CB, int WR, int WC, int KB_ST, int PF, bool NT, int AR, bool GROUPED>
 __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
     int M, int N, int K,
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t ldsa,
-    const uint8_t* __restrict__ Bp, uint16_t* __restrict__ C, int64_t ldc, int m_tiles)
+    const uint8_t* __restrict__ Bp, uint16_t* __restrict__ C, int64_t ldc, int m_tiles,
+    const int32_t* __restrict__ offsets, int n_groups, int64_t b_stride)
 {
     constexpr int NTHR = 64 * WAVES;
     constexpr int BM = 16 * RB;
@@ -73,14 +81,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
     const int tile = xcd_remap(blockIdx.x, gridDim.x);
     const int nt = tile / m_tiles;
     const int mt = tile - nt * m_tiles;
-    const int m0 = mt * BM;
+    int m0 = mt * BM;
+    int row_end = M;                                  // rows [m0, row_end) are this tile's
+    if constexpr (GROUPED) {
+        const int g = group_of_slot(offsets, n_groups, M, BM, mt, m0, row_end);
+        if (g == n_groups)
+            return;                                   // an unused slot (uniform per workgroup)
+        Bp += g * b_stride;
+    }
     const int NB = (N + 15) >> 4;
     const int nkb = K / KBK;
     const int nbw = nt * CB;
     const uint8_t* scales = Bp + (int64_t)NB * nkb * CTILE;
 
     const int nst = (nkb + KB_ST - 1) / KB_ST;
-    const int rows_valid = M - m0 < BM ? M - m0 : BM;
+    const int rows_valid = row_end - m0 < BM ? row_end - m0 : BM;
     const int li = lane & 15;
     const int lg = lane >> 4;
     const uint32_t OOB = 0x80000000u;
@@ -298,7 +313,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = m0 + 16 * (wr0 + r) + 4 * lg + j;
-                    if (row < M && col < N)
+                    if (row < row_end && col < N)
                         C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc[r][c][j]);
                 }
             }
@@ -347,17 +362,34 @@ struct Cfg {
 
 // The geometry table.  Every entry runs the same per-element arithmetic.
 constexpr Cfg kCfg[] = {
-    /* 0 */ {4, 1, 4, 1, 1, 4, 4, true, 16},    // 16 x 64: four waves, one block each
-    /* 1 */ {4, 1, 4, 1, 1, 4, 4, true, 8},     //   the same, 8 rows of A staged
+    /* 0 */ {4, 1, 4, 1, 1, 4, 2, true, 16},    // 16 x 64: four waves, one block each
+    /* 1 */ {4, 1, 4, 1, 1, 4, 2, true, 8},     //   the same, 8 rows of A staged
     /* 2 */ {4, 4, 4, 2, 2, 2, 2, true, 64},    // 64 x 64, two K blocks per stage
     /* 3 */ {4, 4, 4, 2, 2, 1, 4, false, 64},   // 64 x 64, one K block per stage, weights shared
     /* 4 */ {8, 4, 4, 2, 2, 4, 2, true, 64},    // 64 x 64, eight waves (four only load), four K blocks per stage
     /* 5 */ {4, 2, 4, 1, 2, 4, 2, true, 32},    // 32 x 64, four waves of 16 x 32, four K blocks per stage
     /* 6 */ {4, 4, 8, 2, 4, 1, 2, false, 64},   // 64 x 128, four waves of 32 x 64, weights shared
+    /* 7 */ {1, 1, 1, 1, 1, 4, 2, true, 16},    // 16 x 16, one wave (narrow weights)
+    /* 8 */ {2, 1, 2, 1, 1, 4, 2, true, 16},    // 16 x 32, two waves (narrow weights)
+    /* 9 */ {1, 1, 1, 1, 1, 4, 2, true, 8},     //   16 x 16, 8 rows of A staged
+    /* 10 */ {2, 1, 2, 1, 1, 4, 2, true, 8},    //   16 x 32, 8 rows of A staged
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
-Geometry describe(int id, int64_t M, int64_t N)
+int64_t n_tiles_of(const Cfg& c, int64_t N) { return ceil_div(ceil_div(N, 16), c.cb); }
+
+// Row slots of a grouped call: at most k = min(groups, M) groups hold rows,
+// and sum ceil(r_g / BM) <= floor((M + k (BM - 1)) / BM) -- one slot at M = 1.
+int64_t m_tiles_of(const Cfg& c, int64_t M, int64_t groups)
+{
+    const int64_t bm = 16 * c.rb;
+    if (groups <= 0)
+        return ceil_div(M, bm);
+    const int64_t k = std::min<int64_t>(groups, M);
+    return (M + k * (bm - 1)) / bm;
+}
+
+Geometry describe(int id, int64_t M, int64_t N, int64_t groups = 0)
 {
     const Cfg& c = kCfg[id];
     Geometry g;
@@ -368,22 +400,66 @@ Geometry describe(int id, int64_t M, int64_t N)
     g.a_rows = c.ar;
     g.k_stage = c.kb_st * KBK;
     g.stages = c.pf;
-    g.workgroups = ceil_div(ceil_div(N, 16), c.cb) * ceil_div(M, 16 * c.rb);
+    g.workgroups = n_tiles_of(c, N) * m_tiles_of(c, M, groups);
     return g;
 }
 
 template <int I>
-hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
+hipError_t launch_cfg(const GemmArgs& a, const GroupArgs* grp, const Geometry& g, hipStream_t stream)
 {
     constexpr Cfg c = kCfg[I];
     if (g.workgroups <= 0 || g.workgroups > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
-    const int m_tiles = (int)ceil_div(a.M, 16 * c.rb);
-    gemm_w4a8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.nt, c.ar>
-        <<<dim3((unsigned)g.workgroups), dim3(64 * c.waves), 0, stream>>>(
-            a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
-            (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
+    const int m_tiles = (int)m_tiles_of(c, a.M, grp ? grp->n_groups : 0);
+    const dim3 grid((unsigned)g.workgroups), block(64 * c.waves);
+    if (grp)
+        gemm_w4a8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.nt, c.ar, true>
+            <<<grid, block, 0, stream>>>(
+                a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
+                (const uint8_t*)a.B, a.C, a.ldc, m_tiles, grp->offsets, grp->n_groups, grp->b_stride);
+    else
+        gemm_w4a8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.nt, c.ar, false>
+            <<<grid, block, 0, stream>>>(
+                a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
+                (const uint8_t*)a.B, a.C, a.ldc, m_tiles, nullptr, 0, 0);
     return hipGetLastError();
+}
+
+hipError_t launch_id(const GemmArgs& a, const GroupArgs* grp, const Geometry& g, hipStream_t stream)
+{
+    switch (g.id) {
+    case 0: return launch_cfg<0>(a, grp, g, stream);
+    case 1: return launch_cfg<1>(a, grp, g, stream);
+    case 2: return launch_cfg<2>(a, grp, g, stream);
+    case 3: return launch_cfg<3>(a, grp, g, stream);
+    case 4: return launch_cfg<4>(a, grp, g, stream);
+    case 5: return launch_cfg<5>(a, grp, g, stream);
+    case 6: return launch_cfg<6>(a, grp, g, stream);
+    case 7: return launch_cfg<7>(a, grp, g, stream);
+    case 8: return launch_cfg<8>(a, grp, g, stream);
+    case 9: return launch_cfg<9>(a, grp, g, stream);
+    case 10: return launch_cfg<10>(a, grp, g, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+static_assert(kNumCfg == 11, "every table entry needs its case in launch_id");
+
+// The 16-row geometry for calls of at most 16 rows per group: 16 x 64 tiles
+// of four waves where `slots` x N/64 tiles fill the compute units in one
+// round; for narrower weights the narrowest of 16 x 16 (one wave) and 16 x 32
+// (two waves) whose tiles still fit in one round, so that narrow weights keep
+// more compute units streaming; each with 8 rows of A staged when the whole
+// call has at most 8 rows.  Two stages in flight (against four: K = 4096,
+// N = 14336, M = 1 9.2 -> 8.7 us; K = 7168, N = 2048, M = 1 on one-wave
+// 16 x 16 tiles 11.9 -> about 10.5 us).
+int narrow_rows_id(int64_t M, int64_t N, int64_t slots)
+{
+    const bool few = M <= 8;
+    if (slots * n_tiles_of(kCfg[0], N) >= 256 || slots * n_tiles_of(kCfg[8], N) > 256)
+        return few ? 1 : 0;
+    if (slots * n_tiles_of(kCfg[7], N) <= 256)
+        return few ? 9 : 7;
+    return few ? 10 : 8;
 }
 
 }  // namespace
@@ -410,7 +486,7 @@ Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K)
     const int64_t col_tiles = ceil_div(ceil_div(N, 16), 4);
     int id;
     if (M <= 16)
-        id = M <= 8 ? 1 : 0;
+        id = narrow_rows_id(M, N, 1);
     else if (M <= 32 && ceil_div(M, 32) * col_tiles <= 256)
         id = 5;
     else if (ceil_div(M, 64) * col_tiles <= 256)
@@ -424,19 +500,33 @@ Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K)
 
 hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream)
 {
-    const Geometry g = geometry_w4a8_packed(a.M, a.N, a.K);
-    switch (g.id) {
-    case 0: return launch_cfg<0>(a, g, stream);
-    case 1: return launch_cfg<1>(a, g, stream);
-    case 2: return launch_cfg<2>(a, g, stream);
-    case 3: return launch_cfg<3>(a, g, stream);
-    case 4: return launch_cfg<4>(a, g, stream);
-    case 5: return launch_cfg<5>(a, g, stream);
-    case 6: return launch_cfg<6>(a, g, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_id(a, nullptr, geometry_w4a8_packed(a.M, a.N, a.K), stream);
 }
-static_assert(kNumCfg == 7, "every table entry needs its case in launch_w4a8_packed");
+
+// Grouped calls: the tiles must cover every group's rows, so the grid holds
+// sum over groups of ceil(rows / BM) row slots per column tile (bounded by
+// m_tiles_of; slots past the occupied ones exit at once).  While the groups
+// average at most 16 rows, 16 x 64 tiles (the 8-row variant only when the
+// whole call has at most 8 rows, all of which may fall into one group);
+// otherwise the smallest of 32 x 64 and 64 x 64 (eight waves) whose grid
+// fits in one round, else 64 x 64 on four waves.
+Geometry geometry_w4a8_grouped(int64_t M, int64_t N, int64_t K, int64_t groups)
+{
+    (void)K;
+    if (ceil_div(M, groups) <= 16)
+        return describe(narrow_rows_id(M, N, std::min<int64_t>(groups, M)), M, N, groups);
+    for (int id : {5, 4}) {
+        const Geometry g = describe(id, M, N, groups);
+        if (g.workgroups <= 256)
+            return g;
+    }
+    return describe(M > 128 ? 3 : 2, M, N, groups);
+}
+
+hipError_t launch_w4a8_grouped_packed(const GemmArgs& a, const GroupArgs& g, hipStream_t stream)
+{
+    return launch_id(a, &g, geometry_w4a8_grouped(a.M, a.N, a.K, g.n_groups), stream);
+}
 
 hipError_t launch_pack_mxfp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sE,
                              int64_t ldse, uint8_t* Bp, hipStream_t stream)

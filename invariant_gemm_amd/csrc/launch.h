@@ -63,6 +63,7 @@ Geometry geometry_fp8_grouped(int64_t M, int64_t N, int64_t K, int64_t groups);
 Geometry geometry_fp4(int64_t M, int64_t N, int64_t K);
 Geometry geometry_fp4_packed(int64_t M, int64_t N, int64_t K);
 Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K);
+Geometry geometry_w4a8_grouped(int64_t M, int64_t N, int64_t K, int64_t groups);
 
 hipError_t launch_bf16(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_bf16_bt(const GemmArgs& a, hipStream_t stream);
@@ -79,6 +80,7 @@ hipError_t launch_pack_fp8(int N, int K, const uint8_t* B, int64_t ldb, uint8_t*
                            hipStream_t stream);
 hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_w4a8_grouped_packed(const GemmArgs& a, const GroupArgs& g, hipStream_t stream);
 hipError_t launch_pack_mxfp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sE,
                              int64_t ldse, uint8_t* Bp, hipStream_t stream);
 hipError_t launch_pack_fp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sB,

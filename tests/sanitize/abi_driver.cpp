@@ -209,6 +209,32 @@ static void fp4_entries()
            BI_ERR_STRIDE);
     EXPECT(bi_gemm_w4a8_packed(M, N, K8, A8.p, K8 - 8, sA.as<float>(), 2, Bw.p, pw, c, N, nullptr),
            BI_ERR_STRIDE);
+
+    const int64_t G = 3;
+    Buf off((G + 1) * 4), Bwg(G * pw);
+    int32_t* o = off.as<int32_t>();
+    o[0] = 0; o[1] = 4; o[2] = 4; o[3] = (int32_t)M;
+    EXPECT(bi_gemm_w4a8_grouped_packed(G, o, M, N, K8, A8.p, K8, sA.as<float>(), 2, Bwg.p, G * pw, c, N,
+                                       nullptr),
+           BI_ERR_LAUNCH);
+    EXPECT(bi_gemm_w4a8_grouped_packed(G, o, M, N, K8, A8.p, K8, sA.as<float>(), 2, Bwg.p, G * pw - 1,
+                                       c, N, nullptr),
+           BI_ERR_WORKSPACE);
+    EXPECT(bi_gemm_w4a8_grouped_packed(G, o, M, N, 200, A8.p, K8, sA.as<float>(), 2, Bwg.p, G * pw, c,
+                                       N, nullptr),
+           BI_ERR_SHAPE);
+    EXPECT(bi_gemm_w4a8_grouped_packed(0, o, M, N, K8, A8.p, K8, sA.as<float>(), 2, Bwg.p, G * pw, c, N,
+                                       nullptr),
+           BI_ERR_SHAPE);
+    EXPECT(bi_gemm_w4a8_grouped_packed(G, o, M, N, K8, A8.p, K8, sA.as<float>(), 1, Bwg.p, G * pw, c, N,
+                                       nullptr),
+           BI_ERR_STRIDE);
+    EXPECT(bi_gemm_w4a8_grouped_packed(INT64_MAX, o, M, N, K8, A8.p, K8, sA.as<float>(), 2, Bwg.p,
+                                       SIZE_MAX, c, N, nullptr),
+           BI_ERR_UNSUPPORTED);
+    EXPECT(bi_gemm_w4a8_grouped_packed(0, nullptr, 0, N, K8, nullptr, K8, nullptr, 2, nullptr, 0,
+                                       nullptr, N, nullptr),
+           BI_OK);
 }
 
 static void queries()
@@ -220,12 +246,13 @@ static void queries()
     EXPECT(bi_schedule_query((bi_dtype)77, 256, 1024, &s), BI_ERR_UNSUPPORTED);
     EXPECT(bi_schedule_query(BI_BF16, 256, 1024, nullptr), BI_ERR_NULL);
     bi_geometry g;
-    for (int e = 0; e <= 9; ++e) {
+    for (int e = 0; e <= 10; ++e) {
         EXPECT(bi_geometry_query((bi_entry)e, 1, 2048, 7168, 8, &g), BI_OK);
         EXPECT(bi_geometry_query((bi_entry)e, 0, 2048, 7168, 8, &g), BI_ERR_SHAPE);
         EXPECT(bi_geometry_query((bi_entry)e, INT64_MAX, 2048, 7168, 8, &g), BI_ERR_UNSUPPORTED);
     }
     EXPECT(bi_geometry_query(BI_ENTRY_FP8_GROUPED_PACKED, 4, 256, 256, 0, &g), BI_ERR_SHAPE);
+    EXPECT(bi_geometry_query(BI_ENTRY_W4A8_GROUPED_PACKED, 4, 256, 256, 0, &g), BI_ERR_SHAPE);
     EXPECT(bi_geometry_query((bi_entry)99, 4, 256, 256, 1, &g), BI_ERR_UNSUPPORTED);
     EXPECT(bi_geometry_query(BI_ENTRY_BF16, 4, 256, 256, 1, nullptr), BI_ERR_NULL);
     for (bi_dtype d : {BI_BF16, BI_FP8_BS, BI_FP4_W, BI_W4A8})

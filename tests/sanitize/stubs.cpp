@@ -31,6 +31,7 @@ Geometry geometry_fp8_grouped(int64_t M, int64_t N, int64_t, int64_t) { return n
 Geometry geometry_fp4(int64_t M, int64_t N, int64_t) { return none(M, N); }
 Geometry geometry_fp4_packed(int64_t M, int64_t N, int64_t) { return none(M, N); }
 Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t) { return none(M, N); }
+Geometry geometry_w4a8_grouped(int64_t M, int64_t N, int64_t, int64_t) { return none(M, N); }
 
 hipError_t launch_bf16(const GemmArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_bf16_bt(const GemmArgs&, hipStream_t) { return hipErrorInvalidValue; }
@@ -56,6 +57,10 @@ hipError_t launch_pack_fp8(int, int, const uint8_t*, int64_t, uint8_t*, hipStrea
 }
 hipError_t launch_fp4w_packed(const GemmArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_w4a8_packed(const GemmArgs&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_w4a8_grouped_packed(const GemmArgs&, const GroupArgs&, hipStream_t)
+{
+    return hipErrorInvalidValue;
+}
 hipError_t launch_pack_mxfp4(int, int, const uint8_t*, int64_t, const uint8_t*, int64_t, uint8_t*,
                              hipStream_t)
 {

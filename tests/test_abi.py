@@ -243,6 +243,27 @@ def test_grouped_fp8_validation():
     assert f(1 << 20, 8) == UNSUP
 
 
+def test_grouped_w4a8_validation():
+    need = bigemm.packed_b_bytes(bigemm.BI_W4A8, 64, 256)
+    f = lambda G, M, N=64, K=256, off=P, A=P, lda=None, sA=P, Bp=P, nb=None, C=P: \
+        lib.bi_gemm_w4a8_grouped_packed(G, off, M, N, K, A, K if lda is None else lda, sA,
+                                        max(K // 128, 1), Bp, need * G if nb is None else nb, C, N, None)
+    assert f(-1, 8) == SHAPE
+    assert f(0, 8) == SHAPE                    # rows but no group
+    assert f(3, 8, K=200) == SHAPE             # K % 128
+    assert f(3, 8, N=63) == SHAPE              # N odd
+    assert f(0, 0) == OK
+    assert f(3, 0, off=None, A=None, sA=None, Bp=None, C=None) == OK
+    assert f(3, 8, off=None) == NULL
+    assert f(3, 8, sA=None) == NULL
+    assert f(3, 8, lda=128) == STRIDE
+    assert f(3, 8, nb=need * 3 - 1) == WS
+    assert f(3, 8, off=P + 2) == ALIGN
+    assert f(3, 8, lda=264) == ALIGN
+    assert f(3, 8, sA=P + 2) == ALIGN
+    assert f(1 << 20, 8) == UNSUP
+
+
 def test_w4a8_validation():
     need = lambda N, K: bigemm.packed_b_bytes(bigemm.BI_W4A8, N, K)
     assert need(2048, 7168) == 128 * 56 * 1088 and need(64, 100) == 0 and need(63, 128) == 0
