@@ -29,11 +29,11 @@
 // exactly the operands, K order and scales of the full-block path.
 // Weight bytes are read once and loaded non-temporal.
 //
-// Only the first AR rows of each A stage are loaded and written to LDS (AR =
-// BM, or 8 for calls of at most 8 rows on half blocks): LDS rows past them
-// keep stale bytes, which reach only output rows that are never stored -- an
-// MFMA output row depends on its own A row alone, and each row's scale FMA on
-// its own sA value.
+// Only the first AR rows of each A stage are loaded and written to LDS (every
+// table entry stages the whole tile, AR = BM; calls with fewer rows go to the
+// unstaged kernel below): LDS rows past them would keep stale bytes, which
+// reach only output rows that are never stored -- an MFMA output row depends
+// on its own A row alone, and each row's scale FMA on its own sA value.
 #include <algorithm>
 
 #include "common.h"
@@ -381,6 +381,159 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     }
 }
 
+// Small-M variant without operand staging: one 16-row block, 16 columns (or
+// 8, HALF as above) per workgroup.  The K blocks are taken in rounds of
+// R = WAVES*KPW; in a round, wave w loads the A and B operands of blocks
+// kb0 + w*KPW .. + KPW-1 straight from global memory into its registers (the
+// packed weights are already in the MFMA's lane order), all loads issued
+// before the first MFMA, and forms each block's product P with the same
+// MFMA into a zero accumulator.  The products go to LDS, and four waves --
+// one per accumulator component -- fold them in ascending K order with the
+// same acc = fma(P, sA*sB, acc), so every output element sees exactly the
+// operations of the staged kernel above.  Loads for the next round are
+// issued before the fold of the current one.  Blocks past K/128 in the last
+// round are loaded (B as zero outside its extent) but never folded.
+template <int WAVES, int KPW, bool HALF, bool GROUPED>
+__global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_direct_kernel(
+    int M, int N, int K,
+    const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t ldsa,
+    const uint8_t* __restrict__ Bp, const float* __restrict__ sB, int64_t ldsb,
+    uint16_t* __restrict__ C, int64_t ldc, int m_tiles,
+    const int32_t* __restrict__ offsets, int n_groups, int64_t b_stride, int64_t sb_stride)
+{
+    static_assert(WAVES >= 4, "four folding waves, one per accumulator component");
+    constexpr int NTHR = 64 * WAVES;
+    constexpr int R = WAVES * KPW;                    // K blocks per round
+    constexpr int SPT = (R * 16 + NTHR - 1) / NTHR;   // activation scales per thread and round
+    static_assert(R <= NTHR, "one weight scale per thread and round");
+    __shared__ float pbuf[R][4][64];                  // [block][component][lane]
+    __shared__ float sas[R][16];                      // sA of the tile's rows, block-major
+    __shared__ float sbs[R];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    const int ntile = tile / m_tiles;
+    const int mt = tile - ntile * m_tiles;
+    const int nb = HALF ? ntile >> 1 : ntile;
+    const int ch = HALF ? ntile & 1 : 0;
+    int m0 = mt * 16;
+    int row_end = M;
+    if constexpr (GROUPED) {
+        const int g = group_of_slot(offsets, n_groups, M, 16, mt, m0, row_end);
+        if (g == n_groups)
+            return;                                   // an unused slot (uniform per workgroup)
+        Bp += g * b_stride;
+        sB += g * sb_stride;
+    }
+    const int NB = (N + 15) >> 4;
+    const int nkb = K / KBK;
+    const int rows_valid = row_end - m0 < 16 ? row_end - m0 : 16;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const uint32_t OOB = 0x80000000u;
+    // A operand of lane 16g + i: row i, bytes 32g .. 32g+31 of the block;
+    // rows past the tile's valid rows lie outside the extent and read zero.
+    const uint32_t a_off = (uint32_t)(li * lda + 32 * lg);
+    // B operand: the lane's two 16-byte pieces of the packed tile (HALF: of
+    // the lane that holds the same column among the workgroup's 8).
+    const uint32_t b_off = (uint32_t)((HALF ? 16 * lg + 8 * ch + (li & 7) : lane) * 16);
+    const int q0 = wave * KPW;                        // the wave's first block in a round
+    const int scol = (16 * nb) / 128;                 // the tile's column of sB
+
+    u32x4 a[KPW][2], b[KPW][2];
+    float sav[SPT], sbv;
+    auto issue = [&](int kb0) {
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+            Bp + ((int64_t)nb * nkb + kb0) * BTILE, nb < NB ? clamp_bytes((int64_t)(nkb - kb0) * BTILE) : 0u);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+            A + (int64_t)m0 * lda + (int64_t)kb0 * KBK,
+            clamp_bytes((int64_t)(rows_valid - 1) * lda + K - (int64_t)kb0 * KBK));
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
+            sA + (int64_t)m0 * ldsa + kb0, clamp_bytes(((int64_t)(rows_valid - 1) * ldsa + nkb - kb0) * 4));
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
+            sB + (int64_t)kb0 * ldsb + scol, clamp_bytes(((int64_t)(nkb - 1 - kb0) * ldsb + 1) * 4));
+#pragma unroll
+        for (int t = 0; t < KPW; ++t) {
+            const uint32_t o = (uint32_t)(q0 + t) * BTILE + b_off;
+            b[t][0] = buf_load16_nt(rb, o);
+            b[t][1] = buf_load16_nt(rb, o + 1024);
+        }
+#pragma unroll
+        for (int t = 0; t < KPW; ++t) {
+            const uint32_t o = a_off + (uint32_t)(q0 + t) * KBK;
+            a[t][0] = buf_load16(ra, o);
+            a[t][1] = buf_load16(ra, o + 16);
+        }
+        // scale value u of the round: row u / R, block u % R
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int u = j * NTHR + tid;
+            const uint32_t o = u < R * 16 ? (uint32_t)(((u / R) * ldsa + u % R) * 4) : OOB;
+            sav[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)o, 0, 0));
+        }
+        sbv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+            rsb, (int)(tid < R ? (uint32_t)(tid * ldsb * 4) : OOB), 0, 0));
+    };
+
+    float acc = 0.f;
+    // K = 0 issues no load at all: the extents above assume a live round
+    if (nkb > 0)
+        issue(0);
+    for (int kb0 = 0; kb0 < nkb; kb0 += R) {
+        // keep every load above issued before the first MFMA below waits
+        __builtin_amdgcn_sched_barrier(0);
+        if (kb0 + q0 < nkb) {
+#pragma unroll
+            for (int t = 0; t < KPW; ++t) {
+                const i32x8 av = {(int)a[t][0][0], (int)a[t][0][1], (int)a[t][0][2], (int)a[t][0][3],
+                                  (int)a[t][1][0], (int)a[t][1][1], (int)a[t][1][2], (int)a[t][1][3]};
+                const i32x8 bv = {(int)b[t][0][0], (int)b[t][0][1], (int)b[t][0][2], (int)b[t][0][3],
+                                  (int)b[t][1][0], (int)b[t][1][1], (int)b[t][1][2], (int)b[t][1][3]};
+                // fp8 e4m3 x fp8 e4m3, unit E8M0 block scales (127 = 2^0)
+                const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    pbuf[q0 + t][j][lane] = P[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int u = j * NTHR + tid;
+            if (u < R * 16)
+                sas[u % R][u / R] = sav[j];
+        }
+        if (tid < R)
+            sbs[tid] = sbv;
+        __syncthreads();
+        if (kb0 + R < nkb)
+            issue(kb0 + R);
+        if (wave < 4) {
+            // wave j folds component j: rows 4g + j of the block
+            const int nq = nkb - kb0 < R ? nkb - kb0 : R;
+            if (nq == R) {
+#pragma unroll
+                for (int q = 0; q < R; ++q)
+                    acc = __builtin_fmaf(pbuf[q][wave][lane], sas[q][4 * lg + wave] * sbs[q], acc);
+            } else {
+#pragma unroll 8
+                for (int q = 0; q < nq; ++q)
+                    acc = __builtin_fmaf(pbuf[q][wave][lane], sas[q][4 * lg + wave] * sbs[q], acc);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (wave < 4) {
+        const int row = m0 + 4 * lg + wave;
+        const int col = HALF ? 16 * nb + 8 * ch + li : 16 * nb + li;
+        if (row < row_end && col < N && (!HALF || li < 8))
+            C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc);
+    }
+}
+
 // One thread per 16-byte packed chunk: u = ((nb*KB + kb)*2 + h)*64 + l.
 __global__ void pack_fp8_kernel(int N, int K, const uint8_t* __restrict__ B, int64_t ldb,
                                 uint8_t* __restrict__ Bp, int64_t nchunks)
@@ -412,11 +565,13 @@ __global__ void pack_fp8_kernel(int N, int K, const uint8_t* __restrict__ B, int
 
 // One launch geometry: WAVES waves, RB x CB MFMA blocks per workgroup split
 // among the waves as WR x WC sub-tiles, KB_ST K blocks per stage, PF stages
-// in flight, half blocks, AR staged A rows.
+// in flight, half blocks, AR staged A rows; KPW > 0 selects the unstaged
+// kernel (one 16-row block, KPW K blocks per wave and round).
 struct Cfg {
     int waves, rb, cb, wr, wc, kb_st, pf;
     bool half;
     int ar;
+    int kpw = 0;
 };
 
 // The geometry table.  Every entry runs the same per-element arithmetic.
@@ -425,9 +580,15 @@ struct Cfg {
 // one and the loads of the next stage overlap the LDS reads and MFMAs of the
 // current one (measured at K = 7168, N = 2048 against four-wave versions of
 // the same tiles: M = 128 22.8 -> 14 us, M = 256 25.5 -> 18.7 us, M = 512
-// 35 -> 27.5 us).  The half-block entries take 16 K blocks per stage with two
-// stages in flight (against 8 blocks and four stages: M = 1 8.8 -> 8.4 us,
-// M = 4 9.2 -> 8.8 us, M = 16 10.2 -> 10.0 us).
+// 35 -> 27.5 us).  The staged half-block entry takes 16 K blocks per stage
+// with two stages in flight.  The unstaged entries (8, 9) issue all loads of
+// a round at once and skip the LDS round trip per stage: at K = 7168,
+// N = 2048 against the staged half blocks, M = 1 8.6 -> 6.4 us, M = 8
+// 9.4 -> 7.2 us, M = 16 10.2 -> 8.2 us; at N = 4096 against the staged
+// 16 x 16 tile, M = 1 11.6 -> 8.2 us, M = 16 12.3 -> 10.4 us.  Beyond one
+// round (K > 7168) each round waits for its own loads, and for more than 8
+// rows the staged kernel is faster there (M = 16, K = 16384: 15.8 against
+// 17.9 us).
 constexpr Cfg kCfg[] = {
     /* 0 */ {8, 1, 1, 1, 1, 8, 4, false, 16},   // 16 x 16, eight waves streaming
     /* 1 */ {8, 2, 1, 1, 1, 8, 2, false, 32},   // 32 x 16
@@ -435,9 +596,10 @@ constexpr Cfg kCfg[] = {
     /* 3 */ {8, 4, 2, 2, 1, 4, 2, false, 64},   // 64 x 32
     /* 4 */ {8, 4, 4, 2, 2, 4, 2, false, 64},   // 64 x 64
     /* 5 */ {4, 1, 1, 1, 1, 16, 2, true, 16},   // 16 x 8 half blocks, four waves
-    /* 6 */ {4, 1, 1, 1, 1, 16, 2, true, 8},    //   the same, 8 rows of A staged
-    /* 7 */ {8, 1, 2, 1, 1, 8, 2, false, 16},   // 16 x 32, two computing waves (grouped calls)
-    /* 8 */ {8, 1, 4, 1, 1, 4, 2, false, 16},   // 16 x 64, four computing waves (grouped calls)
+    /* 6 */ {8, 1, 2, 1, 1, 8, 2, false, 16},   // 16 x 32, two computing waves (grouped calls)
+    /* 7 */ {8, 1, 4, 1, 1, 4, 2, false, 16},   // 16 x 64, four computing waves (grouped calls)
+    /* 8 */ {8, 1, 1, 1, 1, 0, 1, true, 16, 7}, // 16 x 8 half blocks, unstaged, 56 K blocks a round
+    /* 9 */ {8, 1, 1, 1, 1, 0, 1, false, 16, 7}, // 16 x 16, unstaged
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -454,7 +616,7 @@ Geometry describe(int id, int64_t M, int64_t N, int64_t groups = 0)
     g.bn = c.half ? 8 : 16 * c.cb;
     g.waves = c.waves;
     g.a_rows = c.ar;
-    g.k_stage = c.kb_st * KBK;
+    g.k_stage = (c.kpw > 0 ? c.waves * c.kpw : c.kb_st) * KBK;
     g.stages = c.pf;
     g.workgroups = n_tiles_of(c, N) * m_tiles_of(c, M, groups);
     return g;
@@ -480,18 +642,31 @@ hipError_t launch_cfg(const GemmArgs& a, const GroupArgs* grp, int64_t sb_stride
         return hipErrorInvalidConfiguration;
     const int m_tiles = (int)m_tiles_of(c, a.M, grp ? grp->n_groups : 0);
     const dim3 grid((unsigned)g.workgroups), block(64 * c.waves);
-    if (grp)
-        gemm_fp8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.half, c.ar, true>
-            <<<grid, block, 0, stream>>>(
+    if constexpr (c.kpw > 0) {
+        if (grp)
+            gemm_fp8_packed_direct_kernel<c.waves, c.kpw, c.half, true><<<grid, block, 0, stream>>>(
                 a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
                 (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles,
                 grp->offsets, grp->n_groups, grp->b_stride, sb_stride);
-    else
-        gemm_fp8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.half, c.ar, false>
-            <<<grid, block, 0, stream>>>(
+        else
+            gemm_fp8_packed_direct_kernel<c.waves, c.kpw, c.half, false><<<grid, block, 0, stream>>>(
                 a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
                 (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles,
                 nullptr, 0, 0, 0);
+    } else {
+        if (grp)
+            gemm_fp8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.half, c.ar, true>
+                <<<grid, block, 0, stream>>>(
+                    a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
+                    (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles,
+                    grp->offsets, grp->n_groups, grp->b_stride, sb_stride);
+        else
+            gemm_fp8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.half, c.ar, false>
+                <<<grid, block, 0, stream>>>(
+                    a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
+                    (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles,
+                    nullptr, 0, 0, 0);
+    }
     return hipGetLastError();
 }
 
@@ -508,78 +683,87 @@ hipError_t launch_id(const GemmArgs& a, const GroupArgs* grp, int64_t sb_stride,
     case 6: return launch_cfg<6>(a, grp, sb_stride, g, stream);
     case 7: return launch_cfg<7>(a, grp, sb_stride, g, stream);
     case 8: return launch_cfg<8>(a, grp, sb_stride, g, stream);
+    case 9: return launch_cfg<9>(a, grp, sb_stride, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 9, "every table entry needs its case in launch_id");
+static_assert(kNumCfg == 10, "every table entry needs its case in launch_id");
 
 }  // namespace
 
 // Launch geometry (tile sharing only: every geometry runs the same
-// per-element arithmetic).  For M <= 16 one 16 x 16 block per workgroup with
-// eight waves streaming its weights -- or, while N/16 blocks would leave
-// compute units without a workgroup, half a block (8 columns, four waves) per
-// workgroup, staging only the first 8 rows of A for calls of at most 8 rows
-// (M = 1: 9.4 -> 8.9 us at K = 7168, N = 2048; staging 4 measured slower).
-// Above 16 rows: the smallest tile (16 x 16, 32 x 16, 32 x 32, 64 x 32,
-// 64 x 64) whose grid still fits on the compute units in one round, else the
-// largest.  A second, partial round of workgroups costs more than the larger
-// tile's extra rows: at K = 7168, N = 2048, M = 257 runs 33.8 us on 320
-// 64 x 32 tiles and 26.5 us on 160 64 x 64 tiles.
+// per-element arithmetic).  For M <= 16 one 16-row block per workgroup, on
+// half blocks (8 columns) while N/16 blocks would leave compute units without
+// a workgroup, else on whole 16 x 16 blocks.  Above 16 rows: the smallest
+// tile (16 x 16, 32 x 16, 32 x 32, 64 x 32, 64 x 64) whose grid still fits
+// on the compute units in one round, else the largest.  16-row tiles run
+// unstaged while one round of its loads covers K or the call has at most 8
+// rows (at K = 7168, N = 2048, M = 17..32: 11.9 -> 8.7 us), else staged.  A
+// second, partial round of workgroups costs more than the larger tile's
+// extra rows: at K = 7168, N = 2048, M = 257 runs 33.8 us on 320 64 x 32
+// tiles and 26.5 us on 160 64 x 64 tiles, and M = 64 14.5 us on 512 unstaged
+// 16 x 16 tiles against 11.9 us on 256 tiles of 32 x 16.
 namespace {
 constexpr int64_t kComputeUnits = 256;
+constexpr int kHalfDirect = 8, kFullDirect = 9, kHalfStaged = 5;
 
-int fp8_family(int64_t M, int64_t N)
+bool unstaged_fits(int64_t M, int64_t K)
+{
+    const Cfg& c = kCfg[kHalfDirect];
+    return M <= 8 || K / KBK <= (int64_t)c.waves * c.kpw;
+}
+
+// The 16 x 16 tile: unstaged when that fits.
+int tile16(int64_t M, int64_t K) { return unstaged_fits(M, K) ? kFullDirect : 0; }
+
+int fp8_family(int64_t M, int64_t N, int64_t K)
 {
     const int64_t nb = ceil_div(N, 16);
     if (M <= 16) {
         if (nb < kComputeUnits)
-            return M <= 8 ? 6 : 5;
-        return 0;
+            return unstaged_fits(M, K) ? kHalfDirect : kHalfStaged;
+        return tile16(M, K);
     }
     for (int id = 0; id < 4; ++id)
         if (ceil_div(M, 16 * kCfg[id].rb) * ceil_div(nb, kCfg[id].cb) <= kComputeUnits)
-            return id;
+            return id == 0 ? tile16(M, K) : id;
     return 4;
 }
 }  // namespace
 
 Geometry geometry_fp8_packed(int64_t M, int64_t N, int64_t K)
 {
-    (void)K;
-    return describe(fp8_family(M, N), M, N);
+    return describe(fp8_family(M, N, K), M, N);
 }
 
 // Grouped calls: the tiles must cover every group's rows, so the grid holds
 // sum over groups of ceil(rows / BM) row slots per column tile (bounded by
 // m_tiles_of).  The same rule as above on that grid: the smallest tile whose
 // workgroups fit on the compute units in one round (half blocks first while
-// the groups average at most 16 rows), else the largest; the 8-row variant
-// only when the whole call has at most 8 rows (all of them may fall into one
-// group).  While the groups average at most 8 rows, 16-row tiles of 16, 32
-// or 64 columns come next: the narrowest whose occupied slots -- at least one
-// per group that holds rows, min(groups, M) -- times its column tiles fit in
-// one round (the slots past the occupied ones exit at once).  E = 8, N = 2048,
+// the groups average at most 16 rows), else the largest.  While the groups
+// average at most 8 rows, 16-row tiles of 16 (unstaged), 32 or 64 columns
+// come next: the narrowest whose occupied slots -- at least one per group
+// that holds rows, min(groups, M) -- times its column tiles fit in one round
+// (the slots past the occupied ones exit at once).  E = 8, N = 2048,
 // K = 7168, tokens routed uniformly: T = 8 26.6 -> 19.5 us, T = 16 26.6 ->
 // 20.8 us, T = 64 27.1 -> 24.8 us; at 16 rows per group many groups need two
 // 16-row slots and the 64-row tiles stay faster (T = 128 28.7 against 36.5 us).
 Geometry geometry_fp8_grouped(int64_t M, int64_t N, int64_t K, int64_t groups)
 {
-    (void)K;
     const int64_t mean = ceil_div(M, groups);
     if (mean <= 16 && ceil_div(N, 16) < kComputeUnits) {
-        const Geometry h = describe(M <= 8 ? 6 : 5, M, N, groups);
+        const Geometry h = describe(unstaged_fits(M, K) ? kHalfDirect : kHalfStaged, M, N, groups);
         if (h.workgroups <= kComputeUnits)
             return h;
     }
     if (mean <= 8) {
         const int64_t occupied = std::min<int64_t>(groups, M);
-        for (int id : {0, 7, 8})
+        for (int id : {tile16(M, K), 6, 7})
             if (occupied * n_tiles_of(kCfg[id], N) <= kComputeUnits)
                 return describe(id, M, N, groups);
     }
     for (int id = 0; id < 4; ++id) {
-        const Geometry g = describe(id, M, N, groups);
+        const Geometry g = describe(id == 0 ? tile16(M, K) : id, M, N, groups);
         if (g.workgroups <= kComputeUnits)
             return g;
     }

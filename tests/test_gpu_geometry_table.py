@@ -1,12 +1,13 @@
 """Every entry of every launch-geometry table runs the same arithmetic.
 
 For each plain (ungrouped) entry point the geometry query is searched over a
-grid of (M, N) for the smallest call that selects each table entry; that
-call is run with a K whose last pipeline stage lies partly past K, and three
-of its rows are checked (1) against the fp64 oracle within the tolerance and
-(2) bit for bit against the same rows computed alone (M = 1, which selects
-another entry).  The grouped entry points have their own every-geometry
-tests."""
+grid of (M, N) -- and for the packed fp8 kernel two K, one of them past a
+single round of its unstaged entries -- for the smallest call that selects
+each table entry; that call is run with a K whose last pipeline stage lies
+partly past K, and three of its rows are checked (1) against the fp64 oracle
+within the tolerance and (2) bit for bit against the same rows computed alone
+(M = 1, which selects another entry).  The grouped entry points have their
+own every-geometry tests."""
 import numpy as np
 import pytest
 import torch
@@ -32,14 +33,15 @@ def pad16(n):
     return (n + 15) // 16 * 16
 
 
-def cases(bg, entry, K):
-    """{geometry id: (M, N)} -- the smallest M*N on the grid that selects it."""
+def cases(bg, entry, Ks):
+    """{geometry id: (M, N, K)} -- the smallest M*N*K on the grid that selects it."""
     found = {}
-    for N in N_GRID:
-        for M in M_GRID:
-            gid = bg.geometry(entry, M, N, K)["id"]
-            if gid not in found or M * N < found[gid][0] * found[gid][1]:
-                found[gid] = (M, N)
+    for K in Ks:
+        for N in N_GRID:
+            for M in M_GRID:
+                gid = bg.geometry(entry, M, N, K)["id"]
+                if gid not in found or M * N * K < np.prod(found[gid]):
+                    found[gid] = (M, N, K)
     return found
 
 
@@ -59,8 +61,7 @@ def check(bg, entry, gid, M, N, K, batch, alone, ref_rows):
 
 @pytest.mark.parametrize("entry", ["bf16", "bf16_bt", "bf16_packed"])
 def test_bf16_tables(bg, entry):
-    K = 360
-    for gid, (M, N) in sorted(cases(bg, entry, K).items()):
+    for gid, (M, N, K) in sorted(cases(bg, entry, [360]).items()):
         A = inputs.normal_bf16((M, K), 1.0, 9100 + gid)
         B = inputs.normal_bf16((K, N), 0.02, 9200 + gid)
         Ad = dev_bf16(A)
@@ -78,10 +79,14 @@ def test_bf16_tables(bg, entry):
               lambda rows: oracle.gemm_bf16(np.ascontiguousarray(A[rows]), B))
 
 
+# 384: three K blocks; 7296: 57, one more than a round of the packed kernel's
+# unstaged entries, which sends 9..16-row calls to its staged half blocks
+FP8_KS = {"fp8": [384], "fp8_packed": [384, 7296]}
+
+
 @pytest.mark.parametrize("entry", ["fp8", "fp8_packed"])
 def test_fp8_tables(bg, entry):
-    K = 384
-    for gid, (M, N) in sorted(cases(bg, entry, K).items()):
+    for gid, (M, N, K) in sorted(cases(bg, entry, FP8_KS[entry]).items()):
         qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((M, K), 1.0, 9300 + gid))
         qB, sB = inputs.quant_fp8_tiles(inputs.normal_f32((K, N), 1.0, 9400 + gid))
         Ad, sAd, sBd = dev_u8(qA), dev_f32(sA), dev_f32(sB)
@@ -99,8 +104,7 @@ def test_fp8_tables(bg, entry):
 
 @pytest.mark.parametrize("entry", ["fp4", "fp4_packed"])
 def test_fp4_tables(bg, entry):
-    K = 288
-    for gid, (M, N) in sorted(cases(bg, entry, K).items()):
+    for gid, (M, N, K) in sorted(cases(bg, entry, [288]).items()):
         A = inputs.normal_bf16((M, K), 1.0, 9500 + gid)
         Bq, sB = inputs.quant_fp4_weights(inputs.normal_f32((K, N), 0.02, 9600 + gid))
         Ad = dev_bf16(A)
@@ -116,8 +120,8 @@ def test_fp4_tables(bg, entry):
 
 
 def test_w4a8_table(bg):
-    entry, K = "w4a8_packed", 384
-    for gid, (M, N) in sorted(cases(bg, entry, K).items()):
+    entry = "w4a8_packed"
+    for gid, (M, N, K) in sorted(cases(bg, entry, [384]).items()):
         qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((M, K), 1.0, 9700 + gid))
         Bq, sE = inputs.quant_mxfp4_weights(inputs.normal_f32((K, N), 0.02, 9800 + gid))
         Ad, sAd = dev_u8(qA), dev_f32(sA)
@@ -131,8 +135,9 @@ def test_w4a8_table(bg):
 
 def test_tables_fully_reached(bg):
     # the search reaches every plain-call table entry (entry 8 of the packed
-    # bf16 table serves grouped calls only)
-    want = {"bf16": 2, "bf16_bt": 5, "bf16_packed": 14, "fp8": 4, "fp8_packed": 7, "fp4": 1,
+    # bf16 table and entries 6 and 7 of the packed fp8 table serve grouped
+    # calls only)
+    want = {"bf16": 2, "bf16_bt": 5, "bf16_packed": 14, "fp8": 4, "fp8_packed": 8, "fp4": 1,
             "fp4_packed": 6, "w4a8_packed": 11}
     for entry, n in want.items():
-        assert len(cases(bg, entry, 384)) == n, entry
+        assert len(cases(bg, entry, FP8_KS.get(entry, [384]))) == n, entry

@@ -127,23 +127,28 @@ def test_all_tokens_one_expert_and_subsets(bg, moe):
 
 def test_every_geometry(bg):
     # the mean rows per group picks the launch geometry; all give the same bits
-    E, K, N = 4, 256, 4096
-    qBs, sBs = experts(E, K, N, 2400)
-    Bd, Bp, sB = upload(bg, qBs, sBs)
-    single = [bg.pack_b_fp8(b) for b in Bd]
-    for M in (1, 2, 7, 9, 70, 100, 130, 250, 600, 1100):
-        qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((M, K), 1.0, 2410 + M))
-        expert = inputs.route_tokens(M, E, 2420 + M, 1.0)
-        order, offsets = inputs.group_by_expert(expert, E)
-        A, sAd = dev_u8(np.ascontiguousarray(qA[order])), dev_f32(np.ascontiguousarray(sA[order]))
-        C = host_codes(run(bg, A, sAd, offsets, Bp, sB))
-        geo = bg.geometry("fp8_grouped_packed", M, N, K, groups=E)
-        for e in range(E):
-            lo, hi = offsets[e], offsets[e + 1]
-            if hi > lo:
-                ref = host_codes(bg.gemm_fp8_blockscaled_packed(A[lo:hi], sAd[lo:hi], single[e],
-                                                                dev_f32(sBs[e])))
-                assert np.array_equal(C[lo:hi], ref), f"M={M} expert {e} geometry {geo}"
+    E, K = 4, 256
+    seen = set()
+    for N in (1024, 4096):
+        qBs, sBs = experts(E, K, N, 2400 + N)
+        Bd, Bp, sB = upload(bg, qBs, sBs)
+        single = [bg.pack_b_fp8(b) for b in Bd]
+        for M in (1, 2, 7, 9, 70, 100, 130, 250, 600, 1100):
+            qA, sA = inputs.quant_fp8_rowblocks(inputs.normal_f32((M, K), 1.0, 2410 + M))
+            expert = inputs.route_tokens(M, E, 2420 + M, 1.0)
+            order, offsets = inputs.group_by_expert(expert, E)
+            A, sAd = dev_u8(np.ascontiguousarray(qA[order])), dev_f32(np.ascontiguousarray(sA[order]))
+            C = host_codes(run(bg, A, sAd, offsets, Bp, sB))
+            geo = bg.geometry("fp8_grouped_packed", M, N, K, groups=E)
+            seen.add(geo["id"])
+            for e in range(E):
+                lo, hi = offsets[e], offsets[e + 1]
+                if hi > lo:
+                    ref = host_codes(bg.gemm_fp8_blockscaled_packed(A[lo:hi], sAd[lo:hi], single[e],
+                                                                    dev_f32(sBs[e])))
+                    assert np.array_equal(C[lo:hi], ref), f"N={N} M={M} expert {e} geometry {geo}"
+    # unstaged half and whole blocks, 16 x 32 and 16 x 64 tiles, a tiled entry
+    assert seen >= {2, 6, 7, 8, 9}, seen
 
 
 def test_malformed_offsets_stay_in_bounds(bg):
