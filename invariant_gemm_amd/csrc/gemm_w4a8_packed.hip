@@ -321,6 +321,157 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
     }
 }
 
+// Small-M variant without operand staging: one 16-row block, 16 columns (or
+// 8 with HALF: a workgroup owns 8 of a block's columns and feeds them to
+// both halves of the MFMA's columns, storing one) per workgroup.  The K
+// blocks are taken in rounds of R = WAVES*KPW; in a round, wave w loads the
+// A operands, weight codes and weight scales of blocks kb0 + w*KPW ..
+// + KPW-1 straight into its registers (the packed codes and scale bytes are
+// already in the MFMA's lane order), all loads issued before the first
+// MFMA, and forms each block's product P with the same scaled MFMA into a
+// zero accumulator.  The products go to LDS, and four waves -- one per
+// accumulator component -- fold them in ascending K order with the same
+// acc = fma(P, sA, acc), so every output element sees exactly the operations
+// of the staged kernel above.  Loads for the next round are issued before
+// the fold of the current one.  Blocks past K/128 in the last round are
+// loaded (codes and scales as zero outside their extents) but never folded.
+template <int WAVES, int KPW, bool HALF, bool GROUPED>
+__global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_direct_kernel(
+    int M, int N, int K,
+    const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t ldsa,
+    const uint8_t* __restrict__ Bp, uint16_t* __restrict__ C, int64_t ldc, int m_tiles,
+    const int32_t* __restrict__ offsets, int n_groups, int64_t b_stride)
+{
+    static_assert(WAVES >= 4, "four folding waves, one per accumulator component");
+    constexpr int NTHR = 64 * WAVES;
+    constexpr int R = WAVES * KPW;                    // K blocks per round
+    constexpr int SPT = (R * 16 + NTHR - 1) / NTHR;   // activation scales per thread and round
+    __shared__ float pbuf[R][4][64];                  // [block][component][lane]
+    __shared__ float sas[R][16];                      // sA of the tile's rows, block-major
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    const int ntile = tile / m_tiles;
+    const int mt = tile - ntile * m_tiles;
+    const int nb = HALF ? ntile >> 1 : ntile;
+    const int ch = HALF ? ntile & 1 : 0;
+    int m0 = mt * 16;
+    int row_end = M;
+    if constexpr (GROUPED) {
+        const int g = group_of_slot(offsets, n_groups, M, 16, mt, m0, row_end);
+        if (g == n_groups)
+            return;                                   // an unused slot (uniform per workgroup)
+        Bp += g * b_stride;
+    }
+    const int NB = (N + 15) >> 4;
+    const int nkb = K / KBK;
+    const uint8_t* scales = Bp + (int64_t)NB * nkb * CTILE;
+    const int rows_valid = row_end - m0 < 16 ? row_end - m0 : 16;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const uint32_t OOB = 0x80000000u;
+    // A operand of lane 16g + i: row i, K = 16g .. 16g+15 and 64+16g ..
+    // 64+16g+15 of the block; rows past the tile's valid rows read zero.
+    const uint32_t a_off = (uint32_t)(li * lda + 16 * lg);
+    // the packed lane whose column this lane computes (HALF: among the
+    // workgroup's 8), its 16 code bytes and its scale byte
+    const int src = HALF ? 16 * lg + 8 * ch + (li & 7) : lane;
+    const int q0 = wave * KPW;                        // the wave's first block in a round
+
+    u32x4 a[KPW][2], b[KPW];
+    uint32_t sc[KPW];
+    float sav[SPT];
+    auto issue = [&](int kb0) {
+        const bool col = nb < NB;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+            Bp + ((int64_t)nb * nkb + kb0) * CTILE, col ? clamp_bytes((int64_t)(nkb - kb0) * CTILE) : 0u);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+            scales + ((int64_t)nb * nkb + kb0) * STILE, col ? clamp_bytes((int64_t)(nkb - kb0) * STILE) : 0u);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+            A + (int64_t)m0 * lda + (int64_t)kb0 * KBK,
+            clamp_bytes((int64_t)(rows_valid - 1) * lda + K - (int64_t)kb0 * KBK));
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
+            sA + (int64_t)m0 * ldsa + kb0, clamp_bytes(((int64_t)(rows_valid - 1) * ldsa + nkb - kb0) * 4));
+#pragma unroll
+        for (int t = 0; t < KPW; ++t)
+            b[t] = buf_load16_nt(rb, (uint32_t)((q0 + t) * CTILE + src * 16));
+#pragma unroll
+        for (int t = 0; t < KPW; ++t)
+            sc[t] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)((q0 + t) * STILE + (src & ~3)), 0, 2);
+#pragma unroll
+        for (int t = 0; t < KPW; ++t) {
+            const uint32_t o = a_off + (uint32_t)(q0 + t) * KBK;
+            a[t][0] = buf_load16(ra, o);
+            a[t][1] = buf_load16(ra, o + 64);
+        }
+        // scale value u of the round: row u / R, block u % R
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int u = j * NTHR + tid;
+            const uint32_t o = u < R * 16 ? (uint32_t)(((u / R) * ldsa + u % R) * 4) : OOB;
+            sav[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)o, 0, 0));
+        }
+    };
+
+    float acc = 0.f;
+    // K = 0 issues no load at all: the extents above assume a live round
+    if (nkb > 0)
+        issue(0);
+    for (int kb0 = 0; kb0 < nkb; kb0 += R) {
+        // keep every load above issued before the first MFMA below waits
+        __builtin_amdgcn_sched_barrier(0);
+        if (kb0 + q0 < nkb) {
+#pragma unroll
+            for (int t = 0; t < KPW; ++t) {
+                const i32x8 av = {(int)a[t][0][0], (int)a[t][0][1], (int)a[t][0][2], (int)a[t][0][3],
+                                  (int)a[t][1][0], (int)a[t][1][1], (int)a[t][1][2], (int)a[t][1][3]};
+                // fp4 B occupies the first four dwords of the operand
+                const i32x8 bv = {(int)b[t][0], (int)b[t][1], (int)b[t][2], (int)b[t][3], 0, 0, 0, 0};
+                const int bsc = (int)((sc[t] >> (8 * (src & 3))) & 0xFFu);
+                // A fp8 e4m3 (format 0) with unit scale (E8M0 127); B fp4
+                // e2m1 (format 4) with the lane's MX block scale
+                const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, bsc);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    pbuf[q0 + t][j][lane] = P[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int u = j * NTHR + tid;
+            if (u < R * 16)
+                sas[u % R][u / R] = sav[j];
+        }
+        __syncthreads();
+        if (kb0 + R < nkb)
+            issue(kb0 + R);
+        if (wave < 4) {
+            // wave j folds component j: rows 4g + j of the block
+            const int nq = nkb - kb0 < R ? nkb - kb0 : R;
+            if (nq == R) {
+#pragma unroll
+                for (int q = 0; q < R; ++q)
+                    acc = __builtin_fmaf(pbuf[q][wave][lane], sas[q][4 * lg + wave], acc);
+            } else {
+#pragma unroll 8
+                for (int q = 0; q < nq; ++q)
+                    acc = __builtin_fmaf(pbuf[q][wave][lane], sas[q][4 * lg + wave], acc);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (wave < 4) {
+        const int row = m0 + 4 * lg + wave;
+        const int col = HALF ? 16 * nb + 8 * ch + li : 16 * nb + li;
+        if (row < row_end && col < N && (!HALF || li < 8))
+            C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc);
+    }
+}
+
 // Packer: one thread per (nb, kb, lane) writes the lane's 16 code bytes and
 // its scale byte.
 __global__ void pack_mxfp4_kernel(int N, int K, const uint8_t* __restrict__ Bq, int64_t ldbq,
@@ -353,11 +504,15 @@ __global__ void pack_mxfp4_kernel(int N, int K, const uint8_t* __restrict__ Bq, 
 
 // One launch geometry: WAVES waves, RB x CB MFMA blocks split among the
 // waves as WR x WC sub-tiles, KB_ST K blocks per stage, PF stages in flight,
-// non-temporal weight loads, AR staged A rows.
+// non-temporal weight loads, AR staged A rows; KPW > 0 selects the unstaged
+// kernel (one 16-row block, KPW K blocks per wave and round), on half blocks
+// with HALF.
 struct Cfg {
     int waves, rb, cb, wr, wc, kb_st, pf;
     bool nt;
     int ar;
+    int kpw = 0;
+    bool half = false;
 };
 
 // The geometry table.  Every entry runs the same per-element arithmetic.
@@ -369,14 +524,14 @@ constexpr Cfg kCfg[] = {
     /* 4 */ {8, 4, 4, 2, 2, 4, 2, true, 64},    // 64 x 64, eight waves (four only load), four K blocks per stage
     /* 5 */ {4, 2, 4, 1, 2, 4, 2, true, 32},    // 32 x 64, four waves of 16 x 32, four K blocks per stage
     /* 6 */ {4, 4, 8, 2, 4, 1, 2, false, 64},   // 64 x 128, four waves of 32 x 64, weights shared
-    /* 7 */ {1, 1, 1, 1, 1, 4, 2, true, 16},    // 16 x 16, one wave (narrow weights)
-    /* 8 */ {2, 1, 2, 1, 1, 4, 2, true, 16},    // 16 x 32, two waves (narrow weights)
-    /* 9 */ {1, 1, 1, 1, 1, 4, 2, true, 8},     //   16 x 16, 8 rows of A staged
-    /* 10 */ {2, 1, 2, 1, 1, 4, 2, true, 8},    //   16 x 32, 8 rows of A staged
+    /* 7 */ {2, 1, 2, 1, 1, 4, 2, true, 16},    // 16 x 32, two waves (narrow weights)
+    /* 8 */ {2, 1, 2, 1, 1, 4, 2, true, 8},     //   the same, 8 rows of A staged
+    /* 9 */ {8, 1, 1, 1, 1, 0, 1, true, 16, 7},        // 16 x 16, unstaged, 56 K blocks a round
+    /* 10 */ {8, 1, 1, 1, 1, 0, 1, true, 16, 7, true}, // 16 x 8 half blocks, unstaged
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
-int64_t n_tiles_of(const Cfg& c, int64_t N) { return ceil_div(ceil_div(N, 16), c.cb); }
+int64_t n_tiles_of(const Cfg& c, int64_t N) { return ceil_div(ceil_div(N, 16), c.cb) * (c.half ? 2 : 1); }
 
 // Row slots of a grouped call: at most k = min(groups, M) groups hold rows,
 // and sum ceil(r_g / BM) <= floor((M + k (BM - 1)) / BM) -- one slot at M = 1.
@@ -395,10 +550,10 @@ Geometry describe(int id, int64_t M, int64_t N, int64_t groups = 0)
     Geometry g;
     g.id = id;
     g.bm = 16 * c.rb;
-    g.bn = 16 * c.cb;
+    g.bn = c.half ? 8 : 16 * c.cb;
     g.waves = c.waves;
     g.a_rows = c.ar;
-    g.k_stage = c.kb_st * KBK;
+    g.k_stage = (c.kpw > 0 ? c.waves * c.kpw : c.kb_st) * KBK;
     g.stages = c.pf;
     g.workgroups = n_tiles_of(c, N) * m_tiles_of(c, M, groups);
     return g;
@@ -412,16 +567,27 @@ hipError_t launch_cfg(const GemmArgs& a, const GroupArgs* grp, const Geometry& g
         return hipErrorInvalidConfiguration;
     const int m_tiles = (int)m_tiles_of(c, a.M, grp ? grp->n_groups : 0);
     const dim3 grid((unsigned)g.workgroups), block(64 * c.waves);
-    if (grp)
-        gemm_w4a8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.nt, c.ar, true>
-            <<<grid, block, 0, stream>>>(
+    if constexpr (c.kpw > 0) {
+        if (grp)
+            gemm_w4a8_packed_direct_kernel<c.waves, c.kpw, c.half, true><<<grid, block, 0, stream>>>(
                 a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
                 (const uint8_t*)a.B, a.C, a.ldc, m_tiles, grp->offsets, grp->n_groups, grp->b_stride);
-    else
-        gemm_w4a8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.nt, c.ar, false>
-            <<<grid, block, 0, stream>>>(
+        else
+            gemm_w4a8_packed_direct_kernel<c.waves, c.kpw, c.half, false><<<grid, block, 0, stream>>>(
                 a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
                 (const uint8_t*)a.B, a.C, a.ldc, m_tiles, nullptr, 0, 0);
+    } else {
+        if (grp)
+            gemm_w4a8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.nt, c.ar, true>
+                <<<grid, block, 0, stream>>>(
+                    a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
+                    (const uint8_t*)a.B, a.C, a.ldc, m_tiles, grp->offsets, grp->n_groups, grp->b_stride);
+        else
+            gemm_w4a8_packed_kernel<c.waves, c.rb, c.cb, c.wr, c.wc, c.kb_st, c.pf, c.nt, c.ar, false>
+                <<<grid, block, 0, stream>>>(
+                    a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
+                    (const uint8_t*)a.B, a.C, a.ldc, m_tiles, nullptr, 0, 0);
+    }
     return hipGetLastError();
 }
 
@@ -444,35 +610,51 @@ hipError_t launch_id(const GemmArgs& a, const GroupArgs* grp, const Geometry& g,
 }
 static_assert(kNumCfg == 11, "every table entry needs its case in launch_id");
 
-// The 16-row geometry for calls of at most 16 rows per group: 16 x 64 tiles
-// of four waves where `slots` x N/64 tiles fill the compute units in one
-// round; for narrower weights the narrowest of 16 x 16 (one wave) and 16 x 32
-// (two waves) whose tiles still fit in one round, so that narrow weights keep
-// more compute units streaming; each with 8 rows of A staged when the whole
-// call has at most 8 rows.  Two stages in flight (against four: K = 4096,
-// N = 14336, M = 1 9.2 -> 8.7 us; K = 7168, N = 2048, M = 1 on one-wave
-// 16 x 16 tiles 11.9 -> about 10.5 us).
+// 16-row tiles of the unstaged kernel while `slots` row slots of them fit on
+// the compute units in one round -- on half blocks while twice as many still
+// fit -- else -1.  Against the staged narrow tiles: K = 7168, N = 2048,
+// M = 1 10.5 -> 6.1 us, M = 16 11.6 -> 7.1 us, M = 32 15.2 -> 7.5 us;
+// N = 4096, M = 1 11.0 -> 6.7 us; N = 1024, M = 1 10.6 -> 5.5 us; grouped
+// over 8 experts at N = 2048, one token 11.0 -> 5.5 us, two 11.8 -> 6.6 us.
+// Past one round the staged tiles win (N = 8192, M = 16: 8.0 against 12.9).
+int unstaged_id(int64_t N, int64_t slots)
+{
+    const int64_t nb = ceil_div(N, 16);
+    if (slots * nb > 256)
+        return -1;
+    return 2 * slots * nb <= 256 ? 10 : 9;
+}
+
+// The 16-row geometry for calls of at most 16 rows per group: the unstaged
+// kernel where it fits in one round; else 16 x 64 tiles of four waves where
+// `slots` x N/64 tiles fill the compute units in one round, or for narrower
+// weights 16 x 32 tiles of two waves, so that narrow weights keep more
+// compute units streaming; each with 8 rows of A staged when the whole call
+// has at most 8 rows.  Two stages in flight (against four: K = 4096,
+// N = 14336, M = 1 9.2 -> 8.7 us).
 int narrow_rows_id(int64_t M, int64_t N, int64_t slots)
 {
+    const int u = unstaged_id(N, slots);
+    if (u >= 0)
+        return u;
     const bool few = M <= 8;
-    if (slots * n_tiles_of(kCfg[0], N) >= 256 || slots * n_tiles_of(kCfg[8], N) > 256)
+    if (slots * n_tiles_of(kCfg[0], N) >= 256 || slots * n_tiles_of(kCfg[7], N) > 256)
         return few ? 1 : 0;
-    if (slots * n_tiles_of(kCfg[7], N) <= 256)
-        return few ? 9 : 7;
-    return few ? 10 : 8;
+    return few ? 8 : 7;
 }
 
 }  // namespace
 
 // Launch geometry (tile sharing only; the per-element arithmetic is the same
 // for all), from a sweep on the K = 4096, N = 14336 weight shape: for
-// M <= 16 four waves each stream their own 16-column block and share one
-// staged activation tile (of which only the first 8 rows are loaded when the
-// call has no more: LDS rows past them keep stale bytes, which reach only
-// output rows that are never stored, an MFMA output row depending on its own
-// A row alone).  Up to 32 rows, 32 x 64 tiles on four waves while they fit
-// on the compute units in one round (M = 17 16.0 -> 11.0 us, M = 32 16.2 ->
-// 11.2 us); above that 64 x 64 tiles: while they fit in one round, eight
+// M <= 16 (narrow weights aside: the unstaged kernel, above) four waves each
+// stream their own 16-column block and share one staged activation tile (of
+// which only the first 8 rows are loaded when the call has no more: LDS rows
+// past them keep stale bytes, which reach only output rows that are never
+// stored, an MFMA output row depending on its own A row alone).  Up to 32
+// rows, the unstaged kernel on two 16-row slots where they fit in one round,
+// else 32 x 64 tiles on four waves while they fit on the compute units in
+// one round (M = 17 16.0 -> 11.0 us, M = 32 16.2 -> 11.2 us); above that 64 x 64 tiles: while they fit in one round, eight
 // waves of which four only load, four K blocks per stage (M = 64 16.1 ->
 // 14.7 us); past one round four waves, with one K block per stage once
 // M > 128 (the eight-wave version measured 20-30 % slower there); above 192
@@ -487,6 +669,8 @@ Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K)
     int id;
     if (M <= 16)
         id = narrow_rows_id(M, N, 1);
+    else if (M <= 32 && unstaged_id(N, ceil_div(M, 16)) >= 0)
+        id = unstaged_id(N, ceil_div(M, 16));
     else if (M <= 32 && ceil_div(M, 32) * col_tiles <= 256)
         id = 5;
     else if (ceil_div(M, 64) * col_tiles <= 256)
@@ -506,9 +690,9 @@ hipError_t launch_w4a8_packed(const GemmArgs& a, hipStream_t stream)
 // Grouped calls: the tiles must cover every group's rows, so the grid holds
 // sum over groups of ceil(rows / BM) row slots per column tile (bounded by
 // m_tiles_of; slots past the occupied ones exit at once).  While the groups
-// average at most 16 rows, 16 x 64 tiles (the 8-row variant only when the
-// whole call has at most 8 rows, all of which may fall into one group);
-// otherwise the smallest of 32 x 64 and 64 x 64 (eight waves) whose grid
+// average at most 16 rows, the 16-row geometry above for the occupied slots,
+// min(groups, M) (the 8-row variant only when the whole call has at most 8
+// rows, all of which may fall into one group); otherwise the smallest of 32 x 64 and 64 x 64 (eight waves) whose grid
 // fits in one round, else 64 x 64 on four waves.
 Geometry geometry_w4a8_grouped(int64_t M, int64_t N, int64_t K, int64_t groups)
 {
