@@ -712,11 +712,12 @@ def pmc_summary(fetch_dir: str, write_dir: str):
 
 
 def legs_pmc():
-    """(name, kernel, workload class, M sweep, algorithmic bytes) of the
-    quantised legs whose HBM traffic the counters check."""
-    return (("fp8_blockscaled_packed_K7168_N2048", "gemm_fp8_packed_kernel", C3P, SWEEP_C3, bytes_fp8),
-            ("fp4_weight_only_packed_K4096_N14336", "gemm_fp4_packed_kernel", C4P, SWEEP_C4, bytes_fp4),
-            ("w4a8_mxfp4_K4096_N14336", "gemm_w4a8_packed_kernel", W4A8, W4A8.SWEEP, bytes_w4a8))
+    """(name, kernel name prefix, workload class, M sweep, algorithmic bytes)
+    of the quantised legs whose HBM traffic the counters check (the prefix
+    matches a format's staged and unstaged kernels alike)."""
+    return (("fp8_blockscaled_packed_K7168_N2048", "gemm_fp8_packed_", C3P, SWEEP_C3, bytes_fp8),
+            ("fp4_weight_only_packed_K4096_N14336", "gemm_fp4_packed_", C4P, SWEEP_C4, bytes_fp4),
+            ("w4a8_mxfp4_K4096_N14336", "gemm_w4a8_packed_", W4A8, W4A8.SWEEP, bytes_w4a8))
 
 
 def pmc_probe_legs(torch, bg, inputs):
