@@ -321,32 +321,36 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_kernel(
     }
 }
 
-// Small-M variant without operand staging: one 16-row block, 16 columns (or
-// 8 with HALF: a workgroup owns 8 of a block's columns and feeds them to
-// both halves of the MFMA's columns, storing one) per workgroup.  The K
-// blocks are taken in rounds of R = WAVES*KPW; in a round, wave w loads the
-// A operands, weight codes and weight scales of blocks kb0 + w*KPW ..
-// + KPW-1 straight into its registers (the packed codes and scale bytes are
-// already in the MFMA's lane order), all loads issued before the first
-// MFMA, and forms each block's product P with the same scaled MFMA into a
-// zero accumulator.  The products go to LDS, and four waves -- one per
-// accumulator component -- fold them in ascending K order with the same
-// acc = fma(P, sA, acc), so every output element sees exactly the operations
-// of the staged kernel above.  Loads for the next round are issued before
-// the fold of the current one.  Blocks past K/128 in the last round are
-// loaded (codes and scales as zero outside their extents) but never folded.
-template <int WAVES, int KPW, bool HALF, bool GROUPED>
+// Small-M variant without operand staging: one 16-row block and CB column
+// blocks of 16 (or, HALF, 8 columns: a workgroup owns 8 of a block's
+// columns and feeds them to both halves of the MFMA's columns, storing one)
+// per workgroup.  The K blocks are taken in rounds of R = WAVES*KPW; in a
+// round, wave w loads the A operands, weight codes and weight scales of
+// blocks kb0 + w*KPW .. + KPW-1 straight into its registers (the packed
+// codes and scale bytes are already in the MFMA's lane order), all loads
+// issued before the first MFMA, and forms each block's product P with the
+// same scaled MFMA into a zero accumulator.  The products go to LDS, and the
+// waves -- each owning accumulator components of the tile's column blocks --
+// fold them in ascending K order with the same acc = fma(P, sA, acc), so
+// every output element sees exactly the operations of the staged kernel
+// above.  Loads for the next round are issued before the fold of the
+// current one.  Blocks past K/128 in the last round are loaded (codes and
+// scales as zero outside their extents) but never folded.
+template <int WAVES, int KPW, int CB, bool HALF, bool GROUPED>
 __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_direct_kernel(
     int M, int N, int K,
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t ldsa,
     const uint8_t* __restrict__ Bp, uint16_t* __restrict__ C, int64_t ldc, int m_tiles,
     const int32_t* __restrict__ offsets, int n_groups, int64_t b_stride)
 {
-    static_assert(WAVES >= 4, "four folding waves, one per accumulator component");
     constexpr int NTHR = 64 * WAVES;
     constexpr int R = WAVES * KPW;                    // K blocks per round
     constexpr int SPT = (R * 16 + NTHR - 1) / NTHR;   // activation scales per thread and round
-    __shared__ float pbuf[R][4][64];                  // [block][component][lane]
+    constexpr int FOLDS = 4 * CB;                     // (column block, component) chains
+    constexpr int FPW = (FOLDS + WAVES - 1) / WAVES;  // chains per wave
+    static_assert(!HALF || CB == 1, "half blocks: one column block");
+    static_assert(FOLDS % WAVES == 0 || FOLDS < WAVES, "chains split evenly over the folding waves");
+    __shared__ float pbuf[R][CB][4][64];              // [block][column block][component][lane]
     __shared__ float sas[R][16];                      // sA of the tile's rows, block-major
 
     const int tid = threadIdx.x;
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_direct_kernel(
     const int tile = xcd_remap(blockIdx.x, gridDim.x);
     const int ntile = tile / m_tiles;
     const int mt = tile - ntile * m_tiles;
-    const int nb = HALF ? ntile >> 1 : ntile;
+    const int nb0 = HALF ? ntile >> 1 : ntile * CB;   // the tile's first column block
     const int ch = HALF ? ntile & 1 : 0;
     int m0 = mt * 16;
     int row_end = M;
@@ -380,26 +384,36 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_direct_kernel(
     const int src = HALF ? 16 * lg + 8 * ch + (li & 7) : lane;
     const int q0 = wave * KPW;                        // the wave's first block in a round
 
-    u32x4 a[KPW][2], b[KPW];
-    uint32_t sc[KPW];
+    u32x4 a[KPW][2], b[KPW][CB];
+    uint32_t sc[KPW][CB];
     float sav[SPT];
     auto issue = [&](int kb0) {
-        const bool col = nb < NB;
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(
-            Bp + ((int64_t)nb * nkb + kb0) * CTILE, col ? clamp_bytes((int64_t)(nkb - kb0) * CTILE) : 0u);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(
-            scales + ((int64_t)nb * nkb + kb0) * STILE, col ? clamp_bytes((int64_t)(nkb - kb0) * STILE) : 0u);
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(
             A + (int64_t)m0 * lda + (int64_t)kb0 * KBK,
             clamp_bytes((int64_t)(rows_valid - 1) * lda + K - (int64_t)kb0 * KBK));
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
             sA + (int64_t)m0 * ldsa + kb0, clamp_bytes(((int64_t)(rows_valid - 1) * ldsa + nkb - kb0) * 4));
 #pragma unroll
-        for (int t = 0; t < KPW; ++t)
-            b[t] = buf_load16_nt(rb, (uint32_t)((q0 + t) * CTILE + src * 16));
+        for (int c = 0; c < CB; ++c) {
+            // column blocks past N read zero (empty extents)
+            const int nb = nb0 + c;
+            const bool col = nb < NB;
+            const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+                Bp + ((int64_t)nb * nkb + kb0) * CTILE, col ? clamp_bytes((int64_t)(nkb - kb0) * CTILE) : 0u);
 #pragma unroll
-        for (int t = 0; t < KPW; ++t)
-            sc[t] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)((q0 + t) * STILE + (src & ~3)), 0, 2);
+            for (int t = 0; t < KPW; ++t)
+                b[t][c] = buf_load16_nt(rb, (uint32_t)((q0 + t) * CTILE + src * 16));
+        }
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            const int nb = nb0 + c;
+            const bool col = nb < NB;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+                scales + ((int64_t)nb * nkb + kb0) * STILE, col ? clamp_bytes((int64_t)(nkb - kb0) * STILE) : 0u);
+#pragma unroll
+            for (int t = 0; t < KPW; ++t)
+                sc[t][c] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)((q0 + t) * STILE + (src & ~3)), 0, 2);
+        }
 #pragma unroll
         for (int t = 0; t < KPW; ++t) {
             const uint32_t o = a_off + (uint32_t)(q0 + t) * KBK;
@@ -415,7 +429,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_direct_kernel(
         }
     };
 
-    float acc = 0.f;
+    float acc[FPW];
+#pragma unroll
+    for (int f = 0; f < FPW; ++f)
+        acc[f] = 0.f;
     // K = 0 issues no load at all: the extents above assume a live round
     if (nkb > 0)
         issue(0);
@@ -427,16 +444,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_direct_kernel(
             for (int t = 0; t < KPW; ++t) {
                 const i32x8 av = {(int)a[t][0][0], (int)a[t][0][1], (int)a[t][0][2], (int)a[t][0][3],
                                   (int)a[t][1][0], (int)a[t][1][1], (int)a[t][1][2], (int)a[t][1][3]};
-                // fp4 B occupies the first four dwords of the operand
-                const i32x8 bv = {(int)b[t][0], (int)b[t][1], (int)b[t][2], (int)b[t][3], 0, 0, 0, 0};
-                const int bsc = (int)((sc[t] >> (8 * (src & 3))) & 0xFFu);
-                // A fp8 e4m3 (format 0) with unit scale (E8M0 127); B fp4
-                // e2m1 (format 4) with the lane's MX block scale
-                const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, bsc);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    pbuf[q0 + t][j][lane] = P[j];
+                for (int c = 0; c < CB; ++c) {
+                    // fp4 B occupies the first four dwords of the operand
+                    const i32x8 bv = {(int)b[t][c][0], (int)b[t][c][1], (int)b[t][c][2], (int)b[t][c][3],
+                                      0, 0, 0, 0};
+                    const int bsc = (int)((sc[t][c] >> (8 * (src & 3))) & 0xFFu);
+                    // A fp8 e4m3 (format 0) with unit scale (E8M0 127); B fp4
+                    // e2m1 (format 4) with the lane's MX block scale
+                    const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 4, 0, 127, 0, bsc);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pbuf[q0 + t][c][j][lane] = P[j];
+                }
             }
         }
 #pragma unroll
@@ -448,27 +469,38 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_w4a8_packed_direct_kernel(
         __syncthreads();
         if (kb0 + R < nkb)
             issue(kb0 + R);
-        if (wave < 4) {
-            // wave j folds component j: rows 4g + j of the block
-            const int nq = nkb - kb0 < R ? nkb - kb0 : R;
-            if (nq == R) {
+        // chain f of this wave: column block (wave + f*WAVES) / 4, component
+        // (wave + f*WAVES) % 4, i.e. rows 4g + component of the block
+        const int nq = nkb - kb0 < R ? nkb - kb0 : R;
 #pragma unroll
-                for (int q = 0; q < R; ++q)
-                    acc = __builtin_fmaf(pbuf[q][wave][lane], sas[q][4 * lg + wave], acc);
-            } else {
+        for (int f = 0; f < FPW; ++f) {
+            const int chain = wave + f * WAVES;
+            if (chain < FOLDS) {
+                const int c = chain >> 2, j = chain & 3;
+                if (nq == R) {
+#pragma unroll
+                    for (int q = 0; q < R; ++q)
+                        acc[f] = __builtin_fmaf(pbuf[q][c][j][lane], sas[q][4 * lg + j], acc[f]);
+                } else {
 #pragma unroll 8
-                for (int q = 0; q < nq; ++q)
-                    acc = __builtin_fmaf(pbuf[q][wave][lane], sas[q][4 * lg + wave], acc);
+                    for (int q = 0; q < nq; ++q)
+                        acc[f] = __builtin_fmaf(pbuf[q][c][j][lane], sas[q][4 * lg + j], acc[f]);
+                }
             }
         }
         __syncthreads();
     }
 
-    if (wave < 4) {
-        const int row = m0 + 4 * lg + wave;
-        const int col = HALF ? 16 * nb + 8 * ch + li : 16 * nb + li;
-        if (row < row_end && col < N && (!HALF || li < 8))
-            C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc);
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) {
+        const int chain = wave + f * WAVES;
+        if (chain < FOLDS) {
+            const int c = chain >> 2, j = chain & 3;
+            const int row = m0 + 4 * lg + j;
+            const int col = HALF ? 16 * nb0 + 8 * ch + li : 16 * (nb0 + c) + li;
+            if (row < row_end && col < N && (!HALF || li < 8))
+                C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc[f]);
+        }
     }
 }
 
@@ -524,10 +556,9 @@ constexpr Cfg kCfg[] = {
     /* 4 */ {8, 4, 4, 2, 2, 4, 2, true, 64},    // 64 x 64, eight waves (four only load), four K blocks per stage
     /* 5 */ {4, 2, 4, 1, 2, 4, 2, true, 32},    // 32 x 64, four waves of 16 x 32, four K blocks per stage
     /* 6 */ {4, 4, 8, 2, 4, 1, 2, false, 64},   // 64 x 128, four waves of 32 x 64, weights shared
-    /* 7 */ {2, 1, 2, 1, 1, 4, 2, true, 16},    // 16 x 32, two waves (narrow weights)
-    /* 8 */ {2, 1, 2, 1, 1, 4, 2, true, 8},     //   the same, 8 rows of A staged
-    /* 9 */ {8, 1, 1, 1, 1, 0, 1, true, 16, 7},        // 16 x 16, unstaged, 56 K blocks a round
-    /* 10 */ {8, 1, 1, 1, 1, 0, 1, true, 16, 7, true}, // 16 x 8 half blocks, unstaged
+    /* 7 */ {8, 1, 1, 1, 1, 0, 1, true, 16, 7},        // 16 x 16, unstaged, 56 K blocks a round
+    /* 8 */ {8, 1, 1, 1, 1, 0, 1, true, 16, 7, true},  // 16 x 8 half blocks, unstaged
+    /* 9 */ {8, 1, 2, 1, 1, 0, 1, true, 16, 4},        // 16 x 32, unstaged, 32 K blocks a round
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -569,11 +600,11 @@ hipError_t launch_cfg(const GemmArgs& a, const GroupArgs* grp, const Geometry& g
     const dim3 grid((unsigned)g.workgroups), block(64 * c.waves);
     if constexpr (c.kpw > 0) {
         if (grp)
-            gemm_w4a8_packed_direct_kernel<c.waves, c.kpw, c.half, true><<<grid, block, 0, stream>>>(
+            gemm_w4a8_packed_direct_kernel<c.waves, c.kpw, c.cb, c.half, true><<<grid, block, 0, stream>>>(
                 a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
                 (const uint8_t*)a.B, a.C, a.ldc, m_tiles, grp->offsets, grp->n_groups, grp->b_stride);
         else
-            gemm_w4a8_packed_direct_kernel<c.waves, c.kpw, c.half, false><<<grid, block, 0, stream>>>(
+            gemm_w4a8_packed_direct_kernel<c.waves, c.kpw, c.cb, c.half, false><<<grid, block, 0, stream>>>(
                 a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
                 (const uint8_t*)a.B, a.C, a.ldc, m_tiles, nullptr, 0, 0);
     } else {
@@ -604,57 +635,59 @@ hipError_t launch_id(const GemmArgs& a, const GroupArgs* grp, const Geometry& g,
     case 7: return launch_cfg<7>(a, grp, g, stream);
     case 8: return launch_cfg<8>(a, grp, g, stream);
     case 9: return launch_cfg<9>(a, grp, g, stream);
-    case 10: return launch_cfg<10>(a, grp, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 11, "every table entry needs its case in launch_id");
+static_assert(kNumCfg == 10, "every table entry needs its case in launch_id");
 
-// 16-row tiles of the unstaged kernel while `slots` row slots of them fit on
-// the compute units in one round -- on half blocks while twice as many still
-// fit -- else -1.  Against the staged narrow tiles: K = 7168, N = 2048,
-// M = 1 10.5 -> 6.1 us, M = 16 11.6 -> 7.1 us, M = 32 15.2 -> 7.5 us;
-// N = 4096, M = 1 11.0 -> 6.7 us; N = 1024, M = 1 10.6 -> 5.5 us; grouped
-// over 8 experts at N = 2048, one token 11.0 -> 5.5 us, two 11.8 -> 6.6 us.
-// Past one round the staged tiles win (N = 8192, M = 16: 8.0 against 12.9).
-int unstaged_id(int64_t N, int64_t slots)
+// 16-row tiles of the unstaged kernel: the narrowest of 8 (half blocks), 16
+// and 32 columns whose `slots` row slots fit on the compute units in one
+// round -- for a single slot of at most 8 rows 32 columns also in two
+// rounds -- else -1.  Against the staged tiles: K = 7168, N = 2048, M = 1
+// 10.5 -> 5.3 us, M = 32 15.2 -> 7.3 us; N = 4096, M = 1 11.0 -> 6.7 us;
+// K = 4096, N = 8192, M = 1 7.5 -> 5.8 us, M = 16 8.0 -> 6.5 us;
+// N = 14336, M = 1 8.9 -> 8.0 us, M = 8 9.3 -> 8.6 us (448 workgroups;
+// M = 16 9.2 against 9.7 us stays staged); grouped over 8 experts at
+// N = 2048, one token 11.0 -> 5.5 us, two 11.8 -> 6.6 us.
+int unstaged_id(int64_t N, int64_t slots, bool few)
 {
     const int64_t nb = ceil_div(N, 16);
-    if (slots * nb > 256)
-        return -1;
-    return 2 * slots * nb <= 256 ? 10 : 9;
+    if (2 * slots * nb <= 256)
+        return 8;
+    if (slots * nb <= 256)
+        return 7;
+    const int64_t t32 = slots * ceil_div(nb, 2);
+    if (t32 <= 256 || (few && slots == 1 && t32 <= 512))
+        return 9;
+    return -1;
 }
 
 // The 16-row geometry for calls of at most 16 rows per group: the unstaged
-// kernel where it fits in one round; else 16 x 64 tiles of four waves where
-// `slots` x N/64 tiles fill the compute units in one round, or for narrower
-// weights 16 x 32 tiles of two waves, so that narrow weights keep more
-// compute units streaming; each with 8 rows of A staged when the whole call
-// has at most 8 rows.  Two stages in flight (against four: K = 4096,
-// N = 14336, M = 1 9.2 -> 8.7 us).
+// kernel where it fits (above); else 16 x 64 tiles of four waves, with 8
+// rows of A staged when the whole call has at most 8 rows.  Two stages in
+// flight (against four: K = 4096, N = 14336, M = 1 9.2 -> 8.7 us).
 int narrow_rows_id(int64_t M, int64_t N, int64_t slots)
 {
-    const int u = unstaged_id(N, slots);
+    const bool few = M <= 8;
+    const int u = unstaged_id(N, slots, few);
     if (u >= 0)
         return u;
-    const bool few = M <= 8;
-    if (slots * n_tiles_of(kCfg[0], N) >= 256 || slots * n_tiles_of(kCfg[7], N) > 256)
-        return few ? 1 : 0;
-    return few ? 8 : 7;
+    return few ? 1 : 0;
 }
 
 }  // namespace
 
 // Launch geometry (tile sharing only; the per-element arithmetic is the same
 // for all), from a sweep on the K = 4096, N = 14336 weight shape: for
-// M <= 16 (narrow weights aside: the unstaged kernel, above) four waves each
-// stream their own 16-column block and share one staged activation tile (of
-// which only the first 8 rows are loaded when the call has no more: LDS rows
-// past them keep stale bytes, which reach only output rows that are never
-// stored, an MFMA output row depending on its own A row alone).  Up to 32
-// rows, the unstaged kernel on two 16-row slots where they fit in one round,
-// else 32 x 64 tiles on four waves while they fit on the compute units in
-// one round (M = 17 16.0 -> 11.0 us, M = 32 16.2 -> 11.2 us); above that 64 x 64 tiles: while they fit in one round, eight
+// M <= 16 the unstaged kernel where it fits (above), else four waves each
+// streaming their own 16-column block and sharing one staged activation
+// tile (of which only the first 8 rows are loaded when the call has no
+// more: LDS rows past them keep stale bytes, which reach only output rows
+// that are never stored, an MFMA output row depending on its own A row
+// alone).  Up to 32 rows, the unstaged kernel on two 16-row slots where they
+// fit in one round, else 32 x 64 tiles on four waves while they fit on the
+// compute units in one round (M = 17 16.0 -> 11.0 us, M = 32 16.2 ->
+// 11.2 us); above that 64 x 64 tiles: while they fit in one round, eight
 // waves of which four only load, four K blocks per stage (M = 64 16.1 ->
 // 14.7 us); past one round four waves, with one K block per stage once
 // M > 128 (the eight-wave version measured 20-30 % slower there); above 192
@@ -669,8 +702,8 @@ Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K)
     int id;
     if (M <= 16)
         id = narrow_rows_id(M, N, 1);
-    else if (M <= 32 && unstaged_id(N, ceil_div(M, 16)) >= 0)
-        id = unstaged_id(N, ceil_div(M, 16));
+    else if (M <= 32 && unstaged_id(N, ceil_div(M, 16), false) >= 0)
+        id = unstaged_id(N, ceil_div(M, 16), false);
     else if (M <= 32 && ceil_div(M, 32) * col_tiles <= 256)
         id = 5;
     else if (ceil_div(M, 64) * col_tiles <= 256)

@@ -151,7 +151,7 @@ def test_every_geometry(bg):
                     ref = host_codes(bg.gemm_w4a8_packed(A[lo:hi], sAd[lo:hi], single[e]))
                     assert np.array_equal(C[lo:hi], ref), f"N={N} M={M} expert {e} geometry {geo}"
     # every entry but the 64 x 128 tiles (large M only), unstaged ones included
-    assert seen >= {0, 1, 2, 3, 4, 5, 7, 8, 9, 10}, seen
+    assert seen >= {0, 1, 2, 3, 4, 5, 7, 8, 9}, seen
 
 
 def test_malformed_offsets_stay_in_bounds(bg):

@@ -19,7 +19,7 @@ from tests.gpu_util import check_parity, dev_f32, dev_u8, host_codes, require_gp
 pytestmark = pytest.mark.gpu
 
 UNSTAGED_FP8 = {8, 9}        # packed fp8 table: unstaged half / whole blocks
-UNSTAGED_W4A8 = {9, 10}      # packed W4A8 table: unstaged whole / half blocks
+UNSTAGED_W4A8 = {7, 8, 9}    # packed W4A8 table: unstaged 16, 8 (half) and 32 columns
 
 
 @pytest.fixture(scope="module")
@@ -58,9 +58,11 @@ def test_fp8_rounds(bg, M, N, K):
     assert np.array_equal(got, rowmajor)
 
 
-# narrow weights (the unstaged kernel where its tiles fit in one round of
-# workgroups): half blocks, whole blocks, and two 16-row slots
-W4A8_CASES = [(1, 1024, 7296), (16, 2048, 14464), (32, 2048, 7296), (7, 4096, 21504)]
+# the unstaged kernel on half blocks, whole blocks (two 16-row slots among
+# them) and 32-column tiles (32 K blocks a round; a few rows over wide
+# weights, and two slots)
+W4A8_CASES = [(1, 1024, 7296), (16, 2048, 14464), (32, 2048, 7296), (7, 4096, 21504),
+              (4, 14336, 7296), (24, 4096, 7296)]
 
 
 @pytest.mark.parametrize("M,N,K", W4A8_CASES)
