@@ -270,6 +270,167 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_kernel(
     }
 }
 
+// Small-M variant without operand staging: one 16-row block and CB column
+// blocks of 16 per workgroup.  The 32-K steps are taken in rounds of
+// R = WAVES*KPW 128-K groups; in a round, wave w loads the codes, scales and
+// activations of groups kq0 + w*KPW .. + KPW-1 straight into its registers
+// (the packed codes are already in the MFMA's lane order) and forms each
+// step's product P = mfma(A, e2m1 -> bf16, 0) as above; the products and the
+// steps' scales go to LDS, and the waves -- each owning (column block,
+// component) chains -- fold them in ascending K order with the same
+// acc = fma(P, scale, acc), so every output element sees exactly the
+// operations of the staged kernel.  Two register sets: the loads of the
+// round after next are issued as soon as a round's MFMAs are done, so two
+// rounds are always in flight.  Steps past K/32 are loaded (codes and scales
+// as zero outside their extents) but never folded.
+template <int WAVES, int KPW, int CB>
+__global__ __launch_bounds__(64 * WAVES) void gemm_fp4_packed_direct_kernel(
+    int M, int N, int K,
+    const uint16_t* __restrict__ A, int64_t lda,
+    const uint8_t* __restrict__ Bp,
+    uint16_t* __restrict__ C, int64_t ldc, int m_tiles)
+{
+    constexpr int R = WAVES * KPW;                    // 128-K groups per round
+    constexpr int RS = 4 * R;                         // 32-K steps per round
+    constexpr int FOLDS = 4 * CB;                     // (column block, component) chains
+    constexpr int FPW = (FOLDS + WAVES - 1) / WAVES;  // chains per wave
+    static_assert(FOLDS % WAVES == 0 || FOLDS < WAVES, "chains split evenly over the folding waves");
+    __shared__ float pbuf[RS][CB][4][64];             // [step][column block][component][lane]
+    __shared__ float sbuf[RS][CB][16];                // [step][column block][column]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    const int ntile = tile / m_tiles;
+    const int mt = tile - ntile * m_tiles;
+    const int m0 = mt * 16;
+    const int nb0 = ntile * CB;
+    const int NB = (N + 15) >> 4;
+    const int KQ = (K + 127) / 128;
+    const int nsteps = K / 32;
+    const uint8_t* scales = Bp + (int64_t)NB * KQ * 1024;
+    const int rows_valid = M - m0 < 16 ? M - m0 : 16;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    // A operand of lane 16g + i for step s of a group: row i, K = 32s + 8g ..
+    // +7 of the group (bytes); rows past the tile's valid rows read zero.
+    const uint32_t a_off = (uint32_t)((li * lda + 8 * lg) * 2);
+    const int q0 = wave * KPW;                        // the wave's first group in a round
+
+    struct Regs {
+        u32x4 q[KPW][CB];                             // codes: dword s = step s
+        uint32_t sc[KPW][CB];                         // scales: byte s = step s
+        u32x4 a[KPW][4];
+    };
+    auto issue = [&](Regs& r, int kq0) {
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+            A + (int64_t)m0 * lda + (int64_t)kq0 * 128,
+            clamp_bytes(((int64_t)(rows_valid - 1) * lda + K - (int64_t)kq0 * 128) * 2));
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            // column blocks past N read zero (empty extents)
+            const int nb = nb0 + c;
+            const bool ok = nb < NB;
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc(
+                Bp + ((int64_t)nb * KQ + kq0) * 1024, ok ? clamp_bytes((int64_t)(KQ - kq0) * 1024) : 0u);
+#pragma unroll
+            for (int t = 0; t < KPW; ++t)
+                r.q[t][c] = buf_load16_nt(rq, (uint32_t)((q0 + t) * 1024 + lane * 16));
+        }
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            const int nb = nb0 + c;
+            const bool ok = nb < NB;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(
+                scales + ((int64_t)nb * KQ + kq0) * 64, ok ? clamp_bytes((int64_t)(KQ - kq0) * 64) : 0u);
+#pragma unroll
+            for (int t = 0; t < KPW; ++t)
+                r.sc[t][c] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)((q0 + t) * 64 + li * 4), 0, 2);
+        }
+#pragma unroll
+        for (int t = 0; t < KPW; ++t)
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+                r.a[t][st] = buf_load16(ra, a_off + (uint32_t)(((q0 + t) * 128 + 32 * st) * 2));
+    };
+
+    float acc[FPW];
+#pragma unroll
+    for (int f = 0; f < FPW; ++f)
+        acc[f] = 0.f;
+    auto round = [&](Regs& r, int kq0) {
+        // keep every load issued so far ahead of the first MFMA's wait
+        __builtin_amdgcn_sched_barrier(0);
+        if (kq0 + q0 < KQ) {
+#pragma unroll
+            for (int t = 0; t < KPW; ++t)
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const int step = 4 * (q0 + t) + st;
+#pragma unroll
+                    for (int c = 0; c < CB; ++c) {
+                        const uint32_t w = r.q[t][c][st];
+                        const u32x4 bfrag = {e2m1x2_to_bf16x2<0>(w), e2m1x2_to_bf16x2<1>(w),
+                                             e2m1x2_to_bf16x2<2>(w), e2m1x2_to_bf16x2<3>(w)};
+                        const f32x4 P = mfma_bf16(r.a[t][st], bfrag, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            pbuf[step][c][j][lane] = P[j];
+                        if (lg == 0)
+                            sbuf[step][c][li] = e4m3_byte_to_f32(r.sc[t][c], st);
+                    }
+                }
+        }
+        __syncthreads();
+        if (kq0 + 2 * R < KQ)
+            issue(r, kq0 + 2 * R);
+        const int nst = nsteps - 4 * kq0 < RS ? nsteps - 4 * kq0 : RS;
+#pragma unroll
+        for (int f = 0; f < FPW; ++f) {
+            const int chain = wave + f * WAVES;
+            if (chain < FOLDS) {
+                // chain (c, j): component j (rows 4g + j) of column block c
+                const int c = chain >> 2, j = chain & 3;
+                if (nst == RS) {
+#pragma unroll
+                    for (int st = 0; st < RS; ++st)
+                        acc[f] = __builtin_fmaf(pbuf[st][c][j][lane], sbuf[st][c][li], acc[f]);
+                } else {
+#pragma unroll 8
+                    for (int st = 0; st < nst; ++st)
+                        acc[f] = __builtin_fmaf(pbuf[st][c][j][lane], sbuf[st][c][li], acc[f]);
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    Regs r0, r1;
+    // K = 0 issues no load at all: the extents above assume a live round
+    if (KQ > 0)
+        issue(r0, 0);
+    if (KQ > R)
+        issue(r1, R);
+    for (int kq0 = 0; kq0 < KQ; kq0 += 2 * R) {
+        round(r0, kq0);
+        if (kq0 + R < KQ)
+            round(r1, kq0 + R);
+    }
+
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) {
+        const int chain = wave + f * WAVES;
+        if (chain < FOLDS) {
+            const int c = chain >> 2, j = chain & 3;
+            const int row = m0 + 4 * lg + j;
+            const int col = 16 * (nb0 + c) + li;
+            if (row < M && col < N)
+                C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc[f]);
+        }
+    }
+}
+
 // Packer: one thread per (nb, q, lane) writes 16 code bytes; threads with
 // lane < 16 also write the 4 scale bytes of column 16nb + lane.
 __global__ void pack_fp4_kernel(int N, int K, const uint8_t* __restrict__ Bq, int64_t ldbq,
@@ -320,6 +481,7 @@ struct Cfg {
     int waves, cb, rb, qs, pf;
     bool nt;
     int ar, wgr;
+    int kpw = 0;    // > 0: the unstaged kernel, CB column blocks per workgroup, KPW groups per wave and round
 };
 
 // The geometry table.  Every entry runs the same per-element arithmetic.
@@ -330,6 +492,7 @@ constexpr Cfg kCfg[] = {
     /* 3 */ {4, 1, 1, 4, 2, true, 16, 1},    // 16 x 64 streaming, four waves, 512 K per stage
     /* 4 */ {8, 1, 2, 2, 2, true, 32, 2},    // 32 x 64, eight waves of 16 x 16 (two per SIMD)
     /* 5 */ {8, 1, 4, 2, 2, true, 64, 2},    // 64 x 64, eight waves of 32 x 16
+    /* 6 */ {8, 1, 1, 0, 2, true, 16, 1, 2}, // 16 x 16, unstaged, 16 128-K groups a round
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -339,12 +502,13 @@ Geometry describe(int id, int64_t M, int64_t N)
     Geometry g;
     g.id = id;
     g.bm = 16 * c.rb;
-    g.bn = 16 * (c.waves / c.wgr) * c.cb;
+    const int cols = c.kpw > 0 ? c.cb : (c.waves / c.wgr) * c.cb;   // column blocks per workgroup
+    g.bn = 16 * cols;
     g.waves = c.waves;
     g.a_rows = c.ar;
-    g.k_stage = c.qs * 128;
+    g.k_stage = (c.kpw > 0 ? c.waves * c.kpw : c.qs) * 128;
     g.stages = c.pf;
-    g.workgroups = ceil_div(ceil_div(N, 16), (c.waves / c.wgr) * c.cb) * ceil_div(M, 16 * c.rb);
+    g.workgroups = ceil_div(ceil_div(N, 16), cols) * ceil_div(M, 16 * c.rb);
     return g;
 }
 
@@ -355,9 +519,14 @@ hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
     if (g.workgroups <= 0 || g.workgroups > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     const int m_tiles = (int)ceil_div(a.M, 16 * c.rb);
-    gemm_fp4_packed_kernel<c.waves, c.cb, c.rb, c.qs, c.pf, c.nt, c.ar, c.wgr>
-        <<<dim3((unsigned)g.workgroups), dim3(64 * c.waves), 0, stream>>>(
-            a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
+    if constexpr (c.kpw > 0)
+        gemm_fp4_packed_direct_kernel<c.waves, c.kpw, c.cb>
+            <<<dim3((unsigned)g.workgroups), dim3(64 * c.waves), 0, stream>>>(
+                a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
+    else
+        gemm_fp4_packed_kernel<c.waves, c.cb, c.rb, c.qs, c.pf, c.nt, c.ar, c.wgr>
+            <<<dim3((unsigned)g.workgroups), dim3(64 * c.waves), 0, stream>>>(
+                a.M, a.N, a.K, (const uint16_t*)a.A, a.lda, (const uint8_t*)a.B, a.C, a.ldc, m_tiles);
     return hipGetLastError();
 }
 
@@ -372,8 +541,12 @@ hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
 // the call has at most three 32-row tiles beyond the first 64 rows' worth
 // (M = 17..32 14.5 -> 13.2 us, M = 65..96 35.6 -> 29 us) and 64 x 64
 // otherwise (M = 33..64 20.4..25.2 -> 18.3..19.3 us, M = 97..128 36 ->
-// 35 us); for narrow weights two waves of 16 x 16 streaming up to 16 rows,
-// 64 x 64 above.  All 16 rows of each A stage are
+// 35 us); for narrow weights two waves of 16 x 16 streaming up to 16 rows
+// -- or, for N/16 <= 128, the unstaged kernel on 16 x 16 tiles (K = 7168,
+// N = 2048: M = 1 14.8 -> 9.1 us, M = 16 15.3 -> 13.4 us) -- and 64 x 64
+// above.  The unstaged kernel forms one product per 32-K step, so its LDS
+// traffic is about eight times its global loads: on wide weights it loses
+// (N = 14336, M = 1: 14.5 against 9.9 us).  All 16 rows of each A stage are
 // staged even for a single row: with the MFMA results kept in VGPRs, staging
 // only the first 8 measured slower (M = 1: 11.2 vs 10.7 us).
 Geometry geometry_fp4_packed(int64_t M, int64_t N, int64_t K)
@@ -385,8 +558,10 @@ Geometry geometry_fp4_packed(int64_t M, int64_t N, int64_t K)
         id = 2;
     else if (nb >= 256)
         id = M <= 16 ? 3 : (M <= 32 || (M > 64 && M <= 96)) ? 4 : 5;
+    else if (M <= 16)
+        id = nb <= 128 ? 6 : 0;
     else
-        id = M <= 16 ? 0 : 1;
+        id = 1;
     return describe(id, M, N);
 }
 
@@ -400,10 +575,11 @@ hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream)
     case 3: return launch_cfg<3>(a, g, stream);
     case 4: return launch_cfg<4>(a, g, stream);
     case 5: return launch_cfg<5>(a, g, stream);
+    case 6: return launch_cfg<6>(a, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 6, "every table entry needs its case in launch_fp4w_packed");
+static_assert(kNumCfg == 7, "every table entry needs its case in launch_fp4w_packed");
 
 hipError_t launch_pack_fp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sB,
                            int64_t ldsb, uint8_t* Bp, hipStream_t stream)

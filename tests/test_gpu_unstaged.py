@@ -1,4 +1,4 @@
-"""GPU tests of the unstaged small-M kernels of the packed fp8 and W4A8
+"""GPU tests of the unstaged small-M kernels of the packed fp8, W4A8 and fp4
 GEMMs over several rounds of K blocks.
 
 Those kernels take the 128-K blocks in rounds of 56 (8 waves x 7 blocks):
@@ -14,12 +14,13 @@ import torch
 
 import oracle
 from invariant_gemm_amd import inputs
-from tests.gpu_util import check_parity, dev_f32, dev_u8, host_codes, require_gpu
+from tests.gpu_util import check_parity, dev_bf16, dev_f32, dev_u8, host_codes, require_gpu
 
 pytestmark = pytest.mark.gpu
 
 UNSTAGED_FP8 = {8, 9}        # packed fp8 table: unstaged half / whole blocks
 UNSTAGED_W4A8 = {7, 8, 9}    # packed W4A8 table: unstaged 16, 8 (half) and 32 columns
+UNSTAGED_FP4 = {6}           # packed fp4 table: unstaged 16 columns (narrow weights)
 
 
 @pytest.fixture(scope="module")
@@ -101,3 +102,28 @@ def test_grouped_rounds(bg):
     assert bg.geometry("w4a8_grouped_packed", 1, N, K, groups=E)["id"] in UNSTAGED_W4A8
     g4 = host_codes(bg.gemm_w4a8_grouped_packed(A, sAd, off, bg.pack_b_mxfp4_grouped(dq, ds, N)))
     assert np.array_equal(g4, host_codes(bg.gemm_w4a8_packed(A, sAd, bg.pack_b_mxfp4(dq[1], ds[1], N))))
+
+
+# fp4 takes its 32-K steps in rounds of 16 128-K groups with two rounds in
+# flight: K = 7168 is four rounds, 14336 seven (an odd count), 4096 two; 96 is
+# one group of three steps
+FP4_CASES = [(1, 2048, 7168), (16, 1000, 4096), (5, 272, 14336), (3, 64, 96)]
+
+
+@pytest.mark.parametrize("M,N,K", FP4_CASES)
+def test_fp4_rounds(bg, M, N, K):
+    big = 300
+    A = inputs.normal_bf16((big, K), 1.0, 5600 + K + M)
+    Bq, sB = inputs.quant_fp4_weights(inputs.normal_f32((K, N), 0.02, 5700 + N))
+    Ad = dev_bf16(A)
+    Bd, sBd = dev_u8(Bq, pad16(Bq.shape[1])), dev_u8(sB, pad16(sB.shape[1]))
+    Bp = bg.pack_b_fp4(dev_u8(Bq), dev_u8(sB), N)
+    assert bg.geometry("fp4_packed", M, N, K)["id"] in UNSTAGED_FP4
+    assert bg.geometry("fp4_packed", big, N, K)["id"] not in UNSTAGED_FP4
+    got = host_codes(bg.gemm_fp4_w_packed(Ad[:M], Bp))
+    C64, S = oracle.gemm_fp4w(np.ascontiguousarray(A[:M]), Bq, sB, N)
+    check_parity(got, C64, S, K, f"fp4 packed unstaged M{M} N{N} K{K}")
+    staged = host_codes(bg.gemm_fp4_w_packed(Ad, Bp))
+    assert np.array_equal(got, staged[:M])
+    rowmajor = host_codes(bg.gemm_fp4_w(Ad[:M], Bd, sBd, N))
+    assert np.array_equal(got, rowmajor)
