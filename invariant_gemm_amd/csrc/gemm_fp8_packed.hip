@@ -381,19 +381,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_kernel(
     }
 }
 
-// Small-M variant without operand staging: one 16-row block, 16 columns (or
-// 8, HALF as above) per workgroup.  The K blocks are taken in rounds of
-// R = WAVES*KPW; in a round, wave w loads the A and B operands of blocks
-// kb0 + w*KPW .. + KPW-1 straight from global memory into its registers (the
-// packed weights are already in the MFMA's lane order), all loads issued
-// before the first MFMA, and forms each block's product P with the same
-// MFMA into a zero accumulator.  The products go to LDS, and four waves --
-// one per accumulator component -- fold them in ascending K order with the
-// same acc = fma(P, sA*sB, acc), so every output element sees exactly the
-// operations of the staged kernel above.  Loads for the next round are
-// issued before the fold of the current one.  Blocks past K/128 in the last
-// round are loaded (B as zero outside its extent) but never folded.
-template <int WAVES, int KPW, bool HALF, bool GROUPED>
+// Small-M variant without operand staging: one 16-row block and CB column
+// blocks of 16 (or 8 columns, HALF as above) per workgroup.  The K blocks
+// are taken in rounds of R = WAVES*KPW; in a round, wave w loads the A and B
+// operands of blocks kb0 + w*KPW .. + KPW-1 straight from global memory into
+// its registers (the packed weights are already in the MFMA's lane order),
+// all loads issued before the first MFMA, and forms each block's product P
+// with the same MFMA into a zero accumulator.  The products go to LDS, and
+// 4*CB waves -- one per (column block, accumulator component) -- fold them in
+// ascending K order with the same acc = fma(P, sA*sB, acc), so every output
+// element sees exactly the operations of the staged kernel above.  Loads for
+// the next round are issued before the fold of the current one.  Blocks
+// past K/128 in the last round are loaded (B as zero outside its extent) but
+// never folded.
+template <int WAVES, int KPW, int CB, bool HALF, bool GROUPED>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_direct_kernel(
     int M, int N, int K,
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t ldsa,
@@ -401,14 +402,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_direct_kernel(
     uint16_t* __restrict__ C, int64_t ldc, int m_tiles,
     const int32_t* __restrict__ offsets, int n_groups, int64_t b_stride, int64_t sb_stride)
 {
-    static_assert(WAVES >= 4, "four folding waves, one per accumulator component");
+    static_assert(WAVES >= 4 * CB, "one folding wave per (column block, accumulator component)");
+    static_assert(!HALF || CB == 1, "half blocks: one column block");
     constexpr int NTHR = 64 * WAVES;
     constexpr int R = WAVES * KPW;                    // K blocks per round
     constexpr int SPT = (R * 16 + NTHR - 1) / NTHR;   // activation scales per thread and round
     static_assert(R <= NTHR, "one weight scale per thread and round");
-    __shared__ float pbuf[R][4][64];                  // [block][component][lane]
+    __shared__ float pbuf[R][CB][4][64];              // [block][column block][component][lane]
     __shared__ float sas[R][16];                      // sA of the tile's rows, block-major
-    __shared__ float sbs[R];
+    __shared__ float sbs[R][CB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_direct_kernel(
     const int tile = xcd_remap(blockIdx.x, gridDim.x);
     const int ntile = tile / m_tiles;
     const int mt = tile - ntile * m_tiles;
-    const int nb = HALF ? ntile >> 1 : ntile;
+    const int nb0 = HALF ? ntile >> 1 : ntile * CB;   // the tile's first column block
     const int ch = HALF ? ntile & 1 : 0;
     int m0 = mt * 16;
     int row_end = M;
@@ -440,26 +442,36 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_direct_kernel(
     // the lane that holds the same column among the workgroup's 8).
     const uint32_t b_off = (uint32_t)((HALF ? 16 * lg + 8 * ch + (li & 7) : lane) * 16);
     const int q0 = wave * KPW;                        // the wave's first block in a round
-    const int scol = (16 * nb) / 128;                 // the tile's column of sB
 
-    u32x4 a[KPW][2], b[KPW][2];
-    float sav[SPT], sbv;
+    u32x4 a[KPW][2], b[KPW][CB][2];
+    float sav[SPT], sbv[CB];
     auto issue = [&](int kb0) {
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(
-            Bp + ((int64_t)nb * nkb + kb0) * BTILE, nb < NB ? clamp_bytes((int64_t)(nkb - kb0) * BTILE) : 0u);
+        // every buffer resource first, then the loads (B, A, sA, sB)
+        __amdgpu_buffer_rsrc_t rb[CB], rsb[CB];
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+            // column blocks past N read zero (empty extents); scol: the
+            // column block's column of sB
+            const int nb = nb0 + c;
+            const int scol = (16 * nb) / 128;
+            rb[c] = make_rsrc(Bp + ((int64_t)nb * nkb + kb0) * BTILE,
+                              nb < NB ? clamp_bytes((int64_t)(nkb - kb0) * BTILE) : 0u);
+            rsb[c] = make_rsrc(sB + (int64_t)kb0 * ldsb + scol,
+                               clamp_bytes(((int64_t)(nkb - 1 - kb0) * ldsb + 1) * 4));
+        }
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(
             A + (int64_t)m0 * lda + (int64_t)kb0 * KBK,
             clamp_bytes((int64_t)(rows_valid - 1) * lda + K - (int64_t)kb0 * KBK));
         const __amdgpu_buffer_rsrc_t rsa = make_rsrc(
             sA + (int64_t)m0 * ldsa + kb0, clamp_bytes(((int64_t)(rows_valid - 1) * ldsa + nkb - kb0) * 4));
-        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(
-            sB + (int64_t)kb0 * ldsb + scol, clamp_bytes(((int64_t)(nkb - 1 - kb0) * ldsb + 1) * 4));
 #pragma unroll
-        for (int t = 0; t < KPW; ++t) {
-            const uint32_t o = (uint32_t)(q0 + t) * BTILE + b_off;
-            b[t][0] = buf_load16_nt(rb, o);
-            b[t][1] = buf_load16_nt(rb, o + 1024);
-        }
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+            for (int t = 0; t < KPW; ++t) {
+                const uint32_t o = (uint32_t)(q0 + t) * BTILE + b_off;
+                b[t][c][0] = buf_load16_nt(rb[c], o);
+                b[t][c][1] = buf_load16_nt(rb[c], o + 1024);
+            }
 #pragma unroll
         for (int t = 0; t < KPW; ++t) {
             const uint32_t o = a_off + (uint32_t)(q0 + t) * KBK;
@@ -473,10 +485,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_direct_kernel(
             const uint32_t o = u < R * 16 ? (uint32_t)(((u / R) * ldsa + u % R) * 4) : OOB;
             sav[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsa, (int)o, 0, 0));
         }
-        sbv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-            rsb, (int)(tid < R ? (uint32_t)(tid * ldsb * 4) : OOB), 0, 0));
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+            sbv[c] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                rsb[c], (int)(tid < R ? (uint32_t)(tid * ldsb * 4) : OOB), 0, 0));
     };
 
+    // wave 4c + j folds component j (rows 4g + j) of column block c (a
+    // constant 0 for one block keeps the scale reads vectorisable)
+    const int fc = CB == 1 ? 0 : wave >> 2, fj = wave & 3;
     float acc = 0.f;
     // K = 0 issues no load at all: the extents above assume a live round
     if (nkb > 0)
@@ -489,14 +506,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_direct_kernel(
             for (int t = 0; t < KPW; ++t) {
                 const i32x8 av = {(int)a[t][0][0], (int)a[t][0][1], (int)a[t][0][2], (int)a[t][0][3],
                                   (int)a[t][1][0], (int)a[t][1][1], (int)a[t][1][2], (int)a[t][1][3]};
-                const i32x8 bv = {(int)b[t][0][0], (int)b[t][0][1], (int)b[t][0][2], (int)b[t][0][3],
-                                  (int)b[t][1][0], (int)b[t][1][1], (int)b[t][1][2], (int)b[t][1][3]};
-                // fp8 e4m3 x fp8 e4m3, unit E8M0 block scales (127 = 2^0)
-                const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    pbuf[q0 + t][j][lane] = P[j];
+                for (int c = 0; c < CB; ++c) {
+                    const i32x8 bv = {(int)b[t][c][0][0], (int)b[t][c][0][1], (int)b[t][c][0][2],
+                                      (int)b[t][c][0][3], (int)b[t][c][1][0], (int)b[t][c][1][1],
+                                      (int)b[t][c][1][2], (int)b[t][c][1][3]};
+                    // fp8 e4m3 x fp8 e4m3, unit E8M0 block scales (127 = 2^0)
+                    const f32x4 P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pbuf[q0 + t][c][j][lane] = P[j];
+                }
             }
         }
 #pragma unroll
@@ -505,30 +526,32 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp8_packed_direct_kernel(
             if (u < R * 16)
                 sas[u % R][u / R] = sav[j];
         }
-        if (tid < R)
-            sbs[tid] = sbv;
+        if (tid < R) {
+#pragma unroll
+            for (int c = 0; c < CB; ++c)
+                sbs[tid][c] = sbv[c];
+        }
         __syncthreads();
         if (kb0 + R < nkb)
             issue(kb0 + R);
-        if (wave < 4) {
-            // wave j folds component j: rows 4g + j of the block
+        if (wave < 4 * CB) {
             const int nq = nkb - kb0 < R ? nkb - kb0 : R;
             if (nq == R) {
 #pragma unroll
                 for (int q = 0; q < R; ++q)
-                    acc = __builtin_fmaf(pbuf[q][wave][lane], sas[q][4 * lg + wave] * sbs[q], acc);
+                    acc = __builtin_fmaf(pbuf[q][fc][fj][lane], sas[q][4 * lg + fj] * sbs[q][fc], acc);
             } else {
 #pragma unroll 8
                 for (int q = 0; q < nq; ++q)
-                    acc = __builtin_fmaf(pbuf[q][wave][lane], sas[q][4 * lg + wave] * sbs[q], acc);
+                    acc = __builtin_fmaf(pbuf[q][fc][fj][lane], sas[q][4 * lg + fj] * sbs[q][fc], acc);
             }
         }
         __syncthreads();
     }
 
-    if (wave < 4) {
-        const int row = m0 + 4 * lg + wave;
-        const int col = HALF ? 16 * nb + 8 * ch + li : 16 * nb + li;
+    if (wave < 4 * CB) {
+        const int row = m0 + 4 * lg + fj;
+        const int col = HALF ? 16 * nb0 + 8 * ch + li : 16 * (nb0 + fc) + li;
         if (row < row_end && col < N && (!HALF || li < 8))
             C[(int64_t)row * ldc + col] = (uint16_t)gemm_out_bf16(acc);
     }
@@ -588,7 +611,8 @@ struct Cfg {
 // 16 x 16 tile, M = 1 11.6 -> 8.2 us, M = 16 12.3 -> 10.4 us.  Beyond one
 // round (K > 7168) each round waits for its own loads, and for more than 8
 // rows the staged kernel is faster there (M = 16, K = 16384: 15.8 against
-// 17.9 us).
+// 17.9 us).  Entry 10 takes two column blocks per workgroup (rounds of 32
+// K blocks) for wide weights.
 constexpr Cfg kCfg[] = {
     /* 0 */ {8, 1, 1, 1, 1, 8, 4, false, 16},   // 16 x 16, eight waves streaming
     /* 1 */ {8, 2, 1, 1, 1, 8, 2, false, 32},   // 32 x 16
@@ -600,6 +624,7 @@ constexpr Cfg kCfg[] = {
     /* 7 */ {8, 1, 4, 1, 1, 4, 2, false, 16},   // 16 x 64, four computing waves (grouped calls)
     /* 8 */ {8, 1, 1, 1, 1, 0, 1, true, 16, 7}, // 16 x 8 half blocks, unstaged, 56 K blocks a round
     /* 9 */ {8, 1, 1, 1, 1, 0, 1, false, 16, 7}, // 16 x 16, unstaged
+    /* 10 */ {8, 1, 2, 1, 1, 0, 1, false, 16, 4}, // 16 x 32, unstaged, 32 K blocks a round
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -644,12 +669,12 @@ hipError_t launch_cfg(const GemmArgs& a, const GroupArgs* grp, int64_t sb_stride
     const dim3 grid((unsigned)g.workgroups), block(64 * c.waves);
     if constexpr (c.kpw > 0) {
         if (grp)
-            gemm_fp8_packed_direct_kernel<c.waves, c.kpw, c.half, true><<<grid, block, 0, stream>>>(
+            gemm_fp8_packed_direct_kernel<c.waves, c.kpw, c.cb, c.half, true><<<grid, block, 0, stream>>>(
                 a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
                 (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles,
                 grp->offsets, grp->n_groups, grp->b_stride, sb_stride);
         else
-            gemm_fp8_packed_direct_kernel<c.waves, c.kpw, c.half, false><<<grid, block, 0, stream>>>(
+            gemm_fp8_packed_direct_kernel<c.waves, c.kpw, c.cb, c.half, false><<<grid, block, 0, stream>>>(
                 a.M, a.N, a.K, (const uint8_t*)a.A, a.lda, (const float*)a.sA, a.ldsa,
                 (const uint8_t*)a.B, (const float*)a.sB, a.ldsb, a.C, a.ldc, m_tiles,
                 nullptr, 0, 0, 0);
@@ -684,17 +709,20 @@ hipError_t launch_id(const GemmArgs& a, const GroupArgs* grp, int64_t sb_stride,
     case 7: return launch_cfg<7>(a, grp, sb_stride, g, stream);
     case 8: return launch_cfg<8>(a, grp, sb_stride, g, stream);
     case 9: return launch_cfg<9>(a, grp, sb_stride, g, stream);
+    case 10: return launch_cfg<10>(a, grp, sb_stride, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 10, "every table entry needs its case in launch_id");
+static_assert(kNumCfg == 11, "every table entry needs its case in launch_id");
 
 }  // namespace
 
 // Launch geometry (tile sharing only: every geometry runs the same
 // per-element arithmetic).  For M <= 16 one 16-row block per workgroup, on
 // half blocks (8 columns) while N/16 blocks would leave compute units without
-// a workgroup, else on whole 16 x 16 blocks.  Above 16 rows: the smallest
+// a workgroup, on whole 16 x 16 blocks while they fit in one round, and on
+// unstaged 16 x 32 tiles beyond (K = 4096, N = 14336: M = 1 20.4 -> 14.3 us,
+// M = 16 27.4 -> 16.4 us against 16 x 16; N = 8192, M = 1 15.2 -> 13.3 us).  Above 16 rows: the smallest
 // tile (16 x 16, 32 x 16, 32 x 32, 64 x 32, 64 x 64) whose grid still fits
 // on the compute units in one round, else the largest.  16-row tiles run
 // unstaged while one round of its loads covers K or the call has at most 8
@@ -705,7 +733,7 @@ static_assert(kNumCfg == 10, "every table entry needs its case in launch_id");
 // 16 x 16 tiles against 11.9 us on 256 tiles of 32 x 16.
 namespace {
 constexpr int64_t kComputeUnits = 256;
-constexpr int kHalfDirect = 8, kFullDirect = 9, kHalfStaged = 5;
+constexpr int kHalfDirect = 8, kFullDirect = 9, kWideDirect = 10, kHalfStaged = 5;
 
 bool unstaged_fits(int64_t M, int64_t K)
 {
@@ -722,6 +750,8 @@ int fp8_family(int64_t M, int64_t N, int64_t K)
     if (M <= 16) {
         if (nb < kComputeUnits)
             return unstaged_fits(M, K) ? kHalfDirect : kHalfStaged;
+        if (nb > kComputeUnits && unstaged_fits(M, K))
+            return kWideDirect;
         return tile16(M, K);
     }
     for (int id = 0; id < 4; ++id)

@@ -18,7 +18,7 @@ from tests.gpu_util import check_parity, dev_bf16, dev_f32, dev_u8, host_codes, 
 
 pytestmark = pytest.mark.gpu
 
-UNSTAGED_FP8 = {8, 9}        # packed fp8 table: unstaged half / whole blocks
+UNSTAGED_FP8 = {8, 9, 10}    # packed fp8 table: unstaged 8 (half), 16 and 32 columns
 UNSTAGED_W4A8 = {7, 8, 9}    # packed W4A8 table: unstaged 16, 8 (half) and 32 columns
 UNSTAGED_FP4 = {6}           # packed fp4 table: unstaged 16 columns (narrow weights)
 
@@ -35,9 +35,11 @@ def pad16(n):
 
 
 # (M, N, K): 57 blocks (one round and one block), 113 (two and one), 168
-# (exactly three); N below, at and past 256 column blocks (half / whole
-# blocks); the big batch of 300 rows runs the staged tiles
-FP8_CASES = [(1, 272, 7296), (8, 2048, 14464), (5, 4112, 21504), (3, 1000, 7296)]
+# (exactly three); N below and past 256 column blocks (half blocks, and the
+# 32-column tiles whose rounds hold 32 blocks: K = 4096 one round, 7296 two,
+# 21504 six); the big batch of 300 rows runs the staged tiles
+FP8_CASES = [(1, 272, 7296), (8, 2048, 14464), (5, 4112, 21504), (3, 1000, 7296),
+             (16, 4112, 4096), (2, 8192, 7296)]
 
 
 @pytest.mark.parametrize("M,N,K", FP8_CASES)
