@@ -13,11 +13,13 @@
 // 32-long K block kb, ascending, P = v_mfma_f32_16x16x32_bf16(A, e2m1 -> bf16
 // exact, 0) then acc = fma(P, e4m3(sB[kb,n]), acc).  Identical bits to the
 // unpacked entry point; rows independent of M, position and companions.
-// Launch geometries: streaming (2 waves x 16 columns, BM 16), medium
-// (4 waves x 16 columns, BM 64), large (4 waves x 32 columns, BM 64).
+// Launch geometries: the table below.
 //
 // Weight codes and scales are read once and loaded non-temporal, except in
-// the largest-M geometry, whose row tiles share each column strip.
+// the largest-M geometry, whose row tiles share each column strip.  Small-M
+// calls on narrow weights run the unstaged kernel further down (operands
+// straight into registers, step products folded in K order); its bits are
+// the same.
 #include "common.h"
 #include "launch.h"
 

@@ -20,7 +20,9 @@
 // blocks is split among the waves as (RB/WR) x (CB/WC) sub-tiles, and waves
 // beyond that count only load.  With a single 16 x 16 block (small M) all
 // waves still stream weights for it, which keeps enough bytes in flight per
-// compute unit when N/16 is below the compute unit count.
+// compute unit when N/16 is below the compute unit count.  Most small-M calls
+// run the unstaged kernel further down instead (operands straight into
+// registers, block products folded in K order); its bits are the same.
 //
 // HALF (small M only): a workgroup owns 8 of a block's 16 columns, so N/8
 // workgroups share the weights.  It loads only those columns' bytes; MFMA

@@ -27,7 +27,10 @@
 // (nb*KB + kb)*64, byte l = sE[4kb + g][16nb + i].  Zero past N.
 //
 // Weight codes and scales are read once and loaded non-temporal, except in
-// the largest-M geometry, whose row tiles share each column strip.
+// the largest-M geometry, whose row tiles share each column strip.  Small-M
+// calls whose tiles fit the compute units run the unstaged kernel further
+// down (operands straight into registers, block products folded in K
+// order); its bits are the same.
 #include <algorithm>
 
 #include "common.h"
