@@ -687,10 +687,12 @@ int narrow_rows_id(int64_t M, int64_t N, int64_t slots)
 // tile (of which only the first 8 rows are loaded when the call has no
 // more: LDS rows past them keep stale bytes, which reach only output rows
 // that are never stored, an MFMA output row depending on its own A row
-// alone).  Up to 32 rows, the unstaged kernel on two 16-row slots where they
-// fit in one round, else 32 x 64 tiles on four waves while they fit on the
+// alone).  Up to 64 rows, the unstaged kernel on 16-row slots where they
+// fit in one round (N = 2048, M = 64: 19.1 -> 9.3 us against 64 x 64 tiles);
+// up to 128 rows, else 32 x 64 tiles on four waves while they fit on the
 // compute units in one round (M = 17 16.0 -> 11.0 us, M = 32 16.2 ->
-// 11.2 us); above that 64 x 64 tiles: while they fit in one round, eight
+// 11.2 us; N = 8192, M = 64 13.7 -> 11.0 us against 64 x 64); above that
+// 64 x 64 tiles: while they fit in one round, eight
 // waves of which four only load, four K blocks per stage (M = 64 16.1 ->
 // 14.7 us); past one round four waves, with one K block per stage once
 // M > 128 (the eight-wave version measured 20-30 % slower there); above 192
@@ -705,9 +707,9 @@ Geometry geometry_w4a8_packed(int64_t M, int64_t N, int64_t K)
     int id;
     if (M <= 16)
         id = narrow_rows_id(M, N, 1);
-    else if (M <= 32 && unstaged_id(N, ceil_div(M, 16), false) >= 0)
+    else if (M <= 64 && unstaged_id(N, ceil_div(M, 16), false) >= 0)
         id = unstaged_id(N, ceil_div(M, 16), false);
-    else if (M <= 32 && ceil_div(M, 32) * col_tiles <= 256)
+    else if (M <= 128 && ceil_div(M, 32) * col_tiles <= 256)
         id = 5;
     else if (ceil_div(M, 64) * col_tiles <= 256)
         id = 4;
