@@ -489,12 +489,11 @@ struct Cfg {
 // The geometry table.  Every entry runs the same per-element arithmetic.
 constexpr Cfg kCfg[] = {
     /* 0 */ {2, 1, 1, 2, 4, true, 16, 1},    // 16 x 32 streaming, two waves
-    /* 1 */ {4, 1, 4, 2, 2, true, 64, 1},    // 64 x 64
-    /* 2 */ {4, 2, 4, 1, 2, false, 64, 1},   // 64 x 128, weights shared by row tiles
-    /* 3 */ {4, 1, 1, 4, 2, true, 16, 1},    // 16 x 64 streaming, four waves, 512 K per stage
-    /* 4 */ {8, 1, 2, 2, 2, true, 32, 2},    // 32 x 64, eight waves of 16 x 16 (two per SIMD)
-    /* 5 */ {8, 1, 4, 2, 2, true, 64, 2},    // 64 x 64, eight waves of 32 x 16
-    /* 6 */ {8, 1, 1, 0, 2, true, 16, 1, 2}, // 16 x 16, unstaged, 16 128-K groups a round
+    /* 1 */ {4, 2, 4, 1, 2, false, 64, 1},   // 64 x 128, weights shared by row tiles
+    /* 2 */ {4, 1, 1, 4, 2, true, 16, 1},    // 16 x 64 streaming, four waves, 512 K per stage
+    /* 3 */ {8, 1, 2, 2, 2, true, 32, 2},    // 32 x 64, eight waves of 16 x 16 (two per SIMD)
+    /* 4 */ {8, 1, 4, 2, 2, true, 64, 2},    // 64 x 64, eight waves of 32 x 16
+    /* 5 */ {8, 1, 1, 0, 2, true, 16, 1, 2}, // 16 x 16, unstaged, 16 128-K groups a round
 };
 constexpr int kNumCfg = sizeof(kCfg) / sizeof(kCfg[0]);
 
@@ -536,34 +535,45 @@ hipError_t launch_cfg(const GemmArgs& a, const Geometry& g, hipStream_t stream)
 
 // Launch geometry (tile sharing only: the per-element arithmetic is the same
 // for all): 64 x 128 tiles once they still give each compute unit a
-// workgroup; below that, for wide weights (N/16 >= 256), 16-row tiles of 64
+// workgroup.  Below that, for wide weights (N/16 >= 512), 16-row tiles of 64
 // columns on four waves with 512 K per stage up to 16 rows (K = 4096,
 // N = 14336: M = 1 11.1 -> 9.5 us), then tiles of 64 columns on eight waves
 // that split the rows two ways, so each SIMD holds two waves: 32 x 64 while
 // the call has at most three 32-row tiles beyond the first 64 rows' worth
 // (M = 17..32 14.5 -> 13.2 us, M = 65..96 35.6 -> 29 us) and 64 x 64
 // otherwise (M = 33..64 20.4..25.2 -> 18.3..19.3 us, M = 97..128 36 ->
-// 35 us); for narrow weights two waves of 16 x 16 streaming up to 16 rows
-// -- or, for N/16 <= 128, the unstaged kernel on 16 x 16 tiles (K = 7168,
-// N = 2048: M = 1 14.8 -> 9.1 us, M = 16 15.3 -> 13.4 us) -- and 64 x 64
-// above.  The unstaged kernel forms one product per 32-K step, so its LDS
-// traffic is about eight times its global loads: on wide weights it loses
-// (N = 14336, M = 1: 14.5 against 9.9 us).  All 16 rows of each A stage are
-// staged even for a single row: with the MFMA results kept in VGPRs, staging
-// only the first 8 measured slower (M = 1: 11.2 vs 10.7 us).
+// 35 us).  Narrower weights: up to 16 rows the unstaged kernel on 16 x 16
+// tiles for N/16 <= 128 (K = 7168, N = 2048: M = 1 14.8 -> 9.1 us,
+// M = 16 15.3 -> 13.4 us), two waves of 16 x 32 streaming below 256 column
+// blocks and 16 x 64 on four waves from there; above 16 rows the largest of
+// 64 x 64 and 32 x 64 (eight waves), 16 x 32 (two waves) and unstaged
+// 16 x 16 whose grid fills the compute units, else the last: K = 7168,
+// N = 2048, M = 32 48.2 -> 13.7 us, M = 64 49.4 -> 15.9 us, M = 256 51.0 ->
+// 21.3 us, M = 512 52.3 -> 31.7 us against 64 x 64 on four waves; K = 4096,
+// N = 4096, M = 32 12.6 -> 10.0 us, M = 64 17.8 -> 11.3 us, M = 128 18.2 ->
+// 13.2 us.  The unstaged kernel forms one product per 32-K step, so its
+// LDS traffic is about eight times its global loads: on wide weights it
+// loses (N = 14336, M = 1: 14.5 against 9.9 us).  All 16 rows of each A
+// stage are staged even for a single row: with the MFMA results kept in
+// VGPRs, staging only the first 8 measured slower (M = 1: 11.2 vs 10.7 us).
 Geometry geometry_fp4_packed(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
     const int64_t nb = ceil_div(N, 16);
     int id;
     if (M >= 64 && ceil_div(M, 64) * ceil_div(nb, 8) >= 256)
-        id = 2;
-    else if (nb >= 256)
-        id = M <= 16 ? 3 : (M <= 32 || (M > 64 && M <= 96)) ? 4 : 5;
-    else if (M <= 16)
-        id = nb <= 128 ? 6 : 0;
-    else
         id = 1;
+    else if (M > 16 && nb < 512) {
+        id = 5;
+        for (int c : {4, 3, 0})
+            if (describe(c, M, N).workgroups >= 256) {
+                id = c;
+                break;
+            }
+    } else if (nb >= 256)
+        id = M <= 16 ? 2 : (M <= 32 || (M > 64 && M <= 96)) ? 3 : 4;
+    else
+        id = nb <= 128 ? 5 : 0;
     return describe(id, M, N);
 }
 
@@ -577,11 +587,10 @@ hipError_t launch_fp4w_packed(const GemmArgs& a, hipStream_t stream)
     case 3: return launch_cfg<3>(a, g, stream);
     case 4: return launch_cfg<4>(a, g, stream);
     case 5: return launch_cfg<5>(a, g, stream);
-    case 6: return launch_cfg<6>(a, g, stream);
     default: return hipErrorInvalidValue;
     }
 }
-static_assert(kNumCfg == 7, "every table entry needs its case in launch_fp4w_packed");
+static_assert(kNumCfg == 6, "every table entry needs its case in launch_fp4w_packed");
 
 hipError_t launch_pack_fp4(int N, int K, const uint8_t* Bq, int64_t ldbq, const uint8_t* sB,
                            int64_t ldsb, uint8_t* Bp, hipStream_t stream)

@@ -138,6 +138,6 @@ def test_tables_fully_reached(bg):
     # bf16 table and entries 6 and 7 of the packed fp8 table serve grouped
     # calls only)
     want = {"bf16": 2, "bf16_bt": 5, "bf16_packed": 14, "fp8": 4, "fp8_packed": 9, "fp4": 1,
-            "fp4_packed": 7, "w4a8_packed": 10}
+            "fp4_packed": 6, "w4a8_packed": 10}
     for entry, n in want.items():
         assert len(cases(bg, entry, FP8_KS.get(entry, [384]))) == n, entry
