@@ -409,6 +409,16 @@ int family(int64_t M, int64_t N)
         return 7;
     if (M >= 64 && medium >= 256)
         return 6;
+    if (M > 16 && nb < 512) {
+        // narrower weights: the largest streaming tile whose grid fills the
+        // compute units, else one wave per 16 x 16 block (K = 7168,
+        // N = 2048: M = 32 17.9 -> 11.1 us, M = 64 27.6 -> 14.0 us, M = 128
+        // 28.3 -> 17.9 us; N = 4096, M = 64 28.1 -> 18.8 us)
+        for (int id : {4, 3, 0})
+            if (describe(id, M, N, 0).workgroups >= 256)
+                return id;
+        return 9;
+    }
     if (M > 32)
         return 4;                                               // streaming, BM 64
     if (M > 16)
@@ -452,7 +462,7 @@ Geometry geometry_bf16_packed(int64_t M, int64_t N, int64_t K)
 {
     (void)K;
     int id = family(M, N);
-    if (id == 9 && ceil_div(N, 16) < 256)
+    if (id == 9 && M <= 16 && ceil_div(N, 16) < 256)
         id = 12;
     if (id == 4 && M <= 64 && ceil_div(M, 32) * ceil_div(ceil_div(N, 16), 4) >= 256)
         id = 5;
